@@ -1,0 +1,191 @@
+/*
+ * rmm.h - C ABI of the Reduced Matrix Multiplication (RMM) hot path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes comes from the pages titled "Reduced Matrix
+ * Multiplication: Input-Adaptive Matrix-Product Reduction for LLM Inference"
+ * (gist.science explainer, es/zh editions, section "Metodología" / "方法论";
+ * arXiv:2608.13426 abstract):
+ *   every Transformer product is Y = A B with A the activation and B a weight
+ *   or intermediate; contraction index j is scored by s_j = ||A[:, j]||_2; the
+ *   k = ceil(rho d) best-scored indices I are kept; A[:, I] B[I, :] replaces
+ *   A B.  Sites: projections X W (hidden dim), Q K^T (head-feature dim) and
+ *   P V (token dim).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked (device) must be device memory visible to the current
+ *     HIP device; (host) pointers are ordinary host memory.
+ *   - Element types: RMM_BF16 = IEEE bfloat16 stored as 16-bit words, RMM_F32 =
+ *     IEEE binary32.  Every pointer must be aligned to its element size.
+ *     Vectorised 16-byte paths are taken automatically when base addresses and
+ *     strides allow; other layouts run a scalar path with identical results.
+ *   - Strides and leading dimensions are counted in elements, not bytes.
+ *   - All matrices are row-major: element (i, j) of a matrix with leading
+ *     dimension ld lives at base[i * ld + j].
+ *   - Ownership: the caller allocates and frees every buffer (inputs, outputs,
+ *     index lists and workspace).  The library never allocates, frees, caches
+ *     or synchronises; it enqueues kernels on `stream` and returns.  Buffers
+ *     must stay alive until that stream work completes.  Outputs must not
+ *     alias inputs or each other.
+ *   - Workspace: `ws` (device) of at least the size returned by the matching
+ *     *_workspace_bytes query (0 is allowed when the query returns 0).  The
+ *     workspace holds no state between calls.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued; a rejected call enqueues nothing and returns
+ *     RMM_ERR_INVALID_ARG / RMM_ERR_UNSUPPORTED / RMM_ERR_WORKSPACE.  A failed
+ *     kernel launch returns RMM_ERR_HIP.  Faults inside kernels surface at the
+ *     caller's next synchronisation, as usual for HIP.  No call aborts or
+ *     prints; rmm_last_error() gives a one-line description of the last
+ *     failure on the calling thread.
+ *   - Determinism: every result is bitwise reproducible for fixed inputs and
+ *     shapes (fixed-order reductions, no floating-point atomics).
+ *   - Index lists: rmm_topk writes, for each batch row, the k kept indices in
+ *     ascending order followed by -1 up to rmm_k_pad(k) entries, so a row of
+ *     an index list is rmm_k_pad(k) int32 words long.
+ */
+#ifndef RMM_H_
+#define RMM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RMM_OK = 0,
+  RMM_ERR_INVALID_ARG = 1, /* bad size, stride, pointer or ratio            */
+  RMM_ERR_UNSUPPORTED = 2, /* valid request this build does not serve       */
+  RMM_ERR_WORKSPACE = 3,   /* ws_bytes below the size the query returns     */
+  RMM_ERR_HIP = 4          /* the HIP runtime rejected a launch             */
+} rmm_status_t;
+
+typedef enum { RMM_BF16 = 0, RMM_F32 = 1 } rmm_dtype_t;
+
+/* A hipStream_t; NULL means the device's null stream. */
+typedef void *rmm_stream_t;
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int rmm_version(void);
+
+/* Static string naming a status code. */
+const char *rmm_status_string(int status);
+
+/* One-line description of the last failure on the calling thread ("" if none). */
+const char *rmm_last_error(void);
+
+/*
+ * rmm_k_from_rho - number of kept indices, k = ceil(rho * d).
+ * Source: "Estrategia de Selección" (k = ceil(rho d), rho the retention ratio).
+ * rho is read as the decimal the caller wrote: the exact product rho*d is
+ * formed, and when it lies within the representation error of rho (d * 2^-52)
+ * of an integer, that integer is k; otherwise k is the ceiling.  So rho = 0.55,
+ * d = 100 gives 55 (a naive binary product gives 56).
+ *   rho  in (0, 1]; d >= 1; k (host) receives the result, 1 <= k <= d.
+ * Returns RMM_ERR_INVALID_ARG for rho outside (0, 1] (or NaN), d < 1 or k NULL.
+ */
+rmm_status_t rmm_k_from_rho(double rho, int64_t d, int64_t *k);
+
+/* Length of one index-list row for k kept indices: k rounded up to a
+ * multiple of 64 (the K tile of the reduced GEMM).  Returns 0 for k < 1. */
+int64_t rmm_k_pad(int64_t k);
+
+/*
+ * rmm_colnorm - column scores s_j = ||A[:, j]||_2 over all m rows, for each of
+ * `batch` matrices.  Source: "Estrategia de Selección" (s_j = ||A_{:,j}||_2).
+ *   dt            RMM_BF16 or RMM_F32 element type of A.
+ *   A (device)    batch matrices of m x d; matrix b starts at A + b*batch_stride,
+ *                 row i of it at + i*lda.
+ *   lda >= d; batch >= 1; batch_stride >= 0 (any value when batch == 1).
+ *   scores (device, float) [batch][d], written.
+ * Accumulation is float32 in a fixed blocked order (per-lane partial sums over
+ * row subsets, combined by a fixed tree), then a correctly rounded sqrt.
+ */
+size_t rmm_colnorm_workspace_bytes(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch);
+rmm_status_t rmm_colnorm(rmm_dtype_t dt, const void *A, int64_t m, int64_t d, int64_t lda,
+                         int64_t batch, int64_t batch_stride, float *scores, void *ws,
+                         size_t ws_bytes, rmm_stream_t stream);
+
+/*
+ * rmm_topk - the k largest scores of each batch row.  Source: "Estrategia de
+ * Selección" (keep the top-k indices).  Ties at the k-th score go to the lower
+ * index; the output is in ascending index order.
+ *   scores (device, float) [batch][d].  Any finite values; -0.0 ranks as +0.0.
+ *   1 <= k <= d.
+ *   idx (device, int32) [batch][rmm_k_pad(k)]: row b receives its k indices
+ *   ascending, then -1 in the remaining rmm_k_pad(k) - k slots.
+ * Exact: the selection is a radix select on the float bit patterns, with no
+ * rounding anywhere.
+ */
+size_t rmm_topk_workspace_bytes(int64_t batch, int64_t d);
+rmm_status_t rmm_topk(const float *scores, int64_t batch, int64_t d, int64_t k, int32_t *idx,
+                      void *ws, size_t ws_bytes, rmm_stream_t stream);
+
+/*
+ * rmm_gemm - the reduced product Y = A[:, I] B[I, :] for one projection.
+ * Source: "Mecanismo Central" (compute A_{:,I} B_{I,:} in place of A B) and
+ * "Alcance de Aplicación" (hidden dimension of X W).  No rescaling.
+ *   dt           RMM_BF16 (float32 accumulation, bf16 output) or RMM_F32
+ *                (float32 throughout).
+ *   A (device)   m x d activation, leading dimension lda >= d.
+ *   B (device)   d x n weight stored with the contraction index as rows
+ *                (row t is B + t*ldb), ldb >= n.  B is only read: kept rows
+ *                are streamed as they lie in memory.
+ *   idx (device, int32) the kept indices; entries 0..k-1 are read (an index
+ *                list row from rmm_topk, or any k indices).  Entries outside
+ *                [0, d) contribute zero instead of being dereferenced.
+ *   1 <= k <= d; m, n >= 1.
+ *   Y (device)   m x n output of element type dt, leading dimension ldy >= n.
+ *   ws           at least rmm_gemm_workspace_bytes(dt, m, n, k) bytes; holds
+ *                the packed A[:, I].
+ */
+size_t rmm_gemm_workspace_bytes(rmm_dtype_t dt, int64_t m, int64_t n, int64_t k);
+rmm_status_t rmm_gemm(rmm_dtype_t dt, const void *A, int64_t lda, const void *B, int64_t ldb,
+                      const int32_t *idx, int64_t m, int64_t d, int64_t n, int64_t k, void *Y,
+                      int64_t ldy, void *ws, size_t ws_bytes, rmm_stream_t stream);
+
+/*
+ * rmm_qk - feature-reduced attention scores for every query head (bf16 in,
+ * float32 out).  Source: "Alcance de Aplicación" (reduce the feature dimension
+ * of Q K^T).  For query head h with kv head g = floor(h*Hkv/Hq):
+ *   s = column scores of Q_h over its Lq rows, I_h = top-k of s,
+ *   S_h = Q_h[:, I_h] Kt_g[I_h, :]   (no softmax scale applied).
+ *   Q (device, bf16)  element (t, h, j) at Q + t*q_tok_stride + h*q_head_stride + j.
+ *   Kt (device, bf16) keys stored feature-major: element (g, j, u) at
+ *                     Kt + g*kt_head_stride + j*ldkt + u, ldkt >= Lk.
+ *   Hq >= 1, 1 <= Hkv <= Hq, Hq % Hkv == 0; 1 <= k <= dh.
+ *   S (device, float) element (h, t, u) at S + h*s_head_stride + t*lds + u.
+ *   idx (device, int32) [Hq][rmm_k_pad(k)], written as by rmm_topk.
+ */
+size_t rmm_qk_workspace_bytes(int64_t Lq, int64_t Hq, int64_t dh, int64_t k);
+rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, int64_t q_tok_stride,
+                    int64_t q_head_stride, const void *Kt, int64_t Lk, int64_t Hkv,
+                    int64_t kt_head_stride, int64_t ldkt, int64_t k, float *S,
+                    int64_t s_head_stride, int64_t lds, int32_t *idx, void *ws, size_t ws_bytes,
+                    rmm_stream_t stream);
+
+/*
+ * rmm_pv - token-reduced attention output for every query head (bf16).
+ * Source: "Alcance de Aplicación" (optionally reduce the token dimension of
+ * P V).  For query head h with kv head g = floor(h*Hkv/Hq):
+ *   s = column scores of P_h over its Lq query rows, J_h = top-k tokens,
+ *   O_h = P_h[:, J_h] V_g[J_h, :].
+ *   P (device, bf16) element (h, t, u) at P + h*p_head_stride + t*ldp + u, ldp >= Lk.
+ *   V (device, bf16) element (u, g, j) at V + u*v_tok_stride + g*v_head_stride + j.
+ *   1 <= k <= Lk.
+ *   O (device, bf16) element (t, h, j) at O + t*o_tok_stride + h*o_head_stride + j.
+ *   idx (device, int32) [Hq][rmm_k_pad(k)], written as by rmm_topk.
+ */
+size_t rmm_pv_workspace_bytes(int64_t Hq, int64_t Lq, int64_t Lk, int64_t k);
+rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, int64_t p_head_stride,
+                    int64_t ldp, const void *V, int64_t Hkv, int64_t dh, int64_t v_tok_stride,
+                    int64_t v_head_stride, int64_t k, void *O, int64_t o_tok_stride,
+                    int64_t o_head_stride, int32_t *idx, void *ws, size_t ws_bytes,
+                    rmm_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMM_H_ */

@@ -1,0 +1,278 @@
+"""ctypes binding of librmm.so: argument marshalling only.
+
+Every computation runs in the library's HIP kernels; this module turns torch
+tensors into pointers, strides and sizes, allocates outputs and workspace with
+torch's device allocator, passes torch's current HIP stream, and raises
+``RMMError`` with the library's message when a call is rejected.  The C
+declarations and their contracts live in include/rmm.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "RMMError", "load", "lib_path",
+    "rmm_version", "rmm_k_from_rho", "rmm_k_pad",
+    "rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_qk", "rmm_pv",
+    "rmm_colnorm_workspace_bytes", "rmm_topk_workspace_bytes", "rmm_gemm_workspace_bytes",
+    "rmm_qk_workspace_bytes", "rmm_pv_workspace_bytes",
+    "rmm_linear",
+]
+
+RMM_BF16, RMM_F32 = 0, 1
+_STATUS = {0: "RMM_OK", 1: "RMM_ERR_INVALID_ARG", 2: "RMM_ERR_UNSUPPORTED", 3: "RMM_ERR_WORKSPACE",
+           4: "RMM_ERR_HIP"}
+
+_here = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_here, "librmm.so")
+_lib = None
+
+
+class RMMError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_i64, _f64, _sz, _vp = ctypes.c_int64, ctypes.c_double, ctypes.c_size_t, ctypes.c_void_p
+_PROTOS = {
+    "rmm_version": (ctypes.c_int, []),
+    "rmm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "rmm_last_error": (ctypes.c_char_p, []),
+    "rmm_k_from_rho": (ctypes.c_int, [_f64, _i64, ctypes.POINTER(_i64)]),
+    "rmm_k_pad": (_i64, [_i64]),
+    "rmm_colnorm_workspace_bytes": (_sz, [ctypes.c_int, _i64, _i64, _i64]),
+    "rmm_colnorm": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "rmm_topk_workspace_bytes": (_sz, [_i64, _i64]),
+    "rmm_topk": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "rmm_gemm_workspace_bytes": (_sz, [ctypes.c_int, _i64, _i64, _i64]),
+    "rmm_gemm": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp,
+                                _i64, _vp, _sz, _vp]),
+    "rmm_qk_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "rmm_qk": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
+                              _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "rmm_pv_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "rmm_pv": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
+                              _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
+}
+
+
+def load():
+    """Load librmm.so (built in-tree by __graft_entry__.build()); raise loudly if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise ImportError(f"RMM HIP library not built: {lib_path} is missing "
+                          "(run `python -c 'import __graft_entry__ as g; g.build()'`)")
+    lib = ctypes.CDLL(lib_path)
+    for name, (res, args) in _PROTOS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise RMMError(status, load().rmm_last_error().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return RMM_BF16
+    if t.dtype == torch.float32:
+        return RMM_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; RMM takes bfloat16 or float32")
+
+
+def _dev(*ts: torch.Tensor):
+    dev = ts[0].device
+    if dev.type != "cuda":
+        raise ValueError("RMM operands must live on a HIP device")
+    for t in ts:
+        if t.device != dev:
+            raise ValueError("RMM operands must share one device")
+    return dev
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ws(nbytes: int, dev, ws: torch.Tensor | None):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace too small: need {nbytes} bytes")
+    return ws, ws.numel() * ws.element_size()
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+# ------------------------------------------------------------------ scalars
+def rmm_version() -> int:
+    return load().rmm_version()
+
+
+def rmm_k_from_rho(rho: float, d: int) -> int:
+    k = _i64(0)
+    _check(load().rmm_k_from_rho(float(rho), int(d), ctypes.byref(k)))
+    return int(k.value)
+
+
+def rmm_k_pad(k: int) -> int:
+    return int(load().rmm_k_pad(int(k)))
+
+
+def rmm_colnorm_workspace_bytes(dtype: torch.dtype, m: int, d: int, batch: int = 1) -> int:
+    dt = RMM_BF16 if dtype == torch.bfloat16 else RMM_F32
+    return int(load().rmm_colnorm_workspace_bytes(dt, m, d, batch))
+
+
+def rmm_topk_workspace_bytes(batch: int, d: int) -> int:
+    return int(load().rmm_topk_workspace_bytes(batch, d))
+
+
+def rmm_gemm_workspace_bytes(dtype: torch.dtype, m: int, n: int, k: int) -> int:
+    dt = RMM_BF16 if dtype == torch.bfloat16 else RMM_F32
+    return int(load().rmm_gemm_workspace_bytes(dt, m, n, k))
+
+
+def rmm_qk_workspace_bytes(Lq: int, Hq: int, dh: int, k: int) -> int:
+    return int(load().rmm_qk_workspace_bytes(Lq, Hq, dh, k))
+
+
+def rmm_pv_workspace_bytes(Hq: int, Lq: int, Lk: int, k: int) -> int:
+    return int(load().rmm_pv_workspace_bytes(Hq, Lq, Lk, k))
+
+
+# ------------------------------------------------------------------ entry points
+def rmm_colnorm(A: torch.Tensor, out: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """Column scores of A [m, d] -> float32 [d], or of A [batch, m, d] -> [batch, d].
+
+    The last dimension must have unit stride; other strides are passed through.
+    """
+    lib = load()
+    dev = _dev(A)
+    squeeze = A.dim() == 2
+    A3 = A.unsqueeze(0) if squeeze else A
+    if A3.dim() != 3 or A3.stride(2) != 1:
+        raise ValueError("A must be [m, d] or [batch, m, d] with unit column stride")
+    batch, m, d = A3.shape
+    if out is None:
+        out = torch.empty((batch, d), dtype=torch.float32, device=dev)
+    dt = _dt(A)
+    ws, wsb = _ws(int(lib.rmm_colnorm_workspace_bytes(dt, m, d, batch)), dev, ws)
+    _check(lib.rmm_colnorm(dt, _ptr(A3), m, d, A3.stride(1), batch, A3.stride(0), _ptr(out), _ptr(ws), wsb,
+                           _stream(dev)))
+    return out[0] if squeeze else out
+
+
+def rmm_topk(scores: torch.Tensor, k: int, out: torch.Tensor | None = None):
+    """Top-k indices of scores [d] or [batch, d] -> int32 [k_pad] or [batch, k_pad]
+    (kept indices ascending, then -1)."""
+    lib = load()
+    dev = _dev(scores)
+    squeeze = scores.dim() == 1
+    s2 = scores.unsqueeze(0) if squeeze else scores
+    if s2.dtype != torch.float32 or not s2.is_contiguous():
+        raise ValueError("scores must be contiguous float32")
+    batch, d = s2.shape
+    kp = rmm_k_pad(k)
+    if out is None:
+        out = torch.empty((batch, max(kp, 1)), dtype=torch.int32, device=dev)
+    _check(lib.rmm_topk(_ptr(s2), batch, d, int(k), _ptr(out), None, 0, _stream(dev)))
+    return out[0] if squeeze else out
+
+
+def rmm_gemm(A: torch.Tensor, B: torch.Tensor, idx: torch.Tensor, k: int, out: torch.Tensor | None = None,
+             ws: torch.Tensor | None = None):
+    """Y = A[:, idx[:k]] @ B[idx[:k], :] for A [m, d], B [d, n] (same dtype)."""
+    lib = load()
+    dev = _dev(A, B, idx)
+    if A.dim() != 2 or B.dim() != 2 or A.stride(1) != 1 or B.stride(1) != 1:
+        raise ValueError("A [m, d] and B [d, n] must be 2-D with unit column stride")
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must share a dtype")
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be contiguous int32")
+    m, d = A.shape
+    d2, n = B.shape
+    if d2 != d:
+        raise ValueError("inner dimensions differ")
+    if out is None:
+        out = torch.empty((m, n), dtype=A.dtype, device=dev)
+    dt = _dt(A)
+    ws, wsb = _ws(int(lib.rmm_gemm_workspace_bytes(dt, m, n, int(k))), dev, ws)
+    _check(lib.rmm_gemm(dt, _ptr(A), A.stride(0), _ptr(B), B.stride(0), _ptr(idx), m, d, n, int(k), _ptr(out),
+                        out.stride(0), _ptr(ws), wsb, _stream(dev)))
+    return out
+
+
+def rmm_qk(Q: torch.Tensor, Kt: torch.Tensor, k: int, S: torch.Tensor | None = None,
+           idx: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """Feature-reduced scores. Q [Lq, Hq, dh], Kt [Hkv, dh, Lk] (bf16) ->
+    (S float32 [Hq, Lq, Lk], idx int32 [Hq, k_pad])."""
+    lib = load()
+    dev = _dev(Q, Kt)
+    if Q.dtype != torch.bfloat16 or Kt.dtype != torch.bfloat16:
+        raise TypeError("rmm_qk takes bfloat16 Q and Kt")
+    if Q.dim() != 3 or Kt.dim() != 3 or Q.stride(2) != 1 or Kt.stride(2) != 1:
+        raise ValueError("Q [Lq, Hq, dh] and Kt [Hkv, dh, Lk] need unit innermost stride")
+    Lq, Hq, dh = Q.shape
+    Hkv, dh2, Lk = Kt.shape
+    if dh2 != dh:
+        raise ValueError("head dims differ")
+    kp = rmm_k_pad(k)
+    if S is None:
+        S = torch.empty((Hq, Lq, Lk), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((Hq, kp), dtype=torch.int32, device=dev)
+    ws, wsb = _ws(int(lib.rmm_qk_workspace_bytes(Lq, Hq, dh, int(k))), dev, ws)
+    _check(lib.rmm_qk(_ptr(Q), Lq, Hq, dh, Q.stride(0), Q.stride(1), _ptr(Kt), Lk, Hkv, Kt.stride(0),
+                      Kt.stride(1), int(k), _ptr(S), S.stride(0), S.stride(1), _ptr(idx), _ptr(ws), wsb,
+                      _stream(dev)))
+    return S, idx
+
+
+def rmm_pv(P: torch.Tensor, V: torch.Tensor, k: int, O: torch.Tensor | None = None,
+           idx: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """Token-reduced output. P [Hq, Lq, Lk], V [Lk, Hkv, dh] (bf16) ->
+    (O bf16 [Lq, Hq, dh], idx int32 [Hq, k_pad])."""
+    lib = load()
+    dev = _dev(P, V)
+    if P.dtype != torch.bfloat16 or V.dtype != torch.bfloat16:
+        raise TypeError("rmm_pv takes bfloat16 P and V")
+    if P.dim() != 3 or V.dim() != 3 or P.stride(2) != 1 or V.stride(2) != 1:
+        raise ValueError("P [Hq, Lq, Lk] and V [Lk, Hkv, dh] need unit innermost stride")
+    Hq, Lq, Lk = P.shape
+    Lk2, Hkv, dh = V.shape
+    if Lk2 != Lk:
+        raise ValueError("token counts differ")
+    kp = rmm_k_pad(k)
+    if O is None:
+        O = torch.empty((Lq, Hq, dh), dtype=torch.bfloat16, device=dev)
+    if idx is None:
+        idx = torch.empty((Hq, kp), dtype=torch.int32, device=dev)
+    ws, wsb = _ws(int(lib.rmm_pv_workspace_bytes(Hq, Lq, Lk, int(k))), dev, ws)
+    _check(lib.rmm_pv(_ptr(P), Hq, Lq, Lk, P.stride(0), P.stride(1), _ptr(V), Hkv, dh, V.stride(0),
+                      V.stride(1), int(k), _ptr(O), O.stride(0), O.stride(1), _ptr(idx), _ptr(ws), wsb,
+                      _stream(dev)))
+    return O, idx
+
+
+def rmm_linear(A: torch.Tensor, B: torch.Tensor, rho: float):
+    """Whole reduced projection: scores -> top-k -> reduced GEMM. Returns (Y, idx, scores, k)."""
+    k = rmm_k_from_rho(rho, A.shape[1])
+    s = rmm_colnorm(A)
+    idx = rmm_topk(s, k)
+    return rmm_gemm(A, B, idx, k), idx, s, k

@@ -1,0 +1,354 @@
+// C ABI of the RMM hot path: argument validation, workspace sizing and the
+// launch sequence of every entry point.  Nothing here allocates device
+// memory, synchronises or reads device data back; every entry point enqueues
+// on the caller's stream and returns.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "rmm_internal.h"
+
+#define RMM_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+rmm_status_t fail(rmm_status_t s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+rmm_status_t fail(rmm_status_t s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+rmm_status_t ok() {
+  g_last_error[0] = '\0';
+  return RMM_OK;
+}
+
+rmm_status_t hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(RMM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+size_t esize(rmm_dtype_t dt) { return dt == RMM_BF16 ? 2 : 4; }
+bool dtype_ok(rmm_dtype_t dt) { return dt == RMM_BF16 || dt == RMM_F32; }
+bool aligned(const void *p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+constexpr int64_t kMaxBatch = 65535;
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // indices are int32
+
+inline size_t align256(size_t x) { return rmm::align_up(x, 256); }
+
+// Workspace carving: successive 256-byte aligned regions.
+struct Carve {
+  char *base;
+  size_t off = 0;
+  explicit Carve(void *p) : base(static_cast<char *>(p)) {}
+  void *take(size_t bytes) {
+    void *p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  }
+};
+
+rmm::ColnormPlan plan_for(rmm_dtype_t dt, const void *A, int64_t m, int64_t d, int64_t lda,
+                          int64_t batch, int64_t bs) {
+  const int64_t v = 16 / (int64_t)esize(dt);
+  const bool vec = aligned(A, 16) && lda % v == 0 && (batch == 1 || bs % v == 0);
+  return rmm::colnorm_plan(dt, m, d, batch, vec);
+}
+
+// Worst case over alignments: the scalar plan has the most chunks only when
+// the vector plan does not; take the max of both.
+size_t colnorm_ws(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch) {
+  const size_t a = rmm::colnorm_ws_bytes(rmm::colnorm_plan(dt, m, d, batch, true), d, batch);
+  const size_t b = rmm::colnorm_ws_bytes(rmm::colnorm_plan(dt, m, d, batch, false), d, batch);
+  return a > b ? a : b;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ misc
+RMM_API int rmm_version(void) { return 100; }
+
+RMM_API const char *rmm_status_string(int s) {
+  switch (s) {
+    case RMM_OK: return "RMM_OK";
+    case RMM_ERR_INVALID_ARG: return "RMM_ERR_INVALID_ARG";
+    case RMM_ERR_UNSUPPORTED: return "RMM_ERR_UNSUPPORTED";
+    case RMM_ERR_WORKSPACE: return "RMM_ERR_WORKSPACE";
+    case RMM_ERR_HIP: return "RMM_ERR_HIP";
+    default: return "RMM_ERR_UNKNOWN";
+  }
+}
+
+RMM_API const char *rmm_last_error(void) { return g_last_error; }
+
+RMM_API rmm_status_t rmm_k_from_rho(double rho, int64_t d, int64_t *k) {
+  if (!k) return fail(RMM_ERR_INVALID_ARG, "k_from_rho: k is NULL");
+  if (!(rho > 0.0 && rho <= 1.0)) return fail(RMM_ERR_INVALID_ARG, "k_from_rho: rho must lie in (0, 1]");
+  if (d < 1 || d >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "k_from_rho: d out of range");
+  // Exact product rho*d = hi + lo (error-free transformation with an fma).
+  const double dd = (double)d;
+  const double hi = rho * dd;
+  const double lo = fma(rho, dd, -hi);
+  const double n = nearbyint(hi);
+  // rho carries a relative representation error of at most 2^-53; its
+  // product with d is therefore within d*2^-53 of the decimal value.  Allow
+  // twice that before treating the product as a non-integer.
+  const double tol = dd * ldexp(1.0, -52);
+  int64_t kk;
+  if (fabs((hi - n) + lo) <= tol) {
+    kk = (int64_t)n;
+  } else {
+    double c = ceil(hi);
+    if (c == hi && lo > 0.0) c += 1.0;  // hi integral but the exact product exceeds it
+    kk = (int64_t)c;
+  }
+  if (kk < 1) kk = 1;
+  if (kk > d) kk = d;
+  *k = kk;
+  return ok();
+}
+
+RMM_API int64_t rmm_k_pad(int64_t k) {
+  if (k < 1) return 0;
+  return rmm::ceil_div(k, rmm::kKTile) * rmm::kKTile;
+}
+
+// ------------------------------------------------------------------ colnorm
+RMM_API size_t rmm_colnorm_workspace_bytes(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch) {
+  if (!dtype_ok(dt) || m < 1 || d < 1 || batch < 1) return 0;
+  return colnorm_ws(dt, m, d, batch);
+}
+
+static rmm_status_t check_colnorm(rmm_dtype_t dt, const void *A, int64_t m, int64_t d,
+                                  int64_t lda, int64_t batch, int64_t bs, const float *scores) {
+  if (!dtype_ok(dt)) return fail(RMM_ERR_INVALID_ARG, "colnorm: unknown dtype");
+  if (!A || !scores) return fail(RMM_ERR_INVALID_ARG, "colnorm: NULL pointer");
+  if (m < 1 || d < 1 || d >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "colnorm: need m >= 1 and 1 <= d < 2^31");
+  if (lda < d) return fail(RMM_ERR_INVALID_ARG, "colnorm: lda < d");
+  if (batch < 1 || batch > kMaxBatch) return fail(RMM_ERR_INVALID_ARG, "colnorm: batch out of [1, 65535]");
+  if (batch > 1 && bs < 0) return fail(RMM_ERR_INVALID_ARG, "colnorm: negative batch stride");
+  if (!aligned(A, esize(dt)) || !aligned(scores, 4)) return fail(RMM_ERR_INVALID_ARG, "colnorm: misaligned pointer");
+  return RMM_OK;
+}
+
+RMM_API rmm_status_t rmm_colnorm(rmm_dtype_t dt, const void *A, int64_t m, int64_t d, int64_t lda,
+                                 int64_t batch, int64_t bs, float *scores, void *ws,
+                                 size_t ws_bytes, rmm_stream_t stream) {
+  rmm_status_t s = check_colnorm(dt, A, m, d, lda, batch, bs, scores);
+  if (s != RMM_OK) return s;
+  const rmm::ColnormPlan p = plan_for(dt, A, m, d, lda, batch, bs);
+  const size_t need = rmm::colnorm_ws_bytes(p, d, batch);
+  if (need > ws_bytes || (need && !ws)) return fail(RMM_ERR_WORKSPACE, "colnorm: workspace needs %zu bytes", need);
+  return hip_status(rmm::launch_colnorm(dt, A, m, d, lda, batch, batch > 1 ? bs : 0, scores, ws, p,
+                                        (hipStream_t)stream),
+                    "colnorm launch");
+}
+
+// ------------------------------------------------------------------ top-k
+RMM_API size_t rmm_topk_workspace_bytes(int64_t, int64_t) { return 0; }
+
+RMM_API rmm_status_t rmm_topk(const float *scores, int64_t batch, int64_t d, int64_t k,
+                              int32_t *idx, void *, size_t, rmm_stream_t stream) {
+  if (!scores || !idx) return fail(RMM_ERR_INVALID_ARG, "topk: NULL pointer");
+  if (batch < 1 || batch > kMaxBatch) return fail(RMM_ERR_INVALID_ARG, "topk: batch out of [1, 65535]");
+  if (d < 1 || d >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "topk: d out of range");
+  if (k < 1 || k > d) return fail(RMM_ERR_INVALID_ARG, "topk: need 1 <= k <= d");
+  if (!aligned(scores, 4) || !aligned(idx, 4)) return fail(RMM_ERR_INVALID_ARG, "topk: misaligned pointer");
+  return hip_status(rmm::launch_topk(scores, batch, d, k, rmm_k_pad(k), idx, (hipStream_t)stream),
+                    "topk launch");
+}
+
+// ------------------------------------------------------------------ gemm
+RMM_API size_t rmm_gemm_workspace_bytes(rmm_dtype_t dt, int64_t m, int64_t n, int64_t k) {
+  (void)n;
+  if (!dtype_ok(dt) || m < 1 || k < 1) return 0;
+  return align256((size_t)m * (size_t)rmm_k_pad(k) * esize(dt));
+}
+
+RMM_API rmm_status_t rmm_gemm(rmm_dtype_t dt, const void *A, int64_t lda, const void *B,
+                              int64_t ldb, const int32_t *idx, int64_t m, int64_t d, int64_t n,
+                              int64_t k, void *Y, int64_t ldy, void *ws, size_t ws_bytes,
+                              rmm_stream_t stream) {
+  if (!dtype_ok(dt)) return fail(RMM_ERR_INVALID_ARG, "gemm: unknown dtype");
+  if (!A || !B || !idx || !Y) return fail(RMM_ERR_INVALID_ARG, "gemm: NULL pointer");
+  if (m < 1 || n < 1 || d < 1 || d >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "gemm: bad m, n or d");
+  if (k < 1 || k > d) return fail(RMM_ERR_INVALID_ARG, "gemm: need 1 <= k <= d");
+  if (lda < d || ldb < n || ldy < n) return fail(RMM_ERR_INVALID_ARG, "gemm: leading dimension too small");
+  const size_t e = esize(dt);
+  if (!aligned(A, e) || !aligned(B, e) || !aligned(Y, e) || !aligned(idx, 4))
+    return fail(RMM_ERR_INVALID_ARG, "gemm: misaligned pointer");
+  const size_t need = rmm_gemm_workspace_bytes(dt, m, n, k);
+  if (!ws || ws_bytes < need || !aligned(ws, 16)) return fail(RMM_ERR_WORKSPACE, "gemm: workspace needs %zu bytes (16-byte aligned)", need);
+  const int64_t k_pad = rmm_k_pad(k);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t he = rmm::launch_pack(dt, A, lda, 0, idx, 0, 1, m, d, k, k_pad, ws, st);
+  if (he != hipSuccess) return hip_status(he, "gemm pack launch");
+  rmm::GemmArgs g{};
+  g.A = ws;
+  g.idx = idx;
+  g.idx_stride = 0;
+  g.B = B;
+  g.ldb = ldb;
+  g.b_batch_stride = 0;
+  g.Y = Y;
+  g.ldy = ldy;
+  g.y_batch_stride = 0;
+  g.batch = 1;
+  g.hq = 1;
+  g.hkv = 1;
+  g.m = m;
+  g.n = n;
+  g.d = d;
+  g.k = k;
+  g.k_pad = k_pad;
+  he = dt == RMM_BF16 ? rmm::launch_gemm_bf16(g, rmm::OutType::BF16, st) : rmm::launch_gemm_f32(g, st);
+  return hip_status(he, "gemm launch");
+}
+
+// ------------------------------------------------------------------ attention
+static size_t qk_layout(int64_t Lq, int64_t Hq, int64_t dh, int64_t k, size_t *o_scores,
+                        size_t *o_part, size_t *o_pack) {
+  Carve c(nullptr);
+  *o_scores = c.off;
+  c.take((size_t)Hq * dh * 4);
+  *o_part = c.off;
+  c.take(colnorm_ws(RMM_BF16, Lq, dh, Hq));
+  *o_pack = c.off;
+  c.take((size_t)Hq * Lq * rmm_k_pad(k) * 2);
+  return c.off;
+}
+
+RMM_API size_t rmm_qk_workspace_bytes(int64_t Lq, int64_t Hq, int64_t dh, int64_t k) {
+  if (Lq < 1 || Hq < 1 || dh < 1 || k < 1) return 0;
+  size_t a, b, c;
+  return qk_layout(Lq, Hq, dh, k, &a, &b, &c);
+}
+
+RMM_API rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, int64_t q_tok_stride,
+                            int64_t q_head_stride, const void *Kt, int64_t Lk, int64_t Hkv,
+                            int64_t kt_head_stride, int64_t ldkt, int64_t k, float *S,
+                            int64_t s_head_stride, int64_t lds, int32_t *idx, void *ws,
+                            size_t ws_bytes, rmm_stream_t stream) {
+  if (!Q || !Kt || !S || !idx) return fail(RMM_ERR_INVALID_ARG, "qk: NULL pointer");
+  if (Lq < 1 || Lk < 1 || dh < 1 || Lk >= kMaxDim || dh >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "qk: bad Lq, Lk or dh");
+  if (Hq < 1 || Hq > kMaxBatch || Hkv < 1 || Hkv > Hq || Hq % Hkv != 0)
+    return fail(RMM_ERR_INVALID_ARG, "qk: need 1 <= Hkv <= Hq <= 65535 and Hq %% Hkv == 0");
+  if (k < 1 || k > dh) return fail(RMM_ERR_INVALID_ARG, "qk: need 1 <= k <= dh");
+  if (q_tok_stride < 0 || q_head_stride < 0 || kt_head_stride < 0 || s_head_stride < 0)
+    return fail(RMM_ERR_INVALID_ARG, "qk: negative stride");
+  if (ldkt < Lk || lds < Lk || q_tok_stride < dh) return fail(RMM_ERR_INVALID_ARG, "qk: leading dimension too small");
+  if (!aligned(Q, 2) || !aligned(Kt, 2) || !aligned(S, 4) || !aligned(idx, 4))
+    return fail(RMM_ERR_INVALID_ARG, "qk: misaligned pointer");
+  size_t o_sc, o_part, o_pack;
+  const size_t need = qk_layout(Lq, Hq, dh, k, &o_sc, &o_part, &o_pack);
+  if (!ws || ws_bytes < need || !aligned(ws, 256)) return fail(RMM_ERR_WORKSPACE, "qk: workspace needs %zu bytes (256-byte aligned)", need);
+  char *w = static_cast<char *>(ws);
+  float *scores = reinterpret_cast<float *>(w + o_sc);
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t k_pad = rmm_k_pad(k);
+
+  const rmm::ColnormPlan p = plan_for(RMM_BF16, Q, Lq, dh, q_tok_stride, Hq, q_head_stride);
+  hipError_t he = rmm::launch_colnorm(RMM_BF16, Q, Lq, dh, q_tok_stride, Hq, q_head_stride, scores,
+                                      w + o_part, p, st);
+  if (he != hipSuccess) return hip_status(he, "qk colnorm launch");
+  he = rmm::launch_topk(scores, Hq, dh, k, k_pad, idx, st);
+  if (he != hipSuccess) return hip_status(he, "qk topk launch");
+  he = rmm::launch_pack(RMM_BF16, Q, q_tok_stride, q_head_stride, idx, k_pad, Hq, Lq, dh, k, k_pad,
+                        w + o_pack, st);
+  if (he != hipSuccess) return hip_status(he, "qk pack launch");
+  rmm::GemmArgs g{};
+  g.A = w + o_pack;
+  g.idx = idx;
+  g.idx_stride = k_pad;
+  g.B = Kt;
+  g.ldb = ldkt;
+  g.b_batch_stride = kt_head_stride;
+  g.Y = S;
+  g.ldy = lds;
+  g.y_batch_stride = s_head_stride;
+  g.batch = Hq;
+  g.hq = Hq;
+  g.hkv = Hkv;
+  g.m = Lq;
+  g.n = Lk;
+  g.d = dh;
+  g.k = k;
+  g.k_pad = k_pad;
+  return hip_status(rmm::launch_gemm_bf16(g, rmm::OutType::F32, st), "qk gemm launch");
+}
+
+static size_t pv_layout(int64_t Hq, int64_t Lq, int64_t Lk, int64_t k, size_t *o_scores,
+                        size_t *o_part, size_t *o_pack) {
+  Carve c(nullptr);
+  *o_scores = c.off;
+  c.take((size_t)Hq * Lk * 4);
+  *o_part = c.off;
+  c.take(colnorm_ws(RMM_BF16, Lq, Lk, Hq));
+  *o_pack = c.off;
+  c.take((size_t)Hq * Lq * rmm_k_pad(k) * 2);
+  return c.off;
+}
+
+RMM_API size_t rmm_pv_workspace_bytes(int64_t Hq, int64_t Lq, int64_t Lk, int64_t k) {
+  if (Lq < 1 || Hq < 1 || Lk < 1 || k < 1) return 0;
+  size_t a, b, c;
+  return pv_layout(Hq, Lq, Lk, k, &a, &b, &c);
+}
+
+RMM_API rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, int64_t p_head_stride,
+                            int64_t ldp, const void *V, int64_t Hkv, int64_t dh,
+                            int64_t v_tok_stride, int64_t v_head_stride, int64_t k, void *O,
+                            int64_t o_tok_stride, int64_t o_head_stride, int32_t *idx, void *ws,
+                            size_t ws_bytes, rmm_stream_t stream) {
+  if (!P || !V || !O || !idx) return fail(RMM_ERR_INVALID_ARG, "pv: NULL pointer");
+  if (Lq < 1 || Lk < 1 || dh < 1 || Lk >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "pv: bad Lq, Lk or dh");
+  if (Hq < 1 || Hq > kMaxBatch || Hkv < 1 || Hkv > Hq || Hq % Hkv != 0)
+    return fail(RMM_ERR_INVALID_ARG, "pv: need 1 <= Hkv <= Hq <= 65535 and Hq %% Hkv == 0");
+  if (k < 1 || k > Lk) return fail(RMM_ERR_INVALID_ARG, "pv: need 1 <= k <= Lk");
+  if (p_head_stride < 0 || v_tok_stride < 0 || v_head_stride < 0 || o_tok_stride < 0 || o_head_stride < 0)
+    return fail(RMM_ERR_INVALID_ARG, "pv: negative stride");
+  if (ldp < Lk) return fail(RMM_ERR_INVALID_ARG, "pv: ldp < Lk");
+  if (!aligned(P, 2) || !aligned(V, 2) || !aligned(O, 2) || !aligned(idx, 4))
+    return fail(RMM_ERR_INVALID_ARG, "pv: misaligned pointer");
+  size_t o_sc, o_part, o_pack;
+  const size_t need = pv_layout(Hq, Lq, Lk, k, &o_sc, &o_part, &o_pack);
+  if (!ws || ws_bytes < need || !aligned(ws, 256)) return fail(RMM_ERR_WORKSPACE, "pv: workspace needs %zu bytes (256-byte aligned)", need);
+  char *w = static_cast<char *>(ws);
+  float *scores = reinterpret_cast<float *>(w + o_sc);
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t k_pad = rmm_k_pad(k);
+
+  const rmm::ColnormPlan p = plan_for(RMM_BF16, P, Lq, Lk, ldp, Hq, p_head_stride);
+  hipError_t he = rmm::launch_colnorm(RMM_BF16, P, Lq, Lk, ldp, Hq, p_head_stride, scores, w + o_part, p, st);
+  if (he != hipSuccess) return hip_status(he, "pv colnorm launch");
+  he = rmm::launch_topk(scores, Hq, Lk, k, k_pad, idx, st);
+  if (he != hipSuccess) return hip_status(he, "pv topk launch");
+  he = rmm::launch_pack(RMM_BF16, P, ldp, p_head_stride, idx, k_pad, Hq, Lq, Lk, k, k_pad, w + o_pack, st);
+  if (he != hipSuccess) return hip_status(he, "pv pack launch");
+  rmm::GemmArgs g{};
+  g.A = w + o_pack;
+  g.idx = idx;
+  g.idx_stride = k_pad;
+  g.B = V;
+  g.ldb = v_tok_stride;
+  g.b_batch_stride = v_head_stride;
+  g.Y = O;
+  g.ldy = o_tok_stride;
+  g.y_batch_stride = o_head_stride;
+  g.batch = Hq;
+  g.hq = Hq;
+  g.hkv = Hkv;
+  g.m = Lq;
+  g.n = dh;
+  g.d = Lk;
+  g.k = k;
+  g.k_pad = k_pad;
+  return hip_status(rmm::launch_gemm_bf16(g, rmm::OutType::BF16, st), "pv gemm launch");
+}

@@ -1,0 +1,222 @@
+// Column scores s_j = ||A[:, j]||_2 ("Estrategia de Selección": the importance of
+// contraction index j is the Euclidean norm of activation column j).
+//
+// HBM-bound streaming reduction.  Each lane owns `VEC` adjacent columns and
+// loads 16 bytes per row, so a wave reads 64 x 16 B = 1 KiB of contiguous row
+// segment(s): for d >= 512 (bf16) a wave covers one row per step; for narrow
+// matrices (head_dim 128) it covers 64/TPR rows at once and the lanes that
+// share a column are folded with cross-lane xor shuffles at the end.  The
+// four waves of a block then meet in LDS.  Rows are split into chunks over
+// gridDim.y to put a few thousand blocks on the 256 CUs; per-chunk partial
+// sums land in the workspace and a small second kernel adds them in chunk
+// order and takes the square root, so the result is bitwise deterministic.
+#include "rmm_internal.h"
+
+namespace rmm {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+template <typename T, int VEC>
+struct Loader;
+
+// bf16, 8 per lane: one 16-byte load.
+template <>
+struct Loader<uint16_t, 8> {
+  __device__ static void load_sq(const uint16_t *p, int64_t c0, int64_t d, float *acc) {
+    if (c0 + 8 <= d) {
+      uint4 v = *reinterpret_cast<const uint4 *>(p);
+      float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                    bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(x[e], x[e], acc[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (c0 + e < d) {
+          float x = bf16_to_f32(p[e]);
+          acc[e] = fmaf(x, x, acc[e]);
+        }
+    }
+  }
+};
+
+// f32, 4 per lane: one 16-byte load.
+template <>
+struct Loader<float, 4> {
+  __device__ static void load_sq(const float *p, int64_t c0, int64_t d, float *acc) {
+    if (c0 + 4 <= d) {
+      float4 v = *reinterpret_cast<const float4 *>(p);
+      acc[0] = fmaf(v.x, v.x, acc[0]);
+      acc[1] = fmaf(v.y, v.y, acc[1]);
+      acc[2] = fmaf(v.z, v.z, acc[2]);
+      acc[3] = fmaf(v.w, v.w, acc[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (c0 + e < d) acc[e] = fmaf(p[e], p[e], acc[e]);
+    }
+  }
+};
+
+// Scalar fallback for layouts that forbid 16-byte loads.
+template <typename T>
+struct Loader<T, 1> {
+  __device__ static void load_sq(const T *p, int64_t c0, int64_t d, float *acc) {
+    if (c0 < d) {
+      float x;
+      if constexpr (sizeof(T) == 2) x = bf16_to_f32(*p);
+      else x = *p;
+      acc[0] = fmaf(x, x, acc[0]);
+    }
+  }
+};
+
+// grid: x = column tile (TPR*VEC columns), y = row chunk, z = batch.
+// out: partial sums [chunk][batch][d] (or final scores when `final_sqrt`).
+template <typename T, int VEC, int TPR>
+__global__ __launch_bounds__(kThreads) void colnorm_kernel(const T *__restrict__ A, int64_t m,
+                                                           int64_t d, int64_t lda,
+                                                           int64_t batch_stride,
+                                                           int64_t rows_per_chunk,
+                                                           float *__restrict__ out,
+                                                           int final_sqrt) {
+  constexpr int RPW = 64 / TPR;       // rows one wave covers per step
+  constexpr int RPB = kWaves * RPW;   // rows the block covers per step
+  constexpr int CT = TPR * VEC;       // columns per block
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane / TPR;
+  const int cl = lane % TPR;
+  const int64_t col0 = (int64_t)blockIdx.x * CT;
+  const int64_t c0 = col0 + (int64_t)cl * VEC;
+  const int64_t r_begin = (int64_t)blockIdx.y * rows_per_chunk;
+  const int64_t r_end = min(m, r_begin + rows_per_chunk);
+  const T *Ab = A + (int64_t)blockIdx.z * batch_stride + c0;
+
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+
+  if (c0 < d) {
+    int64_t r = r_begin + wave * RPW + sub;
+    // four rows in flight per lane
+    for (; r + 3 * RPB < r_end; r += 4 * RPB) {
+      const T *p = Ab + r * lda;
+      Loader<T, VEC>::load_sq(p, c0, d, acc);
+      Loader<T, VEC>::load_sq(p + RPB * lda, c0, d, acc);
+      Loader<T, VEC>::load_sq(p + 2 * RPB * lda, c0, d, acc);
+      Loader<T, VEC>::load_sq(p + 3 * RPB * lda, c0, d, acc);
+    }
+    for (; r < r_end; r += RPB) Loader<T, VEC>::load_sq(Ab + r * lda, c0, d, acc);
+  }
+
+  // Fold the lanes that share a column (lane, lane^TPR, lane^2TPR, ...).
+#pragma unroll
+  for (int off = TPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
+  }
+
+  __shared__ float red[kWaves][CT];
+  if (sub == 0) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) red[wave][cl * VEC + e] = acc[e];
+  }
+  __syncthreads();
+  float *o = out + ((int64_t)blockIdx.y * gridDim.z + blockIdx.z) * d;
+  for (int c = threadIdx.x; c < CT; c += kThreads) {
+    const int64_t col = col0 + c;
+    if (col < d) {
+      float s = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
+      o[col] = final_sqrt ? __builtin_sqrtf(s) : s;
+    }
+  }
+}
+
+// scores[b][j] = sqrt(sum over chunks, in chunk order, of part[c][b][j]).
+__global__ __launch_bounds__(256) void colnorm_finish(const float *__restrict__ part,
+                                                      int64_t chunks, int64_t n,
+                                                      float *__restrict__ scores) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int64_t c = 0; c < chunks; ++c) s += part[c * n + i];
+  scores[i] = __builtin_sqrtf(s);
+}
+
+template <typename T, int VEC>
+hipError_t dispatch_tpr(int tpr, dim3 grid, const T *A, int64_t m, int64_t d, int64_t lda,
+                        int64_t bs, int64_t rpc, float *out, int fin, hipStream_t st) {
+  switch (tpr) {
+#define RMM_CN(TP)                                                                       \
+  case TP:                                                                               \
+    hipLaunchKernelGGL((colnorm_kernel<T, VEC, TP>), grid, dim3(kThreads), 0, st, A, m, d, \
+                       lda, bs, rpc, out, fin);                                          \
+    break;
+    RMM_CN(1) RMM_CN(2) RMM_CN(4) RMM_CN(8) RMM_CN(16) RMM_CN(32) RMM_CN(64)
+#undef RMM_CN
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch, bool vec_ok) {
+  ColnormPlan p;
+  const int esz = dt == RMM_BF16 ? 2 : 4;
+  p.vec = vec_ok ? 16 / esz : 1;
+  const int64_t lanes_needed = ceil_div(d, p.vec);
+  int tpr = 1;
+  while (tpr < 64 && tpr < lanes_needed) tpr <<= 1;
+  p.tpr = tpr;
+  p.col_tiles = ceil_div(d, (int64_t)tpr * p.vec);
+  const int64_t rpb = (int64_t)kWaves * (64 / tpr);
+  // Aim for ~2048 blocks, but give each block at least 8 steps of rows.
+  const int64_t tiles = p.col_tiles * batch;
+  int64_t want_chunks = ceil_div(2048, tiles);
+  int64_t max_chunks = ceil_div(m, rpb * 8);
+  int64_t chunks = want_chunks < max_chunks ? want_chunks : max_chunks;
+  if (chunks < 1) chunks = 1;
+  if (chunks > 65535) chunks = 65535;
+  int64_t rpc = ceil_div(ceil_div(m, chunks), rpb) * rpb;
+  p.rows_per_chunk = rpc;
+  p.chunks = ceil_div(m, rpc);
+  return p;
+}
+
+size_t colnorm_ws_bytes(const ColnormPlan &p, int64_t d, int64_t batch) {
+  return p.chunks > 1 ? (size_t)p.chunks * (size_t)batch * (size_t)d * sizeof(float) : 0;
+}
+
+hipError_t launch_colnorm(rmm_dtype_t dt, const void *A, int64_t m, int64_t d, int64_t lda,
+                          int64_t batch, int64_t batch_stride, float *scores, void *ws,
+                          const ColnormPlan &p, hipStream_t st) {
+  const bool single = p.chunks == 1;
+  float *out = single ? scores : static_cast<float *>(ws);
+  dim3 grid((unsigned)p.col_tiles, (unsigned)p.chunks, (unsigned)batch);
+  hipError_t e;
+  if (dt == RMM_BF16) {
+    const uint16_t *a = static_cast<const uint16_t *>(A);
+    e = p.vec == 8 ? dispatch_tpr<uint16_t, 8>(p.tpr, grid, a, m, d, lda, batch_stride,
+                                                p.rows_per_chunk, out, single, st)
+                   : dispatch_tpr<uint16_t, 1>(p.tpr, grid, a, m, d, lda, batch_stride,
+                                               p.rows_per_chunk, out, single, st);
+  } else {
+    const float *a = static_cast<const float *>(A);
+    e = p.vec == 4 ? dispatch_tpr<float, 4>(p.tpr, grid, a, m, d, lda, batch_stride,
+                                             p.rows_per_chunk, out, single, st)
+                   : dispatch_tpr<float, 1>(p.tpr, grid, a, m, d, lda, batch_stride,
+                                            p.rows_per_chunk, out, single, st);
+  }
+  if (e != hipSuccess || single) return e;
+  const int64_t n = batch * d;
+  hipLaunchKernelGGL(colnorm_finish, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st,
+                     static_cast<const float *>(ws), p.chunks, n, scores);
+  return hipGetLastError();
+}
+
+}  // namespace rmm

@@ -1,0 +1,70 @@
+// Internal declarations shared by the RMM kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rmm.h"
+
+namespace rmm {
+
+// ---------------------------------------------------------------- bf16 helpers
+// bf16 values travel as raw 16-bit words.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int64_t kKTile = 64;  // K tile of the reduced GEMM; index rows are padded to it
+
+// ------------------------------------------------------------------ colnorm
+struct ColnormPlan {
+  int vec;               // elements per lane load (8 bf16 / 4 f32 / 1 scalar)
+  int tpr;               // lanes per row (power of two <= 64)
+  int64_t col_tiles;     // ceil(d / (tpr*vec))
+  int64_t rows_per_chunk;
+  int64_t chunks;        // row chunks; partial sums per chunk when > 1
+};
+ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch, bool vec_ok);
+size_t colnorm_ws_bytes(const ColnormPlan &p, int64_t d, int64_t batch);
+hipError_t launch_colnorm(rmm_dtype_t dt, const void *A, int64_t m, int64_t d, int64_t lda,
+                          int64_t batch, int64_t batch_stride, float *scores, void *ws,
+                          const ColnormPlan &p, hipStream_t stream);
+
+// ------------------------------------------------------------------ top-k
+hipError_t launch_topk(const float *scores, int64_t batch, int64_t d, int64_t k, int64_t k_pad,
+                       int32_t *idx, hipStream_t stream);
+
+// ------------------------------------------------------------------ pack
+// out[b][i][t] = A[b][i][idx[b][t]] for t < k (0 when idx is out of [0,d)), 0 for k <= t < k_pad.
+hipError_t launch_pack(rmm_dtype_t dt, const void *A, int64_t lda, int64_t a_batch_stride,
+                       const int32_t *idx, int64_t idx_batch_stride, int64_t batch, int64_t m,
+                       int64_t d, int64_t k, int64_t k_pad, void *out, hipStream_t stream);
+
+// ------------------------------------------------------------------ gathered GEMM
+struct GemmArgs {
+  const void *A;          // packed [batch][m][k_pad]
+  const int32_t *idx;     // [batch][idx_stride]
+  int64_t idx_stride;
+  const void *B;          // rows gathered via idx: B + g*b_batch_stride + idx*ldb
+  int64_t ldb, b_batch_stride;
+  void *Y;                // Y + b*y_batch_stride + i*ldy + j
+  int64_t ldy, y_batch_stride;
+  int64_t batch, hq, hkv; // batch b reads B group floor(b*hkv/hq)
+  int64_t m, n, d, k, k_pad;
+};
+enum class OutType { BF16, F32 };
+hipError_t launch_gemm_bf16(const GemmArgs &a, OutType out, hipStream_t stream);
+hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t stream);
+
+}  // namespace rmm

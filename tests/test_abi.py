@@ -1,0 +1,145 @@
+"""The C ABI on the host: the library loads, exports what include/rmm.h declares,
+computes k like the oracle, and rejects bad arguments before enqueuing anything.
+
+No test here launches a kernel; the error paths return during host-side
+validation, so they run without a GPU.
+"""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from input_adaptive_reduced_rmm_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rmm.h")
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation rejects the call first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.lib_path):
+        pytest.fail("librmm.so is not built (run __graft_entry__.build())")
+    return B.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rmm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_entry_points():
+    syms = declared_symbols()
+    for name in ("rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_qk", "rmm_pv"):
+        assert name in syms
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    # and the binding wraps each entry point under the same name
+    for name in ("rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_qk", "rmm_pv", "rmm_k_from_rho", "rmm_k_pad"):
+        assert callable(getattr(B, name))
+
+
+def test_status_strings(lib):
+    assert lib.rmm_status_string(0) == b"RMM_OK"
+    assert lib.rmm_status_string(3) == b"RMM_ERR_WORKSPACE"
+    assert lib.rmm_version() >= 100
+
+
+def test_k_from_rho_matches_oracle_table(lib):
+    rows = json.load(open(os.path.join(ROOT, "tests", "golden", "retained_counts.json")))
+    for r in rows["rows"] + rows["decimal_traps"]:
+        assert B.rmm_k_from_rho(r["rho"], r["d"]) == r["k"], r
+
+
+def test_k_from_rho_matches_oracle_on_random_decimals(lib):
+    rng = np.random.default_rng(21)
+    for _ in range(3000):
+        q = int(rng.integers(1, 5))
+        p = int(rng.integers(1, 10 ** q + 1))
+        rho = float(f"{p}e-{q}")
+        d = int(rng.integers(1, 200000))
+        assert B.rmm_k_from_rho(rho, d) == oracle.retained_count(rho, d), (rho, d)
+
+
+@pytest.mark.parametrize("rho,d", [(0.0, 10), (-0.5, 10), (1.5, 10), (float("nan"), 10), (0.5, 0)])
+def test_k_from_rho_rejects(lib, rho, d):
+    with pytest.raises(B.RMMError) as e:
+        B.rmm_k_from_rho(rho, d)
+    assert e.value.status == 1
+
+
+def test_k_pad(lib):
+    assert [B.rmm_k_pad(k) for k in (0, 1, 63, 64, 65, 1434, 11469)] == [0, 64, 64, 64, 128, 1472, 11520]
+
+
+def _st(x):
+    return int(x)
+
+
+def test_colnorm_rejects(lib):
+    f = lib.rmm_colnorm
+    assert f(0, None, 4, 4, 4, 1, 0, FAKE, None, 0, None) == 1          # NULL A
+    assert f(0, FAKE, 4, 8, 4, 1, 0, FAKE, None, 0, None) == 1          # lda < d
+    assert f(0, FAKE, 0, 8, 8, 1, 0, FAKE, None, 0, None) == 1          # m = 0
+    assert f(7, FAKE, 4, 8, 8, 1, 0, FAKE, None, 0, None) == 1          # unknown dtype
+    assert f(0, FAKE, 4, 8, 8, 70000, 8, FAKE, None, 0, None) == 1      # batch too large
+    assert f(1, ctypes.c_void_p(0x10002), 4, 8, 8, 1, 0, FAKE, None, 0, None) == 1   # f32 misaligned
+    need = lib.rmm_colnorm_workspace_bytes(0, 65536, 4096, 1)
+    assert need > 0
+    assert f(0, FAKE, 65536, 4096, 4096, 1, 0, FAKE, FAKE, need - 1, None) == 3
+    assert b"workspace" in lib.rmm_last_error()
+
+
+def test_topk_rejects(lib):
+    f = lib.rmm_topk
+    assert f(FAKE, 1, 10, 0, FAKE, None, 0, None) == 1
+    assert f(FAKE, 1, 10, 11, FAKE, None, 0, None) == 1
+    assert f(None, 1, 10, 5, FAKE, None, 0, None) == 1
+    assert f(FAKE, 0, 10, 5, FAKE, None, 0, None) == 1
+    assert lib.rmm_topk_workspace_bytes(4, 1000) == 0
+
+
+def test_gemm_rejects(lib):
+    f = lib.rmm_gemm
+    args = dict(dt=0, A=FAKE, lda=64, B=FAKE, ldb=32, idx=FAKE, m=16, d=64, n=32, k=8, Y=FAKE, ldy=32)
+    def call(ws=FAKE, wsb=1 << 30, **kw):
+        a = {**args, **kw}
+        return f(a["dt"], a["A"], a["lda"], a["B"], a["ldb"], a["idx"], a["m"], a["d"], a["n"], a["k"], a["Y"],
+                 a["ldy"], ws, wsb, None)
+    assert call(k=0) == 1
+    assert call(k=65) == 1
+    assert call(lda=63) == 1
+    assert call(ldb=31) == 1
+    assert call(ldy=31) == 1
+    assert call(idx=None) == 1
+    assert call(dt=5) == 1
+    need = lib.rmm_gemm_workspace_bytes(0, 16, 32, 8)
+    assert need == 16 * 64 * 2
+    assert call(wsb=need - 1) == 3
+    assert call(ws=None) == 3
+
+
+def test_qk_pv_reject(lib):
+    q = lib.rmm_qk
+    # Hq % Hkv != 0
+    assert q(FAKE, 64, 6, 128, 768, 128, FAKE, 64, 4, 8192, 64, 32, FAKE, 4096, 64, FAKE, FAKE, 1 << 30, None) == 1
+    # k > dh
+    assert q(FAKE, 64, 4, 128, 512, 128, FAKE, 64, 2, 8192, 64, 129, FAKE, 4096, 64, FAKE, FAKE, 1 << 30, None) == 1
+    # q_tok_stride < dh
+    assert q(FAKE, 64, 4, 128, 100, 128, FAKE, 64, 2, 8192, 64, 64, FAKE, 4096, 64, FAKE, FAKE, 1 << 30, None) == 1
+    need = lib.rmm_qk_workspace_bytes(64, 4, 128, 64)
+    assert q(FAKE, 64, 4, 128, 512, 128, FAKE, 64, 2, 8192, 64, 64, FAKE, 4096, 64, FAKE, FAKE, need - 1, None) == 3
+    p = lib.rmm_pv
+    assert p(FAKE, 4, 64, 64, 4096, 64, FAKE, 2, 128, 256, 128, 65, FAKE, 512, 128, FAKE, FAKE, 1 << 30, None) == 1
+    assert p(FAKE, 4, 64, 64, 4096, 63, FAKE, 2, 128, 256, 128, 32, FAKE, 512, 128, FAKE, FAKE, 1 << 30, None) == 1
+    need = lib.rmm_pv_workspace_bytes(4, 64, 64, 32)
+    assert need >= 4 * 64 * 64 * 2
+    assert p(FAKE, 4, 64, 64, 4096, 64, FAKE, 2, 128, 256, 128, 32, FAKE, 512, 128, FAKE, FAKE, need - 1, None) == 3
