@@ -1,0 +1,427 @@
+#!/usr/bin/env python3
+"""Throughput of the RMM hot path on one MI355X.
+
+One step = one pass of every reduced product of a layer over one batch of
+synthetic input already resident in HBM: for each projection, column scores ->
+top-k -> reduced GEMM (q/k/v share one selection, up/gate share one, since
+the scores depend on A only); then the feature-reduced Q K^T and the
+token-reduced P V over all heads.  The attention probabilities P are a
+precomputed input (a causal softmax of the layer's logits), like X.
+
+Prints one JSON line.  `value` is effective TFLOP/s: the dense-equivalent
+flops of the step (2 m d n per projection, 2 Lq Lk dh per attention product
+and head) divided by the measured step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "llama3.1-8b-layer-16k"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--rho", type=float, default=None, help="projection ratio filter (multi-ratio workloads)")
+    ap.add_argument("--m", type=int, default=None, help="token-count filter (multi-m workloads)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the rho = 1 pass")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ workload
+def build_layer(wl, args, dev):
+    import numpy as np
+    import torch
+
+    import synth
+
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    lins = list(wl.linears)
+    if args.rho is not None:
+        lins = [l for l in lins if abs(l.rho - args.rho) < 1e-12]
+    elif wl.key == "llama3.2-1b-proj-2k":
+        lins = [l for l in lins if l.rho == 0.5]
+    if wl.key == "llama3.1-70b-layer":
+        m = args.m if args.m is not None else 8192
+        rho = args.rho if args.rho is not None else 0.5
+        lins = [l for l in wl.linears if l.m == m and abs(l.rho - rho) < 1e-12]
+    layer = {"linears": [], "attention": None, "dtype": dt}
+    acts = {}
+    for lin in lins:
+        key = synth.activation_key(wl, lin)
+        if key not in acts:
+            acts[key] = torch.from_numpy(synth.linear_activation(wl, lin)).to(dev, dt)
+        layer["linears"].append({
+            "name": lin.name, "m": lin.m, "d": lin.d, "n": lin.n, "rho": lin.rho,
+            "A": acts[key], "akey": key, "B": torch.from_numpy(synth.linear_weight(wl, lin)).to(dev, dt),
+        })
+    if wl.attention is not None and (wl.key != "llama3.1-70b-layer" or args.m in (None, 8192)):
+        at = wl.attention
+        Q, Kt, V = synth.attention_operands(wl)
+        Qd = torch.from_numpy(Q).to(dev, torch.bfloat16)
+        Ktd = torch.from_numpy(Kt).to(dev, torch.bfloat16)
+        Vd = torch.from_numpy(V).to(dev, torch.bfloat16)
+        del Q, Kt, V
+        P = synth.causal_probs(Qd, Ktd, 1.0 / math.sqrt(at.dh), device=dev)
+        layer["attention"] = {"Q": Qd, "Kt": Ktd, "V": Vd, "P": P, "L": at.L, "Hq": at.Hq, "Hkv": at.Hkv,
+                              "dh": at.dh, "rho": at.rho}
+    return layer
+
+
+class Runner:
+    """Holds outputs/workspaces for one ratio setting and runs a step."""
+
+    def __init__(self, R, layer, dev, rho_scale_one=False):
+        import torch
+
+        self.R, self.layer, self.dev = R, layer, dev
+        dt = layer["dtype"]
+        self.plan = []
+        self.sel = {}
+        ws_cn = ws_g = 0
+        for lin in layer["linears"]:
+            k = lin["d"] if rho_scale_one else R.rmm_k_from_rho(lin["rho"], lin["d"])
+            skey = (lin["akey"], k)
+            if skey not in self.sel:
+                self.sel[skey] = {
+                    "scores": torch.empty(lin["d"], dtype=torch.float32, device=dev),
+                    "idx": torch.empty(R.rmm_k_pad(k), dtype=torch.int32, device=dev),
+                    "owner": lin["name"],
+                }
+                ws_cn = max(ws_cn, R.rmm_colnorm_workspace_bytes(dt, lin["m"], lin["d"], 1))
+            ws_g = max(ws_g, R.rmm_gemm_workspace_bytes(dt, lin["m"], lin["n"], k))
+            self.plan.append({**lin, "k": k, "skey": skey,
+                              "Y": torch.empty((lin["m"], lin["n"]), dtype=dt, device=dev)})
+        self.ws_cn = torch.empty(max(ws_cn, 1), dtype=torch.uint8, device=dev)
+        self.ws_g = torch.empty(max(ws_g, 1), dtype=torch.uint8, device=dev)
+        at = layer["attention"]
+        self.att = None
+        if at is not None:
+            kf = at["dh"] if rho_scale_one else R.rmm_k_from_rho(at["rho"], at["dh"])
+            kt = at["L"] if rho_scale_one else R.rmm_k_from_rho(at["rho"], at["L"])
+            self.att = {
+                "kf": kf, "kt": kt,
+                "S": torch.empty((at["Hq"], at["L"], at["L"]), dtype=torch.float32, device=dev),
+                "O": torch.empty((at["L"], at["Hq"], at["dh"]), dtype=torch.bfloat16, device=dev),
+                "iq": torch.empty((at["Hq"], R.rmm_k_pad(kf)), dtype=torch.int32, device=dev),
+                "ip": torch.empty((at["Hq"], R.rmm_k_pad(kt)), dtype=torch.int32, device=dev),
+                "wq": torch.empty(R.rmm_qk_workspace_bytes(at["L"], at["Hq"], at["dh"], kf), dtype=torch.uint8,
+                                  device=dev),
+                "wp": torch.empty(R.rmm_pv_workspace_bytes(at["Hq"], at["L"], at["L"], kt), dtype=torch.uint8,
+                                  device=dev),
+            }
+
+    def free(self):
+        self.plan = self.sel = self.att = None
+        self.ws_cn = self.ws_g = None
+
+    def step(self, tagged=False):
+        R = self.R
+        T = R.timing
+        done = set()
+        for p in self.plan:
+            s = self.sel[p["skey"]]
+            if p["skey"] not in done:
+                if tagged:
+                    T.tag(p["name"].split("@")[0])
+                R.rmm_colnorm(p["A"], out=s["scores"], ws=self.ws_cn)
+                R.rmm_topk(s["scores"], p["k"], out=s["idx"])
+                done.add(p["skey"])
+            if tagged:
+                T.tag(p["name"].split("@")[0])
+            R.rmm_gemm(p["A"], p["B"], s["idx"], p["k"], out=p["Y"], ws=self.ws_g)
+        if self.att is not None:
+            at, a = self.layer["attention"], self.att
+            if tagged:
+                T.tag("qk")
+            R.rmm_qk(at["Q"], at["Kt"], a["kf"], S=a["S"], idx=a["iq"], ws=a["wq"])
+            if tagged:
+                T.tag("pv")
+            R.rmm_pv(at["P"], at["V"], a["kt"], O=a["O"], idx=a["ip"], ws=a["wp"])
+        if tagged:
+            T.tag(None)
+
+
+def dense_flops(layer):
+    f = sum(2.0 * l["m"] * l["d"] * l["n"] for l in layer["linears"])
+    at = layer["attention"]
+    if at is not None:
+        f += 2 * (2.0 * at["L"] * at["L"] * at["dh"] * at["Hq"])
+    return f
+
+
+def time_steps(runner, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        runner.step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def kernel_breakdown(runner, steps):
+    """Per tag/kernel average launch durations (HIP events recorded by the library)."""
+    import torch
+
+    R = runner.R
+    R.timing.reset()
+    R.timing.enable(True)
+    for _ in range(steps):
+        runner.step(tagged=True)
+    torch.cuda.synchronize()
+    R.timing.enable(False)
+    tot = R.timing.collect()
+    R.timing.reset()
+    return {k: {"avg_ms": v[0] / v[1], "launches_per_step": v[1] / steps} for k, v in tot.items()}
+
+
+def algorithmic_work(runner, key):
+    """(bound, amount per launch, unit) for a tag/kernel entry of the step."""
+    tag, kern = key.split("/", 1) if "/" in key else ("", key)
+    at = runner.layer["attention"]
+    a = runner.att
+    if tag == "qk" and kern.startswith("gemm"):
+        per_head = at["L"] * a["kf"] * 2 + a["kf"] * at["L"] * 2 + at["L"] * at["L"] * 4
+        return "hbm", per_head * at["Hq"], "bytes"
+    if tag == "pv" and kern.startswith("gemm"):
+        per_head = at["L"] * a["kt"] * 2 + a["kt"] * at["dh"] * 2 + at["L"] * at["dh"] * 2
+        return "hbm", per_head * at["Hq"], "bytes"
+    if tag == "pv" and kern == "colnorm":
+        return "hbm", at["Hq"] * (at["L"] * at["L"] * 2 + 4 * at["L"]), "bytes"
+    if tag == "pv" and kern == "pack":
+        return "hbm", at["Hq"] * at["L"] * a["kt"] * 2 * 2, "bytes"
+    if tag == "qk" and kern == "colnorm":
+        return "hbm", at["Hq"] * (at["L"] * at["dh"] * 2 + 4 * at["dh"]), "bytes"
+    if tag == "qk" and kern == "pack":
+        return "hbm", at["Hq"] * at["L"] * a["kf"] * 2 * 2, "bytes"
+    plans = [p for p in runner.plan if p["name"].split("@")[0] == tag]
+    if not plans:
+        return None, 0, None
+    p = plans[0]
+    e = 4 if runner.layer["dtype"].itemsize == 4 else 2
+    if kern.startswith("gemm"):
+        return "mfma", 2.0 * p["m"] * p["k"] * p["n"], "flops"
+    if kern == "colnorm":
+        return "hbm", p["m"] * p["d"] * e + 4 * p["d"], "bytes"
+    if kern == "pack":
+        return "hbm", p["m"] * p["k"] * e * 2, "bytes"
+    return None, 0, None
+
+
+def cpu_baseline(wl, layer_meta):
+    """Time the CPU oracle on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max(i["num_threads"] for i in blas) if blas else os.cpu_count()
+    except Exception:
+        cores = os.cpu_count()
+    lins = layer_meta["linears"]
+    m_s = min(4096, min(l.m for l in lins)) if lins else 0
+    parts = []
+    flops = 0.0
+    t_total = 0.0
+    for lin in lins:
+        A, B = synth.linear_operands(wl, lin, m=m_s)
+        t0 = time.perf_counter()
+        oracle.rmm(A, B, lin.rho)
+        t_total += time.perf_counter() - t0
+        flops += 2.0 * m_s * lin.d * lin.n
+    if lins:
+        parts.append(f"{len(lins)} projections on the first {m_s} tokens")
+    at = layer_meta["attention"]
+    if at is not None:
+        Ls = min(8192, at.L)
+        Q, Kt, V = synth.attention_operands(wl, L=Ls, Hq=1, Hkv=1)
+        t0 = time.perf_counter()
+        oracle.attention_chain(Q, Kt, V, at.rho)
+        t_total += time.perf_counter() - t0
+        flops += 2 * 2.0 * Ls * Ls * at.dh
+        parts.append(f"reduced attention (QK^T, softmax, PV) of 1 head at {Ls} tokens")
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": "; ".join(parts) + f" (float64 NumPy oracle, {t_total:.1f} s)", "seconds": round(t_total, 2)}
+
+
+def copy_calibration(dev):
+    import torch
+
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import input_adaptive_reduced_rmm_amd as R
+    import synth
+
+    R.load()
+    if not torch.cuda.is_available():
+        print("no HIP device visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    layer = build_layer(wl, args, dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    if args.copy_calibration:
+        copy_calibration(dev)
+
+    run = Runner(R, layer, dev)
+    ms, wall = time_steps(run, args.steps, args.warmup)
+    print(f"[bench] rho step {ms:.3f} ms (wall {wall:.3f})", file=sys.stderr, flush=True)
+    kern = kernel_breakdown(run, max(2, min(args.steps, 5)))
+    flops = dense_flops(layer)
+    # Dominant kernel and its roofline.
+    detail = {}
+    best = None
+    for key, v in kern.items():
+        bound, amount, unit = algorithmic_work(run, key)
+        tot = v["avg_ms"] * v["launches_per_step"]
+        ent = {"avg_ms": round(v["avg_ms"], 4), "per_step": v["launches_per_step"]}
+        if bound:
+            rate = amount / (v["avg_ms"] * 1e-3)
+            if unit == "flops":
+                ent["tflops"] = round(rate / 1e12, 1)
+                ent["frac"] = round(rate / 1e12 / PEAK_BF16_TFLOPS, 4)
+            else:
+                ent["gbs"] = round(rate / 1e9, 1)
+                ent["frac"] = round(rate / 1e9 / PEAK_HBM_GBS, 4)
+        detail[key] = ent
+        if bound and (best is None or tot > best[0]):
+            best = (tot, key, bound, amount, unit, v["avg_ms"])
+    roof = None
+    if best:
+        _, key, bound, amount, unit, avg = best
+        if unit == "flops":
+            peak = PEAK_F32_TFLOPS if layer["dtype"] == torch.float32 else PEAK_BF16_TFLOPS
+            ach = amount / (avg * 1e-3) / 1e12
+            roof = {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(ach / peak, 4), "traffic": None, "kernel": key,
+                    "per_launch": f"{amount:.4g} flops", "avg_launch_ms": round(avg, 4)}
+        else:
+            ach = amount / (avg * 1e-3) / 1e9
+            roof = {"bound": bound, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": key,
+                    "per_launch": f"{amount:.4g} bytes", "avg_launch_ms": round(avg, 4)}
+    # Kept-work MFMA fraction over all projection GEMMs.
+    g_fl = g_ms = 0.0
+    for key, v in kern.items():
+        bound, amount, unit = algorithmic_work(run, key)
+        if unit == "flops":
+            g_fl += amount * v["launches_per_step"]
+            g_ms += v["avg_ms"] * v["launches_per_step"]
+    mfma_frac = (g_fl / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS) if g_ms > 0 else None
+    run.free()
+    del run
+    torch.cuda.empty_cache()
+
+    speedup = dense_ms = None
+    if not args.no_dense:
+        run1 = Runner(R, layer, dev, rho_scale_one=True)
+        dense_ms, _ = time_steps(run1, args.steps, args.warmup)
+        speedup = dense_ms / ms
+        print(f"[bench] rho=1 step {dense_ms:.3f} ms", file=sys.stderr, flush=True)
+        run1.free()
+        del run1
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        del layer
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline(wl, {"linears": [l for l in wl.linears if l in _selected(wl, args)],
+                                "attention": wl.attention if _has_attention(wl, args) else None})
+
+    value = flops / (ms * 1e-3) / 1e12
+    cfg = {"workload": wl.key, "dtype": wl.dtype, "rho": _rho_desc(wl, args),
+           "products": _products_desc(wl, args)}
+    out = {
+        "metric": "effective TFLOP/s (dense-equivalent flops / RMM step time)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32", "data": "synthetic (seeded; shapes and value "
+        "distributions of the pages' model families)", "config": cfg,
+        "speedup_vs_rho1": round(speedup, 3) if speedup else None,
+        "rho1_ms_per_step": round(dense_ms, 4) if dense_ms else None,
+        "gemm_kept_mfma_frac": round(mfma_frac, 4) if mfma_frac is not None else None,
+        "roofline": roof, "cpu_baseline": cpu, "kernels": detail,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _selected(wl, args):
+    lins = list(wl.linears)
+    if wl.key == "llama3.1-70b-layer":
+        m = args.m if args.m is not None else 8192
+        rho = args.rho if args.rho is not None else 0.5
+        return [l for l in lins if l.m == m and abs(l.rho - rho) < 1e-12]
+    if args.rho is not None:
+        return [l for l in lins if abs(l.rho - args.rho) < 1e-12]
+    if wl.key == "llama3.2-1b-proj-2k":
+        return [l for l in lins if l.rho == 0.5]
+    return lins
+
+
+def _has_attention(wl, args):
+    return wl.attention is not None and (wl.key != "llama3.1-70b-layer" or args.m in (None, 8192))
+
+
+def _rho_desc(wl, args):
+    rs = sorted({l.rho for l in _selected(wl, args)})
+    d = {"projections": rs}
+    if _has_attention(wl, args):
+        d["attention"] = wl.attention.rho
+    return d
+
+
+def _products_desc(wl, args):
+    out = [f"{l.name.split('@')[0]} {l.m}x{l.d}x{l.n}" for l in _selected(wl, args)]
+    if _has_attention(wl, args):
+        at = wl.attention
+        out.append(f"QK^T+PV L={at.L} Hq={at.Hq} Hkv={at.Hkv} dh={at.dh}")
+    return out
+
+
+if __name__ == "__main__":
+    main()

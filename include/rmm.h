@@ -184,6 +184,31 @@ rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, int64_t p
                     int64_t o_head_stride, int32_t *idx, void *ws, size_t ws_bytes,
                     rmm_stream_t stream);
 
+/*
+ * Per-kernel timing diagnostics (not part of the method; for measurement).
+ * When enabled, each kernel the library enqueues is bracketed by two HIP
+ * events recorded on its launch stream and filed under "<tag>/<kernel>"
+ * (just "<kernel>" while the calling thread's tag is empty).
+ *   rmm_timing_enable(on)     start (on != 0) or stop recording.
+ *   rmm_timing_set_tag(tag)   label for later launches from this thread (host
+ *                             string, copied; NULL or "" clears it).
+ *   rmm_timing_collect()      wait for every recorded launch and add its
+ *                             elapsed time to the totals (host-blocking).
+ *   rmm_timing_count()        number of distinct "<tag>/<kernel>" totals.
+ *   rmm_timing_entry(i, ...)  name (host buffer of name_len bytes), summed
+ *                             milliseconds and launch count of total i.
+ *   rmm_timing_reset()        clear the totals.
+ * HIP events are created on first use and reused; no device memory is
+ * allocated.  Recording adds two event records per launch.
+ */
+rmm_status_t rmm_timing_enable(int on);
+rmm_status_t rmm_timing_set_tag(const char *tag);
+rmm_status_t rmm_timing_collect(void);
+int rmm_timing_count(void);
+rmm_status_t rmm_timing_entry(int i, char *name, size_t name_len, double *total_ms,
+                              int64_t *launches);
+rmm_status_t rmm_timing_reset(void);
+
 #ifdef __cplusplus
 }
 #endif

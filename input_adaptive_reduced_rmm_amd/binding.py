@@ -19,7 +19,7 @@ __all__ = [
     "rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_qk", "rmm_pv",
     "rmm_colnorm_workspace_bytes", "rmm_topk_workspace_bytes", "rmm_gemm_workspace_bytes",
     "rmm_qk_workspace_bytes", "rmm_pv_workspace_bytes",
-    "rmm_linear",
+    "rmm_linear", "timing",
 ]
 
 RMM_BF16, RMM_F32 = 0, 1
@@ -55,6 +55,13 @@ _PROTOS = {
     "rmm_qk": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
                               _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
     "rmm_pv_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "rmm_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+    "rmm_timing_set_tag": (ctypes.c_int, [ctypes.c_char_p]),
+    "rmm_timing_collect": (ctypes.c_int, []),
+    "rmm_timing_count": (ctypes.c_int, []),
+    "rmm_timing_entry": (ctypes.c_int, [ctypes.c_int, ctypes.c_char_p, _sz, ctypes.POINTER(_f64),
+                                        ctypes.POINTER(_i64)]),
+    "rmm_timing_reset": (ctypes.c_int, []),
     "rmm_pv": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
                               _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
 }
@@ -276,3 +283,32 @@ def rmm_linear(A: torch.Tensor, B: torch.Tensor, rho: float):
     s = rmm_colnorm(A)
     idx = rmm_topk(s, k)
     return rmm_gemm(A, B, idx, k), idx, s, k
+
+
+class timing:
+    """Per-kernel HIP-event timing inside the library (see rmm_timing_* in rmm.h)."""
+
+    @staticmethod
+    def enable(on: bool = True):
+        _check(load().rmm_timing_enable(1 if on else 0))
+
+    @staticmethod
+    def tag(name: str | None):
+        _check(load().rmm_timing_set_tag(name.encode() if name else None))
+
+    @staticmethod
+    def reset():
+        _check(load().rmm_timing_reset())
+
+    @staticmethod
+    def collect() -> dict:
+        """Wait for recorded launches; return {"tag/kernel": (total_ms, launches)}."""
+        lib = load()
+        _check(lib.rmm_timing_collect())
+        out = {}
+        buf = ctypes.create_string_buffer(256)
+        for i in range(lib.rmm_timing_count()):
+            ms, n = _f64(0.0), _i64(0)
+            _check(lib.rmm_timing_entry(i, buf, 256, ctypes.byref(ms), ctypes.byref(n)))
+            out[buf.value.decode()] = (ms.value, n.value)
+        return out

@@ -11,6 +11,7 @@
 // sums land in the workspace and a small second kernel adds them in chunk
 // order and takes the square root, so the result is bitwise deterministic.
 #include "rmm_internal.h"
+#include "timing.h"
 
 namespace rmm {
 namespace {
@@ -149,6 +150,7 @@ __global__ __launch_bounds__(256) void colnorm_finish(const float *__restrict__ 
 template <typename T, int VEC>
 hipError_t dispatch_tpr(int tpr, dim3 grid, const T *A, int64_t m, int64_t d, int64_t lda,
                         int64_t bs, int64_t rpc, float *out, int fin, hipStream_t st) {
+  KernelTimer timer("colnorm", st);
   switch (tpr) {
 #define RMM_CN(TP)                                                                       \
   case TP:                                                                               \
@@ -214,6 +216,7 @@ hipError_t launch_colnorm(rmm_dtype_t dt, const void *A, int64_t m, int64_t d, i
   }
   if (e != hipSuccess || single) return e;
   const int64_t n = batch * d;
+  KernelTimer timer("colnorm_finish", st);
   hipLaunchKernelGGL(colnorm_finish, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st,
                      static_cast<const float *>(ws), p.chunks, n, scores);
   return hipGetLastError();

@@ -16,7 +16,10 @@
 //
 // f32 path (MFMA v_mfma_f32_16x16x4f32): 64 x 64 x 16 tiles, one element per
 // lane per operand, so no transposition is needed.
+#include <type_traits>
+
 #include "rmm_internal.h"
+#include "timing.h"
 
 namespace rmm {
 namespace {
@@ -270,6 +273,7 @@ hipError_t launch_bm(const GemmArgs &g, bool bvec, hipStream_t st) {
   constexpr int BN = 128;
   const int64_t tiles = ((g.m + BM - 1) / BM) * ((g.n + BN - 1) / BN);
   dim3 grid((unsigned)tiles, 1, (unsigned)g.batch);
+  KernelTimer timer(std::is_same<OUT, float>::value ? "gemm_bf16_f32out" : "gemm_bf16", st);
   if (bvec)
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, OUT, true>), grid, dim3(256), 0, st, g);
   else
@@ -288,6 +292,7 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, OutType out, hipStream_t st) {
 
 hipError_t launch_gemm_f32(const GemmArgs &g, hipStream_t st) {
   const int64_t tiles = ((g.m + kFBM - 1) / kFBM) * ((g.n + kFBN - 1) / kFBN);
+  KernelTimer timer("gemm_f32", st);
   hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)tiles, 1, (unsigned)g.batch), dim3(256), 0,
                      st, g);
   return hipGetLastError();

@@ -9,6 +9,7 @@
 // addresses of the same source row and a wave's gathers fall in a few cache
 // lines.  Stores are full 16-byte, fully coalesced.
 #include "rmm_internal.h"
+#include "timing.h"
 
 namespace rmm {
 namespace {
@@ -86,6 +87,7 @@ hipError_t launch_pack(rmm_dtype_t dt, const void *A, int64_t lda, int64_t a_bs,
   const int64_t rpb = ceil_div(m, row_blocks);
   row_blocks = ceil_div(m, rpb);
   dim3 grid((unsigned)col_blocks, (unsigned)row_blocks, (unsigned)batch);
+  KernelTimer timer("pack", st);
   if (dt == RMM_BF16)
     hipLaunchKernelGGL(pack_kernel<uint16_t>, grid, dim3(kThreads), 0, st,
                        static_cast<const uint16_t *>(A), lda, a_bs, idx, idx_bs, m, d, k, k_pad,

@@ -11,6 +11,7 @@
 // give every thread its output offset and how many of its == T keys it may
 // take (the lowest-index ones win).  All integer work: the result is exact.
 #include "rmm_internal.h"
+#include "timing.h"
 
 namespace rmm {
 namespace {
@@ -181,6 +182,7 @@ __global__ __launch_bounds__(256) void iota_kernel(int64_t d, int64_t k_pad, int
 
 hipError_t launch_topk(const float *scores, int64_t batch, int64_t d, int64_t k, int64_t k_pad,
                        int32_t *idx, hipStream_t st) {
+  KernelTimer timer("topk", st);
   if (k == d) {
     unsigned gx = (unsigned)ceil_div(k_pad, 256);
     if (gx > 1024) gx = 1024;

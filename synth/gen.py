@@ -49,25 +49,31 @@ def normal(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
 
 
 def outlier_activations(rng: np.random.Generator, m: int, d: int, frac: float, factor: float,
-                        bf16: bool = True) -> np.ndarray:
+                        bf16: bool = True, col_rng: np.random.Generator | None = None) -> np.ndarray:
     """N(0,1) activations with round(frac*d) outlier channels multiplied by ``factor``.
 
-    The outlier channels are drawn uniformly without replacement from the same
-    stream, after the body.
+    The outlier channels are drawn uniformly without replacement from
+    ``col_rng`` (by default the body's stream, after the body).  With a
+    separate ``col_rng`` the first m' rows of an m-row draw equal the m'-row
+    draw.
     """
     a = normal(rng, (m, d))
     n_out = int(round(frac * d))
     if n_out > 0:
-        cols = rng.choice(d, size=n_out, replace=False)
+        cols = (col_rng if col_rng is not None else rng).choice(d, size=n_out, replace=False)
         a[:, cols] *= np.float32(factor)
     return bf16_round(a) if bf16 else a
 
 
 def lognormal_col_activations(rng: np.random.Generator, m: int, d: int, sigma: float,
-                              bf16: bool = True) -> np.ndarray:
-    """A[i, j] = z[i, j] * c[j] with z ~ N(0,1) and c[j] = exp(N(0, sigma^2))."""
+                              bf16: bool = True, col_rng: np.random.Generator | None = None) -> np.ndarray:
+    """A[i, j] = z[i, j] * c[j] with z ~ N(0,1) and c[j] = exp(N(0, sigma^2)).
+
+    The column scales come from ``col_rng`` when given (then row prefixes are
+    stable across m), else from ``rng`` after the body.
+    """
     z = normal(rng, (m, d))
-    c = np.exp(sigma * rng.standard_normal(d)).astype(np.float32)
+    c = np.exp(sigma * (col_rng if col_rng is not None else rng).standard_normal(d)).astype(np.float32)
     a = z * c[None, :]
     return bf16_round(a) if bf16 else a
 

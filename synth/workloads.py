@@ -15,7 +15,8 @@ import numpy as np
 from .gen import (attention_qkv, bf16_round, lognormal_col_activations, normal,
                   outlier_activations, stream, weight)
 
-__all__ = ["Linear", "Attention", "Workload", "WORKLOADS", "linear_operands", "attention_operands"]
+__all__ = ["Linear", "Attention", "Workload", "WORKLOADS", "linear_operands", "linear_activation",
+           "linear_weight", "activation_key", "attention_operands"]
 
 
 @dataclass(frozen=True)
@@ -106,27 +107,39 @@ WORKLOADS = {
 
 
 def _activation(w: Workload, seed: int, tensor_id: int, m: int, d: int) -> np.ndarray:
+    """Activation matrix; the column-level draws (outlier channels, column
+    scales) use their own stream, so the first m' rows do not depend on m."""
     rng = stream(seed, w.wid, tensor_id * 100003 + d)
+    col_rng = stream(seed, w.wid, tensor_id * 100003 + d + 50000)
     bf16 = w.dtype == "bf16"
     if w.act == "outlier":
-        return outlier_activations(rng, m, d, w.act_frac, w.act_factor, bf16=bf16)
+        return outlier_activations(rng, m, d, w.act_frac, w.act_factor, bf16=bf16, col_rng=col_rng)
     if w.act == "lognormal1":
-        return lognormal_col_activations(rng, m, d, w.act_sigma, bf16=bf16)
+        return lognormal_col_activations(rng, m, d, w.act_sigma, bf16=bf16, col_rng=col_rng)
     a = normal(rng, (m, d))
     return bf16_round(a) if bf16 else a
 
 
-def linear_operands(w: Workload, lin: Linear, seed: int = 0, m: int | None = None):
-    """(A [m, d], B [d, n]) for one projection of workload ``w`` (float32 arrays).
+def linear_weight(w: Workload, lin: Linear, seed: int = 0) -> np.ndarray:
+    """B [d, n] of one projection (rows are the contraction index)."""
+    return weight(stream(seed, w.wid, lin.tensor_b * 100003 + lin.d * 7 + lin.n), lin.d, lin.n,
+                  bf16=w.dtype == "bf16")
 
-    ``m`` overrides the token count (same distributions, fewer rows).  For the
-    LLaMA-3.2-1B workload the down-projection input is the SiLU-gated MLP
-    activation silu(X Wg) * (X Wu), formed in float32 from the workload's bf16
-    X, Wg and Wu and rounded to bf16.
-    """
+
+def activation_key(w: Workload, lin: Linear, m: int | None = None):
+    """Projections with equal keys read the same activation matrix."""
     m = lin.m if m is None else m
-    bf16 = w.dtype == "bf16"
-    B = weight(stream(seed, w.wid, lin.tensor_b * 100003 + lin.d * 7 + lin.n), lin.d, lin.n, bf16=bf16)
+    if lin.name.startswith("down") and w.silu_down:
+        return ("silu", m, lin.d)
+    return (lin.tensor_a, m, lin.d)
+
+
+def linear_activation(w: Workload, lin: Linear, seed: int = 0, m: int | None = None) -> np.ndarray:
+    """A [m, d] of one projection.  ``m`` overrides the token count (same
+    distributions, fewer rows).  For the LLaMA-3.2-1B workload the
+    down-projection input is the SiLU-gated MLP activation silu(X Wg) * (X Wu),
+    formed in float32 from the workload's bf16 X, Wg and Wu, rounded to bf16."""
+    m = lin.m if m is None else m
     if lin.name.startswith("down") and w.silu_down:
         hidden = lin.n
         X = _activation(w, seed, 20, m, hidden)
@@ -134,10 +147,13 @@ def linear_operands(w: Workload, lin: Linear, seed: int = 0, m: int | None = Non
         Wg = weight(stream(seed, w.wid, 6 * 100003 + hidden * 7 + lin.d), hidden, lin.d)
         g = X @ Wg
         u = X @ Wu
-        A = bf16_round((g / (1.0 + np.exp(-g))) * u)
-        return A, B
-    A = _activation(w, seed, lin.tensor_a, m, lin.d)
-    return A, B
+        return bf16_round((g / (1.0 + np.exp(-g))) * u)
+    return _activation(w, seed, lin.tensor_a, m, lin.d)
+
+
+def linear_operands(w: Workload, lin: Linear, seed: int = 0, m: int | None = None):
+    """(A [m, d], B [d, n]) for one projection of workload ``w`` (float32 arrays)."""
+    return linear_activation(w, lin, seed, m), linear_weight(w, lin, seed)
 
 
 def attention_operands(w: Workload, seed: int = 0, L: int | None = None, Hq: int | None = None,

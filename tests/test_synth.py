@@ -41,3 +41,11 @@ def test_workload_shapes_small():
     assert A2.shape == (64, 8192) and B2.shape == (8192, 2048)
     Q, Kt, V = synth.attention_operands(synth.WORKLOADS["llama3.1-8b-layer-16k"], L=64)
     assert Q.shape == (64, 32, 128) and Kt.shape == (8, 128, 64) and V.shape == (64, 8, 128)
+
+
+def test_row_prefix_is_stable_across_m():
+    w = synth.WORKLOADS["llama3.1-8b-layer-16k"]
+    lin = w.linears[0]
+    a = synth.linear_activation(w, lin, m=40)
+    b = synth.linear_activation(w, lin, m=13)
+    np.testing.assert_array_equal(a[:13], b)
