@@ -137,8 +137,9 @@ rmm_status_t rmm_topk(const float *scores, int64_t batch, int64_t d, int64_t k, 
  *                [0, d) contribute zero instead of being dereferenced.
  *   1 <= k <= d; m, n >= 1.
  *   Y (device)   m x n output of element type dt, leading dimension ldy >= n.
- *   ws           at least rmm_gemm_workspace_bytes(dt, m, n, k) bytes; holds
- *                the packed A[:, I].
+ *   ws           at least rmm_gemm_workspace_bytes(dt, m, n, k) bytes,
+ *                256-byte aligned; holds the packed A[:, I] and a cleaned
+ *                copy of the k indices.
  */
 size_t rmm_gemm_workspace_bytes(rmm_dtype_t dt, int64_t m, int64_t n, int64_t k);
 rmm_status_t rmm_gemm(rmm_dtype_t dt, const void *A, int64_t lda, const void *B, int64_t ldb,
@@ -173,9 +174,17 @@ rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, int64_t q
  *   O_h = P_h[:, J_h] V_g[J_h, :].
  *   P (device, bf16) element (h, t, u) at P + h*p_head_stride + t*ldp + u, ldp >= Lk.
  *   V (device, bf16) element (u, g, j) at V + u*v_tok_stride + g*v_head_stride + j.
- *   1 <= k <= Lk.
+ *   1 <= k <= Lk <= 524288 (RMM_ERR_UNSUPPORTED above).
+ *   Layouts with 16-byte aligned rows (bases on 16-byte boundaries, strides
+ *   multiples of 8) use 16-byte loads; others take a slower path with the
+ *   same results.  256 rows of P (256*ldp elements) and the rows of one V
+ *   head must each span less than 4 GiB (RMM_ERR_UNSUPPORTED otherwise).
  *   O (device, bf16) element (t, h, j) at O + t*o_tok_stride + h*o_head_stride + j.
  *   idx (device, int32) [Hq][rmm_k_pad(k)], written as by rmm_topk.
+ * The product reads P at 64-token tile granularity: tiles holding no kept
+ * token are skipped, dropped tokens inside a kept tile are zeroed in both P
+ * and V before the multiply, so the result equals the reduced product exactly
+ * (float32 accumulation, bf16 output).
  */
 size_t rmm_pv_workspace_bytes(int64_t Hq, int64_t Lq, int64_t Lk, int64_t k);
 rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, int64_t p_head_stride,

@@ -169,7 +169,7 @@ RMM_API rmm_status_t rmm_topk(const float *scores, int64_t batch, int64_t d, int
 RMM_API size_t rmm_gemm_workspace_bytes(rmm_dtype_t dt, int64_t m, int64_t n, int64_t k) {
   (void)n;
   if (!dtype_ok(dt) || m < 1 || k < 1) return 0;
-  return align256((size_t)m * (size_t)rmm_k_pad(k) * esize(dt));
+  return align256((size_t)m * (size_t)rmm_k_pad(k) * esize(dt)) + align256((size_t)rmm_k_pad(k) * 4);
 }
 
 RMM_API rmm_status_t rmm_gemm(rmm_dtype_t dt, const void *A, int64_t lda, const void *B,
@@ -185,15 +185,16 @@ RMM_API rmm_status_t rmm_gemm(rmm_dtype_t dt, const void *A, int64_t lda, const 
   if (!aligned(A, e) || !aligned(B, e) || !aligned(Y, e) || !aligned(idx, 4))
     return fail(RMM_ERR_INVALID_ARG, "gemm: misaligned pointer");
   const size_t need = rmm_gemm_workspace_bytes(dt, m, n, k);
-  if (!ws || ws_bytes < need || !aligned(ws, 16)) return fail(RMM_ERR_WORKSPACE, "gemm: workspace needs %zu bytes (16-byte aligned)", need);
+  if (!ws || ws_bytes < need || !aligned(ws, 256)) return fail(RMM_ERR_WORKSPACE, "gemm: workspace needs %zu bytes (256-byte aligned)", need);
   const int64_t k_pad = rmm_k_pad(k);
   hipStream_t st = (hipStream_t)stream;
-  hipError_t he = rmm::launch_pack(dt, A, lda, 0, idx, 0, 1, m, d, k, k_pad, ws, st);
+  int32_t *idx_clean = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + align256((size_t)m * k_pad * e));
+  hipError_t he = rmm::launch_pack(dt, A, lda, 0, idx, 0, 1, m, d, k, k_pad, ws, idx_clean, st);
   if (he != hipSuccess) return hip_status(he, "gemm pack launch");
   rmm::GemmArgs g{};
   g.A = ws;
-  g.idx = idx;
-  g.idx_stride = 0;
+  g.idx = idx_clean;
+  g.idx_stride = k_pad;
   g.B = B;
   g.ldb = ldb;
   g.b_batch_stride = 0;
@@ -214,7 +215,7 @@ RMM_API rmm_status_t rmm_gemm(rmm_dtype_t dt, const void *A, int64_t lda, const 
 
 // ------------------------------------------------------------------ attention
 static size_t qk_layout(int64_t Lq, int64_t Hq, int64_t dh, int64_t k, size_t *o_scores,
-                        size_t *o_part, size_t *o_pack) {
+                        size_t *o_part, size_t *o_pack, size_t *o_idx) {
   Carve c(nullptr);
   *o_scores = c.off;
   c.take((size_t)Hq * dh * 4);
@@ -222,13 +223,15 @@ static size_t qk_layout(int64_t Lq, int64_t Hq, int64_t dh, int64_t k, size_t *o
   c.take(colnorm_ws(RMM_BF16, Lq, dh, Hq));
   *o_pack = c.off;
   c.take((size_t)Hq * Lq * rmm_k_pad(k) * 2);
+  *o_idx = c.off;
+  c.take((size_t)Hq * rmm_k_pad(k) * 4);
   return c.off;
 }
 
 RMM_API size_t rmm_qk_workspace_bytes(int64_t Lq, int64_t Hq, int64_t dh, int64_t k) {
   if (Lq < 1 || Hq < 1 || dh < 1 || k < 1) return 0;
-  size_t a, b, c;
-  return qk_layout(Lq, Hq, dh, k, &a, &b, &c);
+  size_t a, b, c, e;
+  return qk_layout(Lq, Hq, dh, k, &a, &b, &c, &e);
 }
 
 RMM_API rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, int64_t q_tok_stride,
@@ -246,8 +249,8 @@ RMM_API rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, i
   if (ldkt < Lk || lds < Lk || q_tok_stride < dh) return fail(RMM_ERR_INVALID_ARG, "qk: leading dimension too small");
   if (!aligned(Q, 2) || !aligned(Kt, 2) || !aligned(S, 4) || !aligned(idx, 4))
     return fail(RMM_ERR_INVALID_ARG, "qk: misaligned pointer");
-  size_t o_sc, o_part, o_pack;
-  const size_t need = qk_layout(Lq, Hq, dh, k, &o_sc, &o_part, &o_pack);
+  size_t o_sc, o_part, o_pack, o_idx;
+  const size_t need = qk_layout(Lq, Hq, dh, k, &o_sc, &o_part, &o_pack, &o_idx);
   if (!ws || ws_bytes < need || !aligned(ws, 256)) return fail(RMM_ERR_WORKSPACE, "qk: workspace needs %zu bytes (256-byte aligned)", need);
   char *w = static_cast<char *>(ws);
   float *scores = reinterpret_cast<float *>(w + o_sc);
@@ -260,12 +263,13 @@ RMM_API rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, i
   if (he != hipSuccess) return hip_status(he, "qk colnorm launch");
   he = rmm::launch_topk(scores, Hq, dh, k, k_pad, idx, st);
   if (he != hipSuccess) return hip_status(he, "qk topk launch");
+  int32_t *idx_clean = reinterpret_cast<int32_t *>(w + o_idx);
   he = rmm::launch_pack(RMM_BF16, Q, q_tok_stride, q_head_stride, idx, k_pad, Hq, Lq, dh, k, k_pad,
-                        w + o_pack, st);
+                        w + o_pack, idx_clean, st);
   if (he != hipSuccess) return hip_status(he, "qk pack launch");
   rmm::GemmArgs g{};
   g.A = w + o_pack;
-  g.idx = idx;
+  g.idx = idx_clean;
   g.idx_stride = k_pad;
   g.B = Kt;
   g.ldb = ldkt;
@@ -285,14 +289,15 @@ RMM_API rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, i
 }
 
 static size_t pv_layout(int64_t Hq, int64_t Lq, int64_t Lk, int64_t k, size_t *o_scores,
-                        size_t *o_part, size_t *o_pack) {
+                        size_t *o_part, size_t *o_plan) {
+  (void)k;
   Carve c(nullptr);
   *o_scores = c.off;
   c.take((size_t)Hq * Lk * 4);
   *o_part = c.off;
   c.take(colnorm_ws(RMM_BF16, Lq, Lk, Hq));
-  *o_pack = c.off;
-  c.take((size_t)Hq * Lq * rmm_k_pad(k) * 2);
+  *o_plan = c.off;
+  c.take(rmm::pv_plan_bytes(Hq, Lk));
   return c.off;
 }
 
@@ -309,6 +314,7 @@ RMM_API rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, i
                             size_t ws_bytes, rmm_stream_t stream) {
   if (!P || !V || !O || !idx) return fail(RMM_ERR_INVALID_ARG, "pv: NULL pointer");
   if (Lq < 1 || Lk < 1 || dh < 1 || Lk >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "pv: bad Lq, Lk or dh");
+  if (Lk > rmm::pv_max_tokens()) return fail(RMM_ERR_UNSUPPORTED, "pv: Lk above %lld", (long long)rmm::pv_max_tokens());
   if (Hq < 1 || Hq > kMaxBatch || Hkv < 1 || Hkv > Hq || Hq % Hkv != 0)
     return fail(RMM_ERR_INVALID_ARG, "pv: need 1 <= Hkv <= Hq <= 65535 and Hq %% Hkv == 0");
   if (k < 1 || k > Lk) return fail(RMM_ERR_INVALID_ARG, "pv: need 1 <= k <= Lk");
@@ -317,8 +323,10 @@ RMM_API rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, i
   if (ldp < Lk) return fail(RMM_ERR_INVALID_ARG, "pv: ldp < Lk");
   if (!aligned(P, 2) || !aligned(V, 2) || !aligned(O, 2) || !aligned(idx, 4))
     return fail(RMM_ERR_INVALID_ARG, "pv: misaligned pointer");
-  size_t o_sc, o_part, o_pack;
-  const size_t need = pv_layout(Hq, Lq, Lk, k, &o_sc, &o_part, &o_pack);
+  if (!rmm::pv_layout_ok(P, ldp, p_head_stride, V, v_tok_stride, v_head_stride, Lk, dh))
+    return fail(RMM_ERR_UNSUPPORTED, "pv: a 256-row block of P or the rows of one V head exceed 4 GiB");
+  size_t o_sc, o_part, o_plan;
+  const size_t need = pv_layout(Hq, Lq, Lk, k, &o_sc, &o_part, &o_plan);
   if (!ws || ws_bytes < need || !aligned(ws, 256)) return fail(RMM_ERR_WORKSPACE, "pv: workspace needs %zu bytes (256-byte aligned)", need);
   char *w = static_cast<char *>(ws);
   float *scores = reinterpret_cast<float *>(w + o_sc);
@@ -330,25 +338,7 @@ RMM_API rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, i
   if (he != hipSuccess) return hip_status(he, "pv colnorm launch");
   he = rmm::launch_topk(scores, Hq, Lk, k, k_pad, idx, st);
   if (he != hipSuccess) return hip_status(he, "pv topk launch");
-  he = rmm::launch_pack(RMM_BF16, P, ldp, p_head_stride, idx, k_pad, Hq, Lq, Lk, k, k_pad, w + o_pack, st);
-  if (he != hipSuccess) return hip_status(he, "pv pack launch");
-  rmm::GemmArgs g{};
-  g.A = w + o_pack;
-  g.idx = idx;
-  g.idx_stride = k_pad;
-  g.B = V;
-  g.ldb = v_tok_stride;
-  g.b_batch_stride = v_head_stride;
-  g.Y = O;
-  g.ldy = o_tok_stride;
-  g.y_batch_stride = o_head_stride;
-  g.batch = Hq;
-  g.hq = Hq;
-  g.hkv = Hkv;
-  g.m = Lq;
-  g.n = dh;
-  g.d = Lk;
-  g.k = k;
-  g.k_pad = k_pad;
-  return hip_status(rmm::launch_gemm_bf16(g, rmm::OutType::BF16, st), "pv gemm launch");
+  he = rmm::launch_pv(P, ldp, p_head_stride, V, v_tok_stride, v_head_stride, O, o_tok_stride, o_head_stride,
+                      idx, k_pad, k, Hq, Hkv, Lq, Lk, dh, w + o_plan, st);
+  return hip_status(he, "pv gemm launch");
 }

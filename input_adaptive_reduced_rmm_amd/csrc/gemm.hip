@@ -1,7 +1,11 @@
 // Index-gathered GEMM: Y = A_I B[I, :] ("Mecanismo Central": the reduced
 // product A_{:,I} B_{I,:} replaces A B), float32 accumulation.
 //
-// bf16 path (MFMA v_mfma_f32_32x32x16_bf16, gfx950):
+// The bf16 products run on the shared MFMA core (mfma_gemm.h) whenever B's
+// base and strides allow 16-byte loads; the kernel below is the fallback for
+// other layouts (same math, plain loads).
+//
+// bf16 fallback (MFMA v_mfma_f32_32x32x16_bf16, gfx950):
 //   block tile BM x BN x 64, 4 waves in a 2 x 2 grid, each wave BM/2 x BN/2 as
 //   (BM/64) x (BN/64) MFMA tiles of 32 x 32.  A_I arrives packed and
 //   K-contiguous, so its tile is copied to LDS as 16-byte chunks.  B is read
@@ -18,6 +22,7 @@
 // lane per operand, so no transposition is needed.
 #include <type_traits>
 
+#include "mfma_gemm.h"
 #include "rmm_internal.h"
 #include "timing.h"
 
@@ -281,9 +286,68 @@ hipError_t launch_bm(const GemmArgs &g, bool bvec, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, typename OUT, int STAGES>
+hipError_t launch_core(const GemmArgs &g, const char *name, hipStream_t st) {
+  const bool bvec = (reinterpret_cast<uintptr_t>(g.B) % 16 == 0) && (g.ldb % 8 == 0) &&
+                    (g.b_batch_stride % 8 == 0);
+  mg::Args a{};
+  a.A = static_cast<const uint16_t *>(g.A);
+  a.lda = g.k_pad;
+  a.a_bs = g.m * g.k_pad;
+  a.a_cols = g.k_pad;
+  a.B = static_cast<const uint16_t *>(g.B);
+  a.ldb = g.ldb;
+  a.b_bs = g.b_batch_stride;
+  a.idx = g.idx;
+  a.idx_bs = g.idx_stride;
+  a.Y = g.Y;
+  a.ldy = g.ldy;
+  a.y_bs = g.y_batch_stride;
+  a.batch = g.batch;
+  a.hq = g.hq;
+  a.hkv = g.hkv;
+  a.m = g.m;
+  a.n = g.n;
+  a.d = g.d;
+  a.k_pad = g.k_pad;
+  a.tiles_m = (g.m + BM - 1) / BM;
+  a.tiles_n = (g.n + BN - 1) / BN;
+  dim3 grid((unsigned)(a.tiles_m * a.tiles_n), 1, (unsigned)g.batch);
+  KernelTimer timer(name, st);
+  if (bvec)
+    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, mg::kGatherRows, OUT, STAGES, true, true>), grid, dim3(256), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, mg::kGatherRows, OUT, STAGES, true, false>), grid, dim3(256), 0,
+                       st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+bool gemm_core_ok(const GemmArgs &g) {
+  const bool aligned16 = (reinterpret_cast<uintptr_t>(g.B) % 2 == 0) &&
+                         (reinterpret_cast<uintptr_t>(g.idx) % 16 == 0) && (g.idx_stride % 4 == 0);
+  const bool fits = (uint64_t)((g.d - 1) * g.ldb + g.n) * 2 < mg::kMaxRecords &&
+                    (uint64_t)256 * g.k_pad * 2 < mg::kMaxRecords;
+  return aligned16 && fits;
+}
+
+// `g.idx` must be the cleaned index list (k_pad entries per batch, -1 where a
+// row contributes zero) when the core path is taken.
 hipError_t launch_gemm_bf16(const GemmArgs &g, OutType out, hipStream_t st) {
+  if (gemm_core_ok(g)) {
+    const int64_t nk = g.k_pad / kBK;
+    if (out == OutType::F32) {
+      if (nk == 1) return launch_core<128, 128, float, 1>(g, "gemm_f32out", st);
+      return launch_core<128, 128, float, 2>(g, "gemm_f32out", st);
+    }
+    const int64_t t256 = ((g.m + 255) / 256) * ((g.n + 255) / 256) * g.batch;
+#ifndef RMM_PROBE_NO_256
+    if (t256 >= 200) return launch_core<256, 256, uint16_t, 2>(g, "gemm_256", st);
+#endif
+    return launch_core<128, 128, uint16_t, 2>(g, "gemm_128", st);
+  }
   const bool bvec = (reinterpret_cast<uintptr_t>(g.B) % 16 == 0) && (g.ldb % 8 == 0) &&
                     (g.b_batch_stride % 8 == 0);
   if (out == OutType::F32) return launch_bm<128, float>(g, bvec, st);

@@ -7,7 +7,9 @@
 // columns).  Its column indices are loaded once and reused for every row the
 // block walks; kept indices ascend, so neighbouring lanes read neighbouring
 // addresses of the same source row and a wave's gathers fall in a few cache
-// lines.  Stores are full 16-byte, fully coalesced.
+// lines.  Stores are full 16-byte, fully coalesced.  The blocks of the first
+// row block also write the cleaned index list (-1 for padding and for indices
+// outside [0, d)) that the GEMM reads with 16-byte loads.
 #include "rmm_internal.h"
 #include "timing.h"
 
@@ -34,7 +36,8 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const T *__restrict__ A,
                                                         int64_t idx_bs, int64_t m, int64_t d,
                                                         int64_t k, int64_t k_pad,
                                                         int64_t rows_per_block,
-                                                        T *__restrict__ out) {
+                                                        T *__restrict__ out,
+                                                        int32_t *__restrict__ idx_clean) {
   constexpr int N = Vec16<T>::N;
   const int64_t t0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * N;
   if (t0 >= k_pad) return;
@@ -49,6 +52,10 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const T *__restrict__ A,
       c = (v >= 0 && v < d) ? v : -1;
     }
     col[e] = c;
+  }
+  if (idx_clean && blockIdx.y == 0) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) idx_clean[b * k_pad + t0 + e] = (int32_t)col[e];
   }
   const T *Ab = A + b * a_bs;
   T *Ob = out + b * m * k_pad + t0;
@@ -76,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const T *__restrict__ A,
 
 hipError_t launch_pack(rmm_dtype_t dt, const void *A, int64_t lda, int64_t a_bs,
                        const int32_t *idx, int64_t idx_bs, int64_t batch, int64_t m, int64_t d,
-                       int64_t k, int64_t k_pad, void *out, hipStream_t st) {
+                       int64_t k, int64_t k_pad, void *out, int32_t *idx_clean, hipStream_t st) {
   const int N = dt == RMM_BF16 ? 8 : 4;
   const int64_t col_blocks = ceil_div(k_pad, (int64_t)kThreads * N);
   // ~4096 blocks in total, at least 4 rows each.
@@ -91,11 +98,11 @@ hipError_t launch_pack(rmm_dtype_t dt, const void *A, int64_t lda, int64_t a_bs,
   if (dt == RMM_BF16)
     hipLaunchKernelGGL(pack_kernel<uint16_t>, grid, dim3(kThreads), 0, st,
                        static_cast<const uint16_t *>(A), lda, a_bs, idx, idx_bs, m, d, k, k_pad,
-                       rpb, static_cast<uint16_t *>(out));
+                       rpb, static_cast<uint16_t *>(out), idx_clean);
   else
     hipLaunchKernelGGL(pack_kernel<float>, grid, dim3(kThreads), 0, st,
                        static_cast<const float *>(A), lda, a_bs, idx, idx_bs, m, d, k, k_pad, rpb,
-                       static_cast<float *>(out));
+                       static_cast<float *>(out), idx_clean);
   return hipGetLastError();
 }
 

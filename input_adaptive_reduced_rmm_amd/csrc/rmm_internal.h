@@ -47,9 +47,11 @@ hipError_t launch_topk(const float *scores, int64_t batch, int64_t d, int64_t k,
 
 // ------------------------------------------------------------------ pack
 // out[b][i][t] = A[b][i][idx[b][t]] for t < k (0 when idx is out of [0,d)), 0 for k <= t < k_pad.
+// idx_clean (optional) [batch][k_pad]: idx[b][t] when t < k and 0 <= idx < d, else -1.
 hipError_t launch_pack(rmm_dtype_t dt, const void *A, int64_t lda, int64_t a_batch_stride,
                        const int32_t *idx, int64_t idx_batch_stride, int64_t batch, int64_t m,
-                       int64_t d, int64_t k, int64_t k_pad, void *out, hipStream_t stream);
+                       int64_t d, int64_t k, int64_t k_pad, void *out, int32_t *idx_clean,
+                       hipStream_t stream);
 
 // ------------------------------------------------------------------ gathered GEMM
 struct GemmArgs {
@@ -66,5 +68,15 @@ struct GemmArgs {
 enum class OutType { BF16, F32 };
 hipError_t launch_gemm_bf16(const GemmArgs &a, OutType out, hipStream_t stream);
 hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t stream);
+
+// ------------------------------------------------------------------ token-reduced P V
+int64_t pv_max_tokens();
+bool pv_layout_ok(const void *P, int64_t ldp, int64_t p_hs, const void *V, int64_t v_ts, int64_t v_hs,
+                  int64_t Lk, int64_t dh);
+size_t pv_plan_bytes(int64_t hq, int64_t Lk);
+hipError_t launch_pv(const void *P, int64_t ldp, int64_t p_hs, const void *V, int64_t v_ts,
+                     int64_t v_hs, void *O, int64_t o_ts, int64_t o_hs, const int32_t *idx,
+                     int64_t idx_stride, int64_t k, int64_t hq, int64_t hkv, int64_t Lq, int64_t Lk,
+                     int64_t dh, void *plan_ws, hipStream_t stream);
 
 }  // namespace rmm

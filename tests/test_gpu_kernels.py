@@ -110,7 +110,9 @@ def test_topk_batched():
 
 # ------------------------------------------------------------------ gemm
 GEMM_SHAPES = [(1, 64, 8, 1), (16, 512, 200, 256), (129, 300, 77, 150), (256, 2048, 512, 1024),
-               (100, 130, 129, 65), (300, 1000, 384, 999), (64, 4096, 1, 4096), (1, 1, 1, 1)]
+               (100, 130, 129, 65), (300, 1000, 384, 999), (64, 4096, 1, 4096), (1, 1, 1, 1),
+               # large-tile path (>= 200 tiles of 256 x 256), ragged edges
+               (2048, 1000, 6500, 517), (4000, 700, 4100, 350), (4096, 2048, 4096, 1024)]
 
 
 @pytest.mark.parametrize("m,d,n,k", GEMM_SHAPES)
@@ -185,9 +187,11 @@ def test_qk_unit(L, Hq, Hkv, k):
         assert rel_fro(S[h], want) < TOL_BF16
 
 
-@pytest.mark.parametrize("L,Hq,Hkv,k", [(64, 4, 2, 32), (300, 4, 4, 150), (129, 2, 1, 1), (100, 2, 2, 100)])
-def test_pv_unit(L, Hq, Hkv, k):
-    Q, Kt, V = synth.attention_qkv(6, 77, L, Hq, Hkv, 128)
+@pytest.mark.parametrize("L,Hq,Hkv,k,dh", [(64, 4, 2, 32, 128), (300, 4, 4, 150, 128), (129, 2, 1, 1, 128),
+                                          (100, 2, 2, 100, 128), (700, 2, 1, 333, 64), (200, 2, 2, 64, 192),
+                                          (1000, 3, 1, 999, 128)])
+def test_pv_unit(L, Hq, Hkv, k, dh):
+    Q, Kt, V = synth.attention_qkv(6, 77, L, Hq, Hkv, dh)
     P = synth.causal_probs(Q, Kt, 128 ** -0.5)                    # torch bf16 on CPU
     Pn = P.float().numpy()
     O, idx = R.rmm_pv(P.to(DEV), dev_tensor(V, BF), k)
