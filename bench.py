@@ -234,6 +234,30 @@ def algorithmic_work(runner, key):
     return None, 0, None
 
 
+def csrc_sha256():
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "input_adaptive_reduced_rmm_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, tag):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs, or None
+    when they were taken on other kernel sources or another kernel."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    try:
+        t = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if t.get("tag") != tag or t.get("csrc_sha256") != csrc_sha256():
+        return None
+    return int(round(t["read_bytes"] + t["write_bytes"]))
+
+
 def cpu_baseline(wl, layer_meta):
     """Time the CPU oracle on a bounded sample of the same workload."""
     import numpy as np
@@ -337,12 +361,12 @@ def main():
             peak = PEAK_F32_TFLOPS if layer["dtype"] == torch.float32 else PEAK_BF16_TFLOPS
             ach = amount / (avg * 1e-3) / 1e12
             roof = {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(ach / peak, 4), "traffic": None, "kernel": key,
+                    "frac": round(ach / peak, 4), "traffic": measured_traffic(wl.key, key), "kernel": key,
                     "per_launch": f"{amount:.4g} flops", "avg_launch_ms": round(avg, 4)}
         else:
             ach = amount / (avg * 1e-3) / 1e9
             roof = {"bound": bound, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": key,
+                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(wl.key, key), "kernel": key,
                     "per_launch": f"{amount:.4g} bytes", "avg_launch_ms": round(avg, 4)}
     # Kept-work MFMA fraction over all projection GEMMs.
     g_fl = g_ms = 0.0

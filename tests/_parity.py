@@ -45,7 +45,13 @@ def check_selection(idx_row: np.ndarray, gpu_scores: np.ndarray, oracle_scores: 
     I = idx_row[:k].astype(np.int64)
     assert np.all(idx_row[k:kp] == -1), "padding must be -1"
     assert np.array_equal(I, oracle.select_top(gpu_scores.astype(np.float64), k)), "selection differs on GPU scores"
+    I_ora = oracle.select_top(oracle_scores, k)
     if rank_gap(oracle_scores, k) > GAP:
-        assert np.array_equal(I, oracle.select_top(oracle_scores, k)), "selection differs from oracle"
+        assert np.array_equal(I, I_ora), "selection differs from oracle"
         return 0
+    # Near tie: any disagreement with the float64 selection must be a swap of
+    # indices whose float64 scores lie within the tie band around the k-th score.
+    kth = np.sort(oracle_scores)[::-1][k - 1]
+    for j in np.setxor1d(I, I_ora):
+        assert abs(oracle_scores[j] - kth) <= GAP * kth, "swap outside the tie band"
     return 1
