@@ -5,12 +5,14 @@ One step = one pass of every reduced product of a layer over one batch of
 synthetic input already resident in HBM: for each projection, column scores ->
 top-k -> reduced GEMM (q/k/v share one selection, up/gate share one, since
 the scores depend on A only); then the feature-reduced Q K^T and the
-token-reduced P V over all heads.  The attention probabilities P are a
-precomputed input (a causal softmax of the layer's logits), like X.
+token-reduced P V over all heads, both in their causal form (the layer is a
+causal decoder: S above the diagonal is not needed and P is zero there).  The
+attention probabilities P are a precomputed input (a causal softmax of the
+layer's logits), like X.
 
 Prints one JSON line.  `value` is effective TFLOP/s: the dense-equivalent
-flops of the step (2 m d n per projection, 2 Lq Lk dh per attention product
-and head) divided by the measured step time.
+flops of the step (2 m d n per projection, 2 dh per causal query-key pair,
+per head, for each attention product) divided by the measured step time.
 """
 from __future__ import annotations
 
@@ -152,19 +154,27 @@ class Runner:
             at, a = self.layer["attention"], self.att
             if tagged:
                 T.tag("qk")
-            R.rmm_qk(at["Q"], at["Kt"], a["kf"], S=a["S"], idx=a["iq"], ws=a["wq"])
+            R.rmm_qk(at["Q"], at["Kt"], a["kf"], S=a["S"], idx=a["iq"], ws=a["wq"], causal=True)
             if tagged:
                 T.tag("pv")
-            R.rmm_pv(at["P"], at["V"], a["kt"], O=a["O"], idx=a["ip"], ws=a["wp"])
+            R.rmm_pv(at["P"], at["V"], a["kt"], O=a["O"], idx=a["ip"], ws=a["wp"], causal=True)
         if tagged:
             T.tag(None)
 
 
+def causal_pairs(L):
+    """(query, key) pairs a causal layer of L tokens uses: L (L + 1) / 2."""
+    return L * (L + 1) / 2.0
+
+
 def dense_flops(layer):
+    """Dense-equivalent flops of the step: 2 m d n per projection; for the causal
+    attention products, 2 dh per used (query, key) pair, per head, for each of
+    Q K^T and P V."""
     f = sum(2.0 * l["m"] * l["d"] * l["n"] for l in layer["linears"])
     at = layer["attention"]
     if at is not None:
-        f += 2 * (2.0 * at["L"] * at["L"] * at["dh"] * at["Hq"])
+        f += 2 * (2.0 * causal_pairs(at["L"]) * at["dh"] * at["Hq"])
     return f
 
 
@@ -207,13 +217,15 @@ def algorithmic_work(runner, key):
     at = runner.layer["attention"]
     a = runner.att
     if tag == "qk" and kern.startswith("gemm"):
-        per_head = at["L"] * a["kf"] * 2 + a["kf"] * at["L"] * 2 + at["L"] * at["L"] * 4
+        # A_I and B_I read once, the causal part of S written (fp32)
+        per_head = at["L"] * a["kf"] * 2 + a["kf"] * at["L"] * 2 + causal_pairs(at["L"]) * 4
         return "hbm", per_head * at["Hq"], "bytes"
     if tag == "pv" and kern.startswith("gemm"):
         per_head = at["L"] * a["kt"] * 2 + a["kt"] * at["dh"] * 2 + at["L"] * at["dh"] * 2
         return "hbm", per_head * at["Hq"], "bytes"
     if tag == "pv" and kern == "colnorm":
-        return "hbm", at["Hq"] * (at["L"] * at["L"] * 2 + 4 * at["L"]), "bytes"
+        # the causal part of P read once
+        return "hbm", at["Hq"] * (causal_pairs(at["L"]) * 2 + 4 * at["L"]), "bytes"
     if tag == "pv" and kern == "pack":
         return "hbm", at["Hq"] * at["L"] * a["kt"] * 2 * 2, "bytes"
     if tag == "qk" and kern == "colnorm":

@@ -162,7 +162,7 @@ rmm_status_t rmm_gemm(rmm_dtype_t dt, const void *A, int64_t lda, const void *B,
 size_t rmm_qk_workspace_bytes(int64_t Lq, int64_t Hq, int64_t dh, int64_t k);
 rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, int64_t q_tok_stride,
                     int64_t q_head_stride, const void *Kt, int64_t Lk, int64_t Hkv,
-                    int64_t kt_head_stride, int64_t ldkt, int64_t k, float *S,
+                    int64_t kt_head_stride, int64_t ldkt, int64_t k, int causal, float *S,
                     int64_t s_head_stride, int64_t lds, int32_t *idx, void *ws, size_t ws_bytes,
                     rmm_stream_t stream);
 
@@ -172,6 +172,9 @@ rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, int64_t q
  * P V).  For query head h with kv head g = floor(h*Hkv/Hq):
  *   s = column scores of P_h over its Lq query rows, J_h = top-k tokens,
  *   O_h = P_h[:, J_h] V_g[J_h, :].
+ *   causal != 0: P is a causal attention matrix: entries (t, u) with
+ *   u > t + (Lk - Lq) are taken as zero and are never read (scores and
+ *   product alike).  causal == 0 reads all of P.
  *   P (device, bf16) element (h, t, u) at P + h*p_head_stride + t*ldp + u, ldp >= Lk.
  *   V (device, bf16) element (u, g, j) at V + u*v_tok_stride + g*v_head_stride + j.
  *   1 <= k <= Lk <= 524288 (RMM_ERR_UNSUPPORTED above).
@@ -189,7 +192,7 @@ rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, int64_t q
 size_t rmm_pv_workspace_bytes(int64_t Hq, int64_t Lq, int64_t Lk, int64_t k);
 rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, int64_t p_head_stride,
                     int64_t ldp, const void *V, int64_t Hkv, int64_t dh, int64_t v_tok_stride,
-                    int64_t v_head_stride, int64_t k, void *O, int64_t o_tok_stride,
+                    int64_t v_head_stride, int64_t k, int causal, void *O, int64_t o_tok_stride,
                     int64_t o_head_stride, int32_t *idx, void *ws, size_t ws_bytes,
                     rmm_stream_t stream);
 

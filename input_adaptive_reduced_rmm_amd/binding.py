@@ -53,7 +53,7 @@ _PROTOS = {
                                 _i64, _vp, _sz, _vp]),
     "rmm_qk_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "rmm_qk": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
-                              _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
+                              ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
     "rmm_pv_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "rmm_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "rmm_timing_set_tag": (ctypes.c_int, [ctypes.c_char_p]),
@@ -63,7 +63,7 @@ _PROTOS = {
                                         ctypes.POINTER(_i64)]),
     "rmm_timing_reset": (ctypes.c_int, []),
     "rmm_pv": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
-                              _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
+                              ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -226,9 +226,10 @@ def rmm_gemm(A: torch.Tensor, B: torch.Tensor, idx: torch.Tensor, k: int, out: t
 
 
 def rmm_qk(Q: torch.Tensor, Kt: torch.Tensor, k: int, S: torch.Tensor | None = None,
-           idx: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+           idx: torch.Tensor | None = None, ws: torch.Tensor | None = None, causal: bool = False):
     """Feature-reduced scores. Q [Lq, Hq, dh], Kt [Hkv, dh, Lk] (bf16) ->
-    (S float32 [Hq, Lq, Lk], idx int32 [Hq, k_pad])."""
+    (S float32 [Hq, Lq, Lk], idx int32 [Hq, k_pad]).  causal=True leaves tiles
+    above the causal diagonal unwritten."""
     lib = load()
     dev = _dev(Q, Kt)
     if Q.dtype != torch.bfloat16 or Kt.dtype != torch.bfloat16:
@@ -246,15 +247,17 @@ def rmm_qk(Q: torch.Tensor, Kt: torch.Tensor, k: int, S: torch.Tensor | None = N
         idx = torch.empty((Hq, kp), dtype=torch.int32, device=dev)
     ws, wsb = _ws(int(lib.rmm_qk_workspace_bytes(Lq, Hq, dh, int(k))), dev, ws)
     _check(lib.rmm_qk(_ptr(Q), Lq, Hq, dh, Q.stride(0), Q.stride(1), _ptr(Kt), Lk, Hkv, Kt.stride(0),
-                      Kt.stride(1), int(k), _ptr(S), S.stride(0), S.stride(1), _ptr(idx), _ptr(ws), wsb,
+                      Kt.stride(1), int(k), 1 if causal else 0, _ptr(S), S.stride(0), S.stride(1), _ptr(idx),
+                      _ptr(ws), wsb,
                       _stream(dev)))
     return S, idx
 
 
 def rmm_pv(P: torch.Tensor, V: torch.Tensor, k: int, O: torch.Tensor | None = None,
-           idx: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+           idx: torch.Tensor | None = None, ws: torch.Tensor | None = None, causal: bool = False):
     """Token-reduced output. P [Hq, Lq, Lk], V [Lk, Hkv, dh] (bf16) ->
-    (O bf16 [Lq, Hq, dh], idx int32 [Hq, k_pad])."""
+    (O bf16 [Lq, Hq, dh], idx int32 [Hq, k_pad]).  causal=True: P above the
+    causal diagonal is taken as zero and never read."""
     lib = load()
     dev = _dev(P, V)
     if P.dtype != torch.bfloat16 or V.dtype != torch.bfloat16:
@@ -272,7 +275,8 @@ def rmm_pv(P: torch.Tensor, V: torch.Tensor, k: int, O: torch.Tensor | None = No
         idx = torch.empty((Hq, kp), dtype=torch.int32, device=dev)
     ws, wsb = _ws(int(lib.rmm_pv_workspace_bytes(Hq, Lq, Lk, int(k))), dev, ws)
     _check(lib.rmm_pv(_ptr(P), Hq, Lq, Lk, P.stride(0), P.stride(1), _ptr(V), Hkv, dh, V.stride(0),
-                      V.stride(1), int(k), _ptr(O), O.stride(0), O.stride(1), _ptr(idx), _ptr(ws), wsb,
+                      V.stride(1), int(k), 1 if causal else 0, _ptr(O), O.stride(0), O.stride(1), _ptr(idx),
+                      _ptr(ws), wsb,
                       _stream(dev)))
     return O, idx
 

@@ -236,7 +236,7 @@ RMM_API size_t rmm_qk_workspace_bytes(int64_t Lq, int64_t Hq, int64_t dh, int64_
 
 RMM_API rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, int64_t q_tok_stride,
                             int64_t q_head_stride, const void *Kt, int64_t Lk, int64_t Hkv,
-                            int64_t kt_head_stride, int64_t ldkt, int64_t k, float *S,
+                            int64_t kt_head_stride, int64_t ldkt, int64_t k, int causal, float *S,
                             int64_t s_head_stride, int64_t lds, int32_t *idx, void *ws,
                             size_t ws_bytes, rmm_stream_t stream) {
   if (!Q || !Kt || !S || !idx) return fail(RMM_ERR_INVALID_ARG, "qk: NULL pointer");
@@ -267,25 +267,11 @@ RMM_API rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, i
   he = rmm::launch_pack(RMM_BF16, Q, q_tok_stride, q_head_stride, idx, k_pad, Hq, Lq, dh, k, k_pad,
                         w + o_pack, idx_clean, st);
   if (he != hipSuccess) return hip_status(he, "qk pack launch");
-  rmm::GemmArgs g{};
-  g.A = w + o_pack;
-  g.idx = idx_clean;
-  g.idx_stride = k_pad;
-  g.B = Kt;
-  g.ldb = ldkt;
-  g.b_batch_stride = kt_head_stride;
-  g.Y = S;
-  g.ldy = lds;
-  g.y_batch_stride = s_head_stride;
-  g.batch = Hq;
-  g.hq = Hq;
-  g.hkv = Hkv;
-  g.m = Lq;
-  g.n = Lk;
-  g.d = dh;
-  g.k = k;
-  g.k_pad = k_pad;
-  return hip_status(rmm::launch_gemm_bf16(g, rmm::OutType::F32, st), "qk gemm launch");
+  if (!rmm::qk_layout_ok(Lq, dh, ldkt, Lk, k_pad))
+    return fail(RMM_ERR_UNSUPPORTED, "qk: the rows of one key head exceed 4 GiB");
+  return hip_status(rmm::launch_qk(w + o_pack, idx_clean, Kt, kt_head_stride, ldkt, S, s_head_stride, lds, Hq,
+                                   Hkv, Lq, Lk, dh, k_pad, causal != 0, st),
+                    "qk gemm launch");
 }
 
 static size_t pv_layout(int64_t Hq, int64_t Lq, int64_t Lk, int64_t k, size_t *o_scores,
@@ -309,7 +295,7 @@ RMM_API size_t rmm_pv_workspace_bytes(int64_t Hq, int64_t Lq, int64_t Lk, int64_
 
 RMM_API rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, int64_t p_head_stride,
                             int64_t ldp, const void *V, int64_t Hkv, int64_t dh,
-                            int64_t v_tok_stride, int64_t v_head_stride, int64_t k, void *O,
+                            int64_t v_tok_stride, int64_t v_head_stride, int64_t k, int causal, void *O,
                             int64_t o_tok_stride, int64_t o_head_stride, int32_t *idx, void *ws,
                             size_t ws_bytes, rmm_stream_t stream) {
   if (!P || !V || !O || !idx) return fail(RMM_ERR_INVALID_ARG, "pv: NULL pointer");
@@ -334,11 +320,12 @@ RMM_API rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, i
   const int64_t k_pad = rmm_k_pad(k);
 
   const rmm::ColnormPlan p = plan_for(RMM_BF16, P, Lq, Lk, ldp, Hq, p_head_stride);
-  hipError_t he = rmm::launch_colnorm(RMM_BF16, P, Lq, Lk, ldp, Hq, p_head_stride, scores, w + o_part, p, st);
+  hipError_t he = rmm::launch_colnorm(RMM_BF16, P, Lq, Lk, ldp, Hq, p_head_stride, scores, w + o_part, p, st,
+                                      causal != 0, Lk - Lq);
   if (he != hipSuccess) return hip_status(he, "pv colnorm launch");
   he = rmm::launch_topk(scores, Hq, Lk, k, k_pad, idx, st);
   if (he != hipSuccess) return hip_status(he, "pv topk launch");
   he = rmm::launch_pv(P, ldp, p_head_stride, V, v_tok_stride, v_head_stride, O, o_tok_stride, o_head_stride,
-                      idx, k_pad, k, Hq, Hkv, Lq, Lk, dh, w + o_plan, st);
+                      idx, k_pad, k, Hq, Hkv, Lq, Lk, dh, causal != 0, w + o_plan, st);
   return hip_status(he, "pv gemm launch");
 }

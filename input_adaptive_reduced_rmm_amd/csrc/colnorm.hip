@@ -76,13 +76,15 @@ struct Loader<T, 1> {
 
 // grid: x = column tile (TPR*VEC columns), y = row chunk, z = batch.
 // out: partial sums [chunk][batch][d] (or final scores when `final_sqrt`).
-template <typename T, int VEC, int TPR>
+// CAUSAL: entry (i, j) is taken as zero and not read when j > i + coff (a
+// causal attention matrix); rows that cannot reach a lane's columns are skipped.
+template <typename T, int VEC, int TPR, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void colnorm_kernel(const T *__restrict__ A, int64_t m,
                                                            int64_t d, int64_t lda,
                                                            int64_t batch_stride,
                                                            int64_t rows_per_chunk,
                                                            float *__restrict__ out,
-                                                           int final_sqrt) {
+                                                           int final_sqrt, int64_t coff) {
   constexpr int RPW = 64 / TPR;       // rows one wave covers per step
   constexpr int RPB = kWaves * RPW;   // rows the block covers per step
   constexpr int CT = TPR * VEC;       // columns per block
@@ -102,15 +104,24 @@ __global__ __launch_bounds__(kThreads) void colnorm_kernel(const T *__restrict__
 
   if (c0 < d) {
     int64_t r = r_begin + wave * RPW + sub;
+    if constexpr (CAUSAL) {
+      // Rows i < col0 - coff reach no column of this tile; keep the lane's row phase.
+      const int64_t first = col0 - coff;
+      if (first > r_begin) r += ((first - r_begin) / RPB) * RPB;
+    }
+    auto lim = [&](int64_t row) -> int64_t {
+      if constexpr (CAUSAL) return min(d, row + coff + 1);
+      else return d;
+    };
     // four rows in flight per lane
     for (; r + 3 * RPB < r_end; r += 4 * RPB) {
       const T *p = Ab + r * lda;
-      Loader<T, VEC>::load_sq(p, c0, d, acc);
-      Loader<T, VEC>::load_sq(p + RPB * lda, c0, d, acc);
-      Loader<T, VEC>::load_sq(p + 2 * RPB * lda, c0, d, acc);
-      Loader<T, VEC>::load_sq(p + 3 * RPB * lda, c0, d, acc);
+      Loader<T, VEC>::load_sq(p, c0, lim(r), acc);
+      Loader<T, VEC>::load_sq(p + RPB * lda, c0, lim(r + RPB), acc);
+      Loader<T, VEC>::load_sq(p + 2 * RPB * lda, c0, lim(r + 2 * RPB), acc);
+      Loader<T, VEC>::load_sq(p + 3 * RPB * lda, c0, lim(r + 3 * RPB), acc);
     }
-    for (; r < r_end; r += RPB) Loader<T, VEC>::load_sq(Ab + r * lda, c0, d, acc);
+    for (; r < r_end; r += RPB) Loader<T, VEC>::load_sq(Ab + r * lda, c0, lim(r), acc);
   }
 
   // Fold the lanes that share a column (lane, lane^TPR, lane^2TPR, ...).
@@ -147,15 +158,15 @@ __global__ __launch_bounds__(256) void colnorm_finish(const float *__restrict__ 
   scores[i] = __builtin_sqrtf(s);
 }
 
-template <typename T, int VEC>
+template <typename T, int VEC, bool CAUSAL>
 hipError_t dispatch_tpr(int tpr, dim3 grid, const T *A, int64_t m, int64_t d, int64_t lda,
-                        int64_t bs, int64_t rpc, float *out, int fin, hipStream_t st) {
+                        int64_t bs, int64_t rpc, float *out, int fin, int64_t coff, hipStream_t st) {
   KernelTimer timer("colnorm", st);
   switch (tpr) {
-#define RMM_CN(TP)                                                                       \
-  case TP:                                                                               \
-    hipLaunchKernelGGL((colnorm_kernel<T, VEC, TP>), grid, dim3(kThreads), 0, st, A, m, d, \
-                       lda, bs, rpc, out, fin);                                          \
+#define RMM_CN(TP)                                                                          \
+  case TP:                                                                                  \
+    hipLaunchKernelGGL((colnorm_kernel<T, VEC, TP, CAUSAL>), grid, dim3(kThreads), 0, st, A, m, \
+                       d, lda, bs, rpc, out, fin, coff);                                    \
     break;
     RMM_CN(1) RMM_CN(2) RMM_CN(4) RMM_CN(8) RMM_CN(16) RMM_CN(32) RMM_CN(64)
 #undef RMM_CN
@@ -196,23 +207,24 @@ size_t colnorm_ws_bytes(const ColnormPlan &p, int64_t d, int64_t batch) {
 
 hipError_t launch_colnorm(rmm_dtype_t dt, const void *A, int64_t m, int64_t d, int64_t lda,
                           int64_t batch, int64_t batch_stride, float *scores, void *ws,
-                          const ColnormPlan &p, hipStream_t st) {
+                          const ColnormPlan &p, hipStream_t st, bool causal, int64_t coff) {
   const bool single = p.chunks == 1;
   float *out = single ? scores : static_cast<float *>(ws);
   dim3 grid((unsigned)p.col_tiles, (unsigned)p.chunks, (unsigned)batch);
+  const int64_t bs = batch_stride, rpc = p.rows_per_chunk;
   hipError_t e;
   if (dt == RMM_BF16) {
     const uint16_t *a = static_cast<const uint16_t *>(A);
-    e = p.vec == 8 ? dispatch_tpr<uint16_t, 8>(p.tpr, grid, a, m, d, lda, batch_stride,
-                                                p.rows_per_chunk, out, single, st)
-                   : dispatch_tpr<uint16_t, 1>(p.tpr, grid, a, m, d, lda, batch_stride,
-                                               p.rows_per_chunk, out, single, st);
+    if (causal)
+      e = p.vec == 8 ? dispatch_tpr<uint16_t, 8, true>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, coff, st)
+                     : dispatch_tpr<uint16_t, 1, true>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, coff, st);
+    else
+      e = p.vec == 8 ? dispatch_tpr<uint16_t, 8, false>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, 0, st)
+                     : dispatch_tpr<uint16_t, 1, false>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, 0, st);
   } else {
     const float *a = static_cast<const float *>(A);
-    e = p.vec == 4 ? dispatch_tpr<float, 4>(p.tpr, grid, a, m, d, lda, batch_stride,
-                                             p.rows_per_chunk, out, single, st)
-                   : dispatch_tpr<float, 1>(p.tpr, grid, a, m, d, lda, batch_stride,
-                                            p.rows_per_chunk, out, single, st);
+    e = p.vec == 4 ? dispatch_tpr<float, 4, false>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, 0, st)
+                   : dispatch_tpr<float, 1, false>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, 0, st);
   }
   if (e != hipSuccess || single) return e;
   const int64_t n = batch * d;

@@ -312,6 +312,8 @@ hipError_t launch_core(const GemmArgs &g, const char *name, hipStream_t st) {
   a.k_pad = g.k_pad;
   a.tiles_m = (g.m + BM - 1) / BM;
   a.tiles_n = (g.n + BN - 1) / BN;
+  a.causal = g.causal;
+  a.causal_off = g.causal_off;
   dim3 grid((unsigned)(a.tiles_m * a.tiles_n), 1, (unsigned)g.batch);
   KernelTimer timer(name, st);
   if (bvec)

@@ -57,6 +57,8 @@ struct Args {
   int64_t m, n, d;              // d = rows of B
   int64_t k_pad;                // kGatherRows
   int64_t tiles_m, tiles_n;
+  int causal;                   // causal attention: only columns j <= row + causal_off matter
+  int64_t causal_off;
 };
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint64_t bytes) {
@@ -144,12 +146,17 @@ __global__ __launch_bounds__(256) void mfma_gemm(Args g) {
   const int wm = wave >> 1, wn = wave & 1;
   int64_t tm, tn;
   tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  // Causal P V: the last row blocks stream the most tiles, so start them first.
+  if (MODE == kMaskedTiles && g.causal) tm = g.tiles_m - 1 - tm;
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const int64_t b = blockIdx.z;
   const int64_t grp = (b * g.hkv) / g.hq;
+  const int64_t rows = g.m - m0 < BM ? g.m - m0 : BM;
+  // Causal Q K^T: an output tile whose every column lies above the diagonal is
+  // not needed by a causal softmax and is not computed.
+  if (MODE == kGatherRows && g.causal && n0 > m0 + rows - 1 + g.causal_off) return;
 
   // Resources: the block's A rows and its B column panel.
-  const int64_t rows = g.m - m0 < BM ? g.m - m0 : BM;
   const uint16_t *Ab = g.A + b * g.a_bs + m0 * g.lda;
   const uint64_t a_bytes = MODE == kGatherRows ? (uint64_t)rows * g.lda * 2
                                                : ((uint64_t)(rows - 1) * g.lda + g.a_cols) * 2;
@@ -163,11 +170,24 @@ __global__ __launch_bounds__(256) void mfma_gemm(Args g) {
   const int32_t *idxb = g.idx + b * g.idx_bs;
   const int32_t *tl = g.tiles + b * g.ntiles;
   const uint64_t *ml = g.masks + b * g.ntiles;
-  const int nk = MODE == kGatherRows ? (int)(g.k_pad / kBK) : g.counts[b];
+  int nk = MODE == kGatherRows ? (int)(g.k_pad / kBK) : g.counts[b];
+  if (MODE == kMaskedTiles && g.causal) {
+    // Tiles are ascending: keep those that start at or before the block's last
+    // allowed column (binary search on the uniform tile list).
+    const int64_t last_col = m0 + rows - 1 + g.causal_off;
+    int lo = 0, hi = nk;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)tl[mid] * kBK <= last_col) lo = mid + 1;
+      else hi = mid;
+    }
+    nk = lo;
+  }
 
   uint4 ra[A_CH], rb[KB];
   int32_t inext[KB];          // kGatherRows: source rows of the next tile to load
   uint64_t mk_cur = 0, mk_next = 0;
+  int64_t c_cur = 0, c_next = 0;   // kMaskedTiles: first column of the current / next tile
 
   auto load_idx = [&](int q, int32_t *dst) {
     if constexpr (MODE == kGatherRows) {
@@ -208,12 +228,22 @@ __global__ __launch_bounds__(256) void mfma_gemm(Args g) {
   };
 
   // Write the loaded registers of a tile into LDS stage `buf`.
-  auto store_tile = [&](int buf, uint64_t mk) {
+  auto store_tile = [&](int buf, uint64_t mk, int64_t c0) {
+    // Causal: does this tile reach past the diagonal of the block's first row?
+    const bool diag = MODE == kMaskedTiles && g.causal && c0 + kBK - 1 > m0 + g.causal_off;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int row = (tid >> 3) + 32 * i;
       uint4 v = ra[i];
-      if constexpr (MODE == kMaskedTiles) v = mask8(v, (uint32_t)(mk >> (akc * 8)) & 0xFFu);
+      if constexpr (MODE == kMaskedTiles) {
+        uint32_t bits = (uint32_t)(mk >> (akc * 8)) & 0xFFu;
+        if (diag) {
+          // columns c0 + akc*8 + e are kept only while <= m0 + row + causal_off
+          const int64_t allow = m0 + row + g.causal_off - (c0 + akc * 8) + 1;
+          bits &= allow >= 8 ? 0xFFu : allow <= 0 ? 0u : ((1u << allow) - 1u);
+        }
+        v = mask8(v, bits);
+      }
       *reinterpret_cast<uint4 *>(&As[buf][swz(row, akc)]) = v;
     }
     if constexpr (KB == 8) {
@@ -257,18 +287,24 @@ __global__ __launch_bounds__(256) void mfma_gemm(Args g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   // Prologue: tile 0 into stage 0; indices (or mask) of tile 1 in flight.
-  if constexpr (MODE == kGatherRows) {
-    int32_t i0[KB];
-    load_idx(0, i0);
-    load_tile(0, i0, 0);
-    if (nk > 1) load_idx(1, inext);
-  } else {
-    mk_cur = ml[0];
-    load_tile(0, nullptr, mk_cur);
-    if (nk > 1) mk_next = ml[1];
+  if (nk > 0) {
+    if constexpr (MODE == kGatherRows) {
+      int32_t i0[KB];
+      load_idx(0, i0);
+      load_tile(0, i0, 0);
+      if (nk > 1) load_idx(1, inext);
+    } else {
+      mk_cur = ml[0];
+      c_cur = (int64_t)tl[0] * kBK;
+      load_tile(0, nullptr, mk_cur);
+      if (nk > 1) {
+        mk_next = ml[1];
+        c_next = (int64_t)tl[1] * kBK;
+      }
+    }
+    store_tile(0, mk_cur, c_cur);
+    __syncthreads();
   }
-  store_tile(0, mk_cur);
-  __syncthreads();
 
   const int lrow = lane & 31, lk = lane >> 5;
   for (int q = 0; q < nk; ++q) {
@@ -301,10 +337,14 @@ __global__ __launch_bounds__(256) void mfma_gemm(Args g) {
     }
     if (more) {
       if constexpr (STAGES == 1) __syncthreads();
-      store_tile(STAGES == 2 ? (buf ^ 1) : 0, mk_next);
+      store_tile(STAGES == 2 ? (buf ^ 1) : 0, mk_next, c_next);
       if constexpr (MODE == kMaskedTiles) {
         mk_cur = mk_next;
-        if (q + 2 < nk) mk_next = ml[q + 2];
+        c_cur = c_next;
+        if (q + 2 < nk) {
+          mk_next = ml[q + 2];
+          c_next = (int64_t)tl[q + 2] * kBK;
+        }
       }
     }
     __syncthreads();

@@ -91,7 +91,7 @@ size_t pv_plan_bytes(int64_t hq, int64_t Lk) {
 hipError_t launch_pv(const void *P, int64_t ldp, int64_t p_hs, const void *V, int64_t v_ts,
                      int64_t v_hs, void *O, int64_t o_ts, int64_t o_hs, const int32_t *idx,
                      int64_t idx_stride, int64_t k, int64_t hq, int64_t hkv, int64_t Lq, int64_t Lk,
-                     int64_t dh, void *plan_ws, hipStream_t st) {
+                     int64_t dh, bool causal, void *plan_ws, hipStream_t st) {
   const int64_t nt = ceil_div(Lk, 64);
   char *w = static_cast<char *>(plan_ws);
   int32_t *tiles = reinterpret_cast<int32_t *>(w);
@@ -105,7 +105,13 @@ hipError_t launch_pv(const void *P, int64_t ldp, int64_t p_hs, const void *V, in
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  constexpr int BM = 256, BN = 128;
+#ifndef RMM_PV_BM
+#define RMM_PV_BM 128
+#endif
+#ifndef RMM_PV_STAGES
+#define RMM_PV_STAGES 2
+#endif
+  constexpr int BM = RMM_PV_BM, BN = 128, STG = RMM_PV_STAGES;
   mg::Args a{};
   a.A = static_cast<const uint16_t *>(P);
   a.lda = ldp;
@@ -129,21 +135,23 @@ hipError_t launch_pv(const void *P, int64_t ldp, int64_t p_hs, const void *V, in
   a.d = Lk;
   a.tiles_m = ceil_div(Lq, BM);
   a.tiles_n = ceil_div(dh, BN);
+  a.causal = causal ? 1 : 0;
+  a.causal_off = Lk - Lq;
   dim3 grid((unsigned)(a.tiles_m * a.tiles_n), 1, (unsigned)hq);
   KernelTimer timer("pv_gemm", st);
   const bool avec = reinterpret_cast<uintptr_t>(P) % 16 == 0 && ldp % 8 == 0 && p_hs % 8 == 0;
   const bool bvec = reinterpret_cast<uintptr_t>(V) % 16 == 0 && v_ts % 8 == 0 && v_hs % 8 == 0;
   if (avec && bvec)
-    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, mg::kMaskedTiles, uint16_t, 2, true, true>), grid, dim3(256), 0,
+    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, mg::kMaskedTiles, uint16_t, STG, true, true>), grid, dim3(256), 0,
                        st, a);
   else if (avec)
-    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, mg::kMaskedTiles, uint16_t, 2, true, false>), grid, dim3(256), 0,
+    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, mg::kMaskedTiles, uint16_t, STG, true, false>), grid, dim3(256), 0,
                        st, a);
   else if (bvec)
-    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, mg::kMaskedTiles, uint16_t, 2, false, true>), grid, dim3(256), 0,
+    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, mg::kMaskedTiles, uint16_t, STG, false, true>), grid, dim3(256), 0,
                        st, a);
   else
-    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, mg::kMaskedTiles, uint16_t, 2, false, false>), grid, dim3(256),
+    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, mg::kMaskedTiles, uint16_t, STG, false, false>), grid, dim3(256),
                        0, st, a);
   return hipGetLastError();
 }

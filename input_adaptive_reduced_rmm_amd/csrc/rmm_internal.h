@@ -37,9 +37,11 @@ struct ColnormPlan {
 };
 ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch, bool vec_ok);
 size_t colnorm_ws_bytes(const ColnormPlan &p, int64_t d, int64_t batch);
+// causal (bf16 only): entry (i, j) is zero and not read when j > i + coff.
 hipError_t launch_colnorm(rmm_dtype_t dt, const void *A, int64_t m, int64_t d, int64_t lda,
                           int64_t batch, int64_t batch_stride, float *scores, void *ws,
-                          const ColnormPlan &p, hipStream_t stream);
+                          const ColnormPlan &p, hipStream_t stream, bool causal = false,
+                          int64_t coff = 0);
 
 // ------------------------------------------------------------------ top-k
 hipError_t launch_topk(const float *scores, int64_t batch, int64_t d, int64_t k, int64_t k_pad,
@@ -64,10 +66,18 @@ struct GemmArgs {
   int64_t ldy, y_batch_stride;
   int64_t batch, hq, hkv; // batch b reads B group floor(b*hkv/hq)
   int64_t m, n, d, k, k_pad;
+  int causal;             // skip output tiles with every column > row + causal_off
+  int64_t causal_off;
 };
 enum class OutType { BF16, F32 };
 hipError_t launch_gemm_bf16(const GemmArgs &a, OutType out, hipStream_t stream);
 hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t stream);
+
+// ------------------------------------------------------------------ feature-reduced Q K^T
+bool qk_layout_ok(int64_t Lq, int64_t dh, int64_t ldkt, int64_t Lk, int64_t k_pad);
+hipError_t launch_qk(const void *Apacked, const int32_t *idx_clean, const void *Kt, int64_t kt_hs,
+                     int64_t ldkt, float *S, int64_t s_hs, int64_t lds, int64_t hq, int64_t hkv,
+                     int64_t Lq, int64_t Lk, int64_t dh, int64_t k_pad, bool causal, hipStream_t stream);
 
 // ------------------------------------------------------------------ token-reduced P V
 int64_t pv_max_tokens();
@@ -77,6 +87,6 @@ size_t pv_plan_bytes(int64_t hq, int64_t Lk);
 hipError_t launch_pv(const void *P, int64_t ldp, int64_t p_hs, const void *V, int64_t v_ts,
                      int64_t v_hs, void *O, int64_t o_ts, int64_t o_hs, const int32_t *idx,
                      int64_t idx_stride, int64_t k, int64_t hq, int64_t hkv, int64_t Lq, int64_t Lk,
-                     int64_t dh, void *plan_ws, hipStream_t stream);
+                     int64_t dh, bool causal, void *plan_ws, hipStream_t stream);
 
 }  // namespace rmm

@@ -130,16 +130,16 @@ def test_gemm_rejects(lib):
 def test_qk_pv_reject(lib):
     q = lib.rmm_qk
     # Hq % Hkv != 0
-    assert q(FAKE, 64, 6, 128, 768, 128, FAKE, 64, 4, 8192, 64, 32, FAKE, 4096, 64, FAKE, FAKE, 1 << 30, None) == 1
+    assert q(FAKE, 64, 6, 128, 768, 128, FAKE, 64, 4, 8192, 64, 32, 0, FAKE, 4096, 64, FAKE, FAKE, 1 << 30, None) == 1
     # k > dh
-    assert q(FAKE, 64, 4, 128, 512, 128, FAKE, 64, 2, 8192, 64, 129, FAKE, 4096, 64, FAKE, FAKE, 1 << 30, None) == 1
+    assert q(FAKE, 64, 4, 128, 512, 128, FAKE, 64, 2, 8192, 64, 129, 0, FAKE, 4096, 64, FAKE, FAKE, 1 << 30, None) == 1
     # q_tok_stride < dh
-    assert q(FAKE, 64, 4, 128, 100, 128, FAKE, 64, 2, 8192, 64, 64, FAKE, 4096, 64, FAKE, FAKE, 1 << 30, None) == 1
+    assert q(FAKE, 64, 4, 128, 100, 128, FAKE, 64, 2, 8192, 64, 64, 1, FAKE, 4096, 64, FAKE, FAKE, 1 << 30, None) == 1
     need = lib.rmm_qk_workspace_bytes(64, 4, 128, 64)
-    assert q(FAKE, 64, 4, 128, 512, 128, FAKE, 64, 2, 8192, 64, 64, FAKE, 4096, 64, FAKE, FAKE, need - 1, None) == 3
+    assert q(FAKE, 64, 4, 128, 512, 128, FAKE, 64, 2, 8192, 64, 64, 0, FAKE, 4096, 64, FAKE, FAKE, need - 1, None) == 3
     p = lib.rmm_pv
-    assert p(FAKE, 4, 64, 64, 4096, 64, FAKE, 2, 128, 256, 128, 65, FAKE, 512, 128, FAKE, FAKE, 1 << 30, None) == 1
-    assert p(FAKE, 4, 64, 64, 4096, 63, FAKE, 2, 128, 256, 128, 32, FAKE, 512, 128, FAKE, FAKE, 1 << 30, None) == 1
+    assert p(FAKE, 4, 64, 64, 4096, 64, FAKE, 2, 128, 256, 128, 65, 0, FAKE, 512, 128, FAKE, FAKE, 1 << 30, None) == 1
+    assert p(FAKE, 4, 64, 64, 4096, 63, FAKE, 2, 128, 256, 128, 32, 1, FAKE, 512, 128, FAKE, FAKE, 1 << 30, None) == 1
     need = lib.rmm_pv_workspace_bytes(4, 64, 64, 32)
     assert need > 0
-    assert p(FAKE, 4, 64, 64, 4096, 64, FAKE, 2, 128, 256, 128, 32, FAKE, 512, 128, FAKE, FAKE, need - 1, None) == 3
+    assert p(FAKE, 4, 64, 64, 4096, 64, FAKE, 2, 128, 256, 128, 32, 0, FAKE, 512, 128, FAKE, FAKE, need - 1, None) == 3

@@ -202,3 +202,42 @@ def test_pv_unit(L, Hq, Hkv, k, dh):
         check_selection(idx[h], gpu_scores[h], oracle.column_scores(Pn[h]), k)
         want = oracle.reduced_product(Pn[h], V[:, oracle.kv_head(h, Hq, Hkv), :], idx[h][:k])
         assert rel_fro(O[:, h, :], want) < TOL_BF16
+
+
+# ------------------------------------------------------------------ causal attention
+@pytest.mark.parametrize("Lq,Lk,Hq,Hkv,k", [(300, 300, 4, 2, 64), (200, 330, 2, 1, 39), (1000, 1000, 2, 2, 128),
+                                            (129, 129, 2, 1, 1)])
+def test_qk_causal_skips_only_upper_tiles(Lq, Lk, Hq, Hkv, k):
+    Q, _, _ = synth.attention_qkv(7, 77, Lq, Hq, Hkv, 128)
+    _, Kt, _ = synth.attention_qkv(8, 77, Lk, Hq, Hkv, 128)
+    S0 = torch.full((Hq, Lq, Lk), float("nan"), device=DEV)
+    S, idx = R.rmm_qk(dev_tensor(Q, BF), dev_tensor(Kt, BF), k, S=S0, causal=True)
+    S = S.cpu().numpy()
+    idx = idx.cpu().numpy()
+    allowed = np.arange(Lk)[None, :] <= np.arange(Lq)[:, None] + (Lk - Lq)
+    for h in range(Hq):
+        want = oracle.reduced_product(Q[:, h, :], Kt[oracle.kv_head(h, Hq, Hkv)], idx[h][:k])
+        got = S[h]
+        assert not np.isnan(got[allowed]).any()
+        assert rel_fro(got[allowed], want[allowed]) < TOL_BF16
+
+
+@pytest.mark.parametrize("Lq,Lk,Hq,Hkv,k", [(300, 300, 4, 2, 150), (200, 330, 2, 1, 165), (1000, 1000, 2, 2, 333),
+                                            (700, 700, 2, 1, 1), (640, 640, 2, 2, 640)])
+def test_pv_causal_never_uses_upper_triangle(Lq, Lk, Hq, Hkv, k):
+    Q, _, _ = synth.attention_qkv(9, 77, Lq, Hq, Hkv, 128)
+    _, Kt, V = synth.attention_qkv(10, 77, Lk, Hq, Hkv, 128)
+    P = synth.causal_probs(Q, Kt, 128 ** -0.5)                    # exact zeros above the diagonal
+    Pn = P.float().numpy()
+    above = np.arange(Lk)[None, :] > np.arange(Lq)[:, None] + (Lk - Lq)
+    Pg = P.clone()
+    Pg[:, torch.from_numpy(above)] = float("nan")                 # poison what must not be used
+    O, idx = R.rmm_pv(Pg.to(DEV), dev_tensor(V, BF), k, causal=True)
+    O = O.float().cpu().numpy()
+    idx = idx.cpu().numpy()
+    sc = R.rmm_colnorm(P.to(DEV)).cpu().numpy()                   # scores of the clean P
+    assert not np.isnan(O).any()
+    for h in range(Hq):
+        check_selection(idx[h], sc[h], oracle.column_scores(Pn[h]), k)
+        want = oracle.reduced_product(Pn[h], V[:, oracle.kv_head(h, Hq, Hkv), :], idx[h][:k])
+        assert rel_fro(O[:, h, :], want) < TOL_BF16
