@@ -216,11 +216,11 @@ def algorithmic_work(runner, key):
     tag, kern = key.split("/", 1) if "/" in key else ("", key)
     at = runner.layer["attention"]
     a = runner.att
-    if tag == "qk" and kern.startswith("gemm"):
+    if tag == "qk" and "gemm" in kern:
         # A_I and B_I read once, the causal part of S written (fp32)
         per_head = at["L"] * a["kf"] * 2 + a["kf"] * at["L"] * 2 + causal_pairs(at["L"]) * 4
         return "hbm", per_head * at["Hq"], "bytes"
-    if tag == "pv" and kern.startswith("gemm"):
+    if tag == "pv" and "gemm" in kern:
         per_head = at["L"] * a["kt"] * 2 + a["kt"] * at["dh"] * 2 + at["L"] * at["dh"] * 2
         return "hbm", per_head * at["Hq"], "bytes"
     if tag == "pv" and kern == "colnorm":
@@ -239,6 +239,9 @@ def algorithmic_work(runner, key):
     e = 4 if runner.layer["dtype"].itemsize == 4 else 2
     if kern.startswith("gemm"):
         return "mfma", 2.0 * p["m"] * p["k"] * p["n"], "flops"
+    if kern == "bt_pack":
+        # kept weight rows read, their transposed copy written
+        return "hbm", 2.0 * p["k"] * p["n"] * e, "bytes"
     if kern == "colnorm":
         return "hbm", p["m"] * p["d"] * e + 4 * p["d"], "bytes"
     if kern == "pack":

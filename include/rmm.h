@@ -173,8 +173,11 @@ rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, int64_t q
  *   s = column scores of P_h over its Lq query rows, J_h = top-k tokens,
  *   O_h = P_h[:, J_h] V_g[J_h, :].
  *   causal != 0: P is a causal attention matrix: entries (t, u) with
- *   u > t + (Lk - Lq) are taken as zero and are never read (scores and
- *   product alike).  causal == 0 reads all of P.
+ *   u > t + (Lk - Lq) are taken as zero, in the scores and the product
+ *   alike.  Their values are never used (16-byte loads that straddle the
+ *   diagonal may fetch them; they are discarded), and the tiles and row
+ *   segments lying wholly above the diagonal are not read at all.
+ *   causal == 0 reads all of P.
  *   P (device, bf16) element (h, t, u) at P + h*p_head_stride + t*ldp + u, ldp >= Lk.
  *   V (device, bf16) element (u, g, j) at V + u*v_tok_stride + g*v_head_stride + j.
  *   1 <= k <= Lk <= 524288 (RMM_ERR_UNSUPPORTED above).

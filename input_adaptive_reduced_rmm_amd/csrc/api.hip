@@ -166,10 +166,15 @@ RMM_API rmm_status_t rmm_topk(const float *scores, int64_t batch, int64_t d, int
 }
 
 // ------------------------------------------------------------------ gemm
+// Many-row bf16 products also keep a transposed copy of the kept weight rows.
+static bool gemm_uses_nt(rmm_dtype_t dt, int64_t m) { return dt == RMM_BF16 && m >= 1024; }
+
 RMM_API size_t rmm_gemm_workspace_bytes(rmm_dtype_t dt, int64_t m, int64_t n, int64_t k) {
-  (void)n;
-  if (!dtype_ok(dt) || m < 1 || k < 1) return 0;
-  return align256((size_t)m * (size_t)rmm_k_pad(k) * esize(dt)) + align256((size_t)rmm_k_pad(k) * 4);
+  if (!dtype_ok(dt) || m < 1 || k < 1 || n < 1) return 0;
+  const int64_t k_pad = rmm_k_pad(k);
+  size_t b = align256((size_t)m * (size_t)k_pad * esize(dt)) + align256((size_t)k_pad * 4);
+  if (gemm_uses_nt(dt, m)) b += rmm::gemm_nt_bt_bytes(n, k_pad);
+  return b;
 }
 
 RMM_API rmm_status_t rmm_gemm(rmm_dtype_t dt, const void *A, int64_t lda, const void *B,
@@ -191,6 +196,11 @@ RMM_API rmm_status_t rmm_gemm(rmm_dtype_t dt, const void *A, int64_t lda, const 
   int32_t *idx_clean = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + align256((size_t)m * k_pad * e));
   hipError_t he = rmm::launch_pack(dt, A, lda, 0, idx, 0, 1, m, d, k, k_pad, ws, idx_clean, st);
   if (he != hipSuccess) return hip_status(he, "gemm pack launch");
+  if (gemm_uses_nt(dt, m) && rmm::gemm_nt_ok(m, n, d, ldb, k_pad)) {
+    void *bt = static_cast<char *>(ws) + align256((size_t)m * k_pad * e) + align256((size_t)k_pad * 4);
+    return hip_status(rmm::launch_gemm_nt(ws, idx_clean, B, ldb, d, bt, Y, ldy, m, n, k_pad, st),
+                      "gemm launch");
+  }
   rmm::GemmArgs g{};
   g.A = ws;
   g.idx = idx_clean;

@@ -22,16 +22,22 @@ constexpr int kWaves = kThreads / 64;
 template <typename T, int VEC>
 struct Loader;
 
-// bf16, 8 per lane: one 16-byte load.
+// bf16, 8 per lane: one 16-byte load.  `d` is the row's column limit; with a
+// separate matrix width `w` >= d (causal rows), a lane whose 8 columns stay
+// inside the row still loads them as one vector and drops those >= d.
 template <>
 struct Loader<uint16_t, 8> {
-  __device__ static void load_sq(const uint16_t *p, int64_t c0, int64_t d, float *acc) {
-    if (c0 + 8 <= d) {
+  __device__ static void load_sq(const uint16_t *p, int64_t c0, int64_t d, float *acc,
+                                 int64_t w = -1) {
+    if (c0 + 8 <= (w < 0 ? d : w) && c0 < d) {
       uint4 v = *reinterpret_cast<const uint4 *>(p);
       float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                     bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(x[e], x[e], acc[e]);
+      for (int e = 0; e < 8; ++e) {
+        const float y = (c0 + e < d) ? x[e] : 0.f;
+        acc[e] = fmaf(y, y, acc[e]);
+      }
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
@@ -46,7 +52,7 @@ struct Loader<uint16_t, 8> {
 // f32, 4 per lane: one 16-byte load.
 template <>
 struct Loader<float, 4> {
-  __device__ static void load_sq(const float *p, int64_t c0, int64_t d, float *acc) {
+  __device__ static void load_sq(const float *p, int64_t c0, int64_t d, float *acc, int64_t = -1) {
     if (c0 + 4 <= d) {
       float4 v = *reinterpret_cast<const float4 *>(p);
       acc[0] = fmaf(v.x, v.x, acc[0]);
@@ -64,7 +70,7 @@ struct Loader<float, 4> {
 // Scalar fallback for layouts that forbid 16-byte loads.
 template <typename T>
 struct Loader<T, 1> {
-  __device__ static void load_sq(const T *p, int64_t c0, int64_t d, float *acc) {
+  __device__ static void load_sq(const T *p, int64_t c0, int64_t d, float *acc, int64_t = -1) {
     if (c0 < d) {
       float x;
       if constexpr (sizeof(T) == 2) x = bf16_to_f32(*p);
@@ -116,12 +122,12 @@ __global__ __launch_bounds__(kThreads) void colnorm_kernel(const T *__restrict__
     // four rows in flight per lane
     for (; r + 3 * RPB < r_end; r += 4 * RPB) {
       const T *p = Ab + r * lda;
-      Loader<T, VEC>::load_sq(p, c0, lim(r), acc);
-      Loader<T, VEC>::load_sq(p + RPB * lda, c0, lim(r + RPB), acc);
-      Loader<T, VEC>::load_sq(p + 2 * RPB * lda, c0, lim(r + 2 * RPB), acc);
-      Loader<T, VEC>::load_sq(p + 3 * RPB * lda, c0, lim(r + 3 * RPB), acc);
+      Loader<T, VEC>::load_sq(p, c0, lim(r), acc, d);
+      Loader<T, VEC>::load_sq(p + RPB * lda, c0, lim(r + RPB), acc, d);
+      Loader<T, VEC>::load_sq(p + 2 * RPB * lda, c0, lim(r + 2 * RPB), acc, d);
+      Loader<T, VEC>::load_sq(p + 3 * RPB * lda, c0, lim(r + 3 * RPB), acc, d);
     }
-    for (; r < r_end; r += RPB) Loader<T, VEC>::load_sq(Ab + r * lda, c0, lim(r), acc);
+    for (; r < r_end; r += RPB) Loader<T, VEC>::load_sq(Ab + r * lda, c0, lim(r), acc, d);
   }
 
   // Fold the lanes that share a column (lane, lane^TPR, lane^2TPR, ...).
@@ -147,15 +153,36 @@ __global__ __launch_bounds__(kThreads) void colnorm_kernel(const T *__restrict__
   }
 }
 
-// scores[b][j] = sqrt(sum over chunks, in chunk order, of part[c][b][j]).
-__global__ __launch_bounds__(256) void colnorm_finish(const float *__restrict__ part,
-                                                      int64_t chunks, int64_t n,
-                                                      float *__restrict__ scores) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
+// scores[b][j] = sqrt(sum over chunks of part[c][b][j]) in a fixed order:
+// 16 thread groups each add the chunks c = g, g + 16, ... (eight loads in
+// flight per step), then the 16 group sums are added in group order.
+constexpr int kFinCols = 64, kFinGroups = 16;
+__global__ __launch_bounds__(kFinCols * kFinGroups) void colnorm_finish(const float *__restrict__ part,
+                                                                      int64_t chunks, int64_t n,
+                                                                      float *__restrict__ scores) {
+  __shared__ float red[kFinGroups][kFinCols];
+  const int col = threadIdx.x % kFinCols, grp = threadIdx.x / kFinCols;
+  const int64_t i = (int64_t)blockIdx.x * kFinCols + col;
   float s = 0.f;
-  for (int64_t c = 0; c < chunks; ++c) s += part[c * n + i];
-  scores[i] = __builtin_sqrtf(s);
+  if (i < n) {
+    int64_t c = grp;
+    for (; c + 7 * kFinGroups < chunks; c += 8 * kFinGroups) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(c + u * kFinGroups) * n + i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; c < chunks; c += kFinGroups) s += part[c * n + i];
+  }
+  red[grp][col] = s;
+  __syncthreads();
+  if (grp == 0 && i < n) {
+    float t = 0.f;
+#pragma unroll
+    for (int q = 0; q < kFinGroups; ++q) t += red[q][col];
+    scores[i] = __builtin_sqrtf(t);
+  }
 }
 
 template <typename T, int VEC, bool CAUSAL>
@@ -188,9 +215,12 @@ ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch, bo
   p.tpr = tpr;
   p.col_tiles = ceil_div(d, (int64_t)tpr * p.vec);
   const int64_t rpb = (int64_t)kWaves * (64 / tpr);
-  // Aim for ~2048 blocks, but give each block at least 8 steps of rows.
+  // Aim for ~4096 blocks of at most ~1024 rows, but give each block at least
+  // 8 steps of rows.
   const int64_t tiles = p.col_tiles * batch;
-  int64_t want_chunks = ceil_div(2048, tiles);
+  int64_t want_chunks = ceil_div(4096, tiles);
+  if (want_chunks < ceil_div(m, 1024)) want_chunks = ceil_div(m, 1024);
+  if (want_chunks > 256) want_chunks = 256;
   int64_t max_chunks = ceil_div(m, rpb * 8);
   int64_t chunks = want_chunks < max_chunks ? want_chunks : max_chunks;
   if (chunks < 1) chunks = 1;
@@ -229,7 +259,7 @@ hipError_t launch_colnorm(rmm_dtype_t dt, const void *A, int64_t m, int64_t d, i
   if (e != hipSuccess || single) return e;
   const int64_t n = batch * d;
   KernelTimer timer("colnorm_finish", st);
-  hipLaunchKernelGGL(colnorm_finish, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL(colnorm_finish, dim3((unsigned)ceil_div(n, kFinCols)), dim3(kFinCols * kFinGroups), 0, st,
                      static_cast<const float *>(ws), p.chunks, n, scores);
   return hipGetLastError();
 }

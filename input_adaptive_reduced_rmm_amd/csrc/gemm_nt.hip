@@ -1,0 +1,315 @@
+// Reduced projection GEMM for many rows: Y = A_I B_I with both operands packed
+// K-contiguous ("Mecanismo Central": A_{:,I} B_{I,:}).
+//
+// When m is large the product is MFMA-bound and the weight slice B_I is
+// re-read by every row tile, so it pays to lay it out once for the matrix
+// cores: `bt_pack` writes B_I^T[n][t] = B[idx[t], n] (zero for padding
+// slots) into the workspace, the same way A_I is packed.  The weights
+// themselves are only read.  Both operand tiles then come straight from
+// memory into LDS with `buffer_load_dwordx4 ... lds` (no staging registers,
+// no in-loop transposes), which leaves the register file to the 256
+// accumulators of a 128 x 128 wave tile and to double-buffered MFMA
+// fragments.
+//
+// Block tile 256 x 256 x 64, 4 waves of 128 x 128, two LDS stages (128 KiB).
+// LDS rows hold 64 bf16 with the 16-byte chunk index XOR-swizzled by the row;
+// since one direct load writes 64 consecutive 16-byte LDS chunks, each lane
+// fetches the global chunk that the swizzle maps onto its LDS slot.  The
+// MFMA takes the B fragment as its first operand so each lane ends up with
+// four consecutive output columns of one row, which the epilogue stages in
+// LDS and writes back as 16-byte row segments.
+#include "mfma_gemm.h"
+#include "rmm_internal.h"
+#include "timing.h"
+
+#define LDS_AS __attribute__((address_space(3)))
+
+namespace rmm {
+namespace {
+
+using mg::bf16x8_t;
+using mg::f32x16_t;
+using mg::rsrc_t;
+
+constexpr int kBM = 256, kBN = 256, kBK = 64;   // kBK: slot granularity of the packed operands
+
+// ---------------------------------------------------------------- B_I^T pack
+// grid: x = 256-wide column block of B, y = 64-wide block of kept slots.
+// Each thread loads an 8 (slots) x 8 (columns) block, transposes it in
+// registers into eight 16-byte K-runs, parks them in LDS as [n][64], and the
+// block then writes 256 rows of 128 contiguous bytes.
+template <bool BVEC>
+__global__ __launch_bounds__(256) void bt_pack_kernel(const uint16_t *__restrict__ B, int64_t ldb,
+                                                      int64_t d, int64_t n,
+                                                      const int32_t *__restrict__ idx_clean,
+                                                      int64_t k_pad, uint16_t *__restrict__ BT) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[256 * kBK];
+  const int tid = threadIdx.x;
+  const int64_t n0 = (int64_t)blockIdx.x * 256;
+  const int64_t t0 = (int64_t)blockIdx.y * kBK;
+  const int nb = tid & 31, tb = tid >> 5;          // columns nb*8.., slots tb*8..
+  const rsrc_t rb = mg::make_rsrc(B + n0, ((uint64_t)(d - 1) * ldb + (n - n0)) * 2);
+  const int4 s0 = *reinterpret_cast<const int4 *>(idx_clean + t0 + tb * 8);
+  const int4 s1 = *reinterpret_cast<const int4 *>(idx_clean + t0 + tb * 8 + 4);
+  const int32_t src[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  uint4 r[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint32_t off = src[q] >= 0 ? (uint32_t)(((int64_t)src[q] * ldb + nb * 8) * 2) : mg::kOOB;
+    r[q] = mg::load_chunk<BVEC>(rb, off);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t w[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q] = mg::u4get(r[q], e);
+    const uint4 ev = make_uint4((w[0] & 0xFFFFu) | (w[1] << 16), (w[2] & 0xFFFFu) | (w[3] << 16),
+                                (w[4] & 0xFFFFu) | (w[5] << 16), (w[6] & 0xFFFFu) | (w[7] << 16));
+    const uint4 od = make_uint4((w[0] >> 16) | (w[1] & 0xFFFF0000u), (w[2] >> 16) | (w[3] & 0xFFFF0000u),
+                                (w[4] >> 16) | (w[5] & 0xFFFF0000u), (w[6] >> 16) | (w[7] & 0xFFFF0000u));
+    const int nr = nb * 8 + 2 * e;
+    *reinterpret_cast<uint4 *>(&tile[mg::swz(nr, tb)]) = ev;
+    *reinterpret_cast<uint4 *>(&tile[mg::swz(nr + 1, tb)]) = od;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = tid + 256 * i;
+    const int row = c >> 3, kc = c & 7;
+    if (n0 + row < n)
+      *reinterpret_cast<uint4 *>(BT + (n0 + row) * k_pad + t0 + kc * 8) =
+          *reinterpret_cast<const uint4 *>(&tile[mg::swz(row, kc)]);
+  }
+}
+
+// ---------------------------------------------------------------- GEMM
+struct NtArgs {
+  const uint16_t *A;   // [m][k_pad]
+  const uint16_t *BT;  // [n][k_pad]
+  uint16_t *Y;
+  int64_t ldy, m, n, k_pad, tiles_m, tiles_n;
+};
+
+// LDS operand tiles are [256 rows][BK] bf16: CH = BK/8 16-byte chunks per
+// row, the chunk index XOR-swizzled by the row so that the 32 consecutive
+// rows an MFMA fragment read touches spread over the banks.
+template <int BK>
+__device__ __forceinline__ int lswz(int row, int c) {
+  constexpr int CH = BK / 8;
+  const int f = CH == 8 ? ((row ^ (row >> 3)) & 7) : ((row >> 2) & (CH - 1));
+  return row * BK + ((c ^ f) << 3);
+}
+
+// 16 bytes per lane from the buffer straight into LDS: the wave's 64 lanes
+// fill the 1 KiB at `lds` in lane order.  (A plain function, so that the
+// kernel templates stay instantiable in the host compilation pass.)
+__device__ __forceinline__ void lds_load16(rsrc_t r, unsigned char *lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void *)lds, 16, voff, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) for the counts the pipelines below use (lgkmcnt and
+// expcnt untouched); encoding: vmcnt[3:0] | vmcnt[5:4] << 14.
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 16: __builtin_amdgcn_s_waitcnt(0x4F70); break;
+    case 24: __builtin_amdgcn_s_waitcnt(0x4F78); break;
+    case 32: __builtin_amdgcn_s_waitcnt(0x8F70); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+}
+
+// BK-deep K tiles, NST LDS stages (NST - 1 tiles in flight while one is multiplied).
+template <int BK, int NST>
+__global__ __launch_bounds__(256) void gemm_nt_kernel(NtArgs g) {
+  constexpr int CH = BK / 8;                       // chunks per LDS row
+  constexpr int TILE = 256 * BK * 2;               // bytes of one operand tile
+  constexpr int STAGE = 2 * TILE;
+  constexpr int LPW = 256 * CH / 64 / 4;           // direct loads per wave per operand
+  constexpr int RPI = 64 / CH;                     // rows covered by one wave load
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * STAGE];
+  static_assert(NST * STAGE >= 4 * 128 * 128 * 2, "epilogue staging must fit");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int64_t tm, tn;
+  mg::tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  const int64_t m0 = tm * kBM, n0 = tn * kBN;
+  const int64_t rows = g.m - m0 < kBM ? g.m - m0 : kBM;
+  const int64_t cols = g.n - n0 < kBN ? g.n - n0 : kBN;
+  const rsrc_t ra = mg::make_rsrc(g.A + m0 * g.k_pad, (uint64_t)rows * g.k_pad * 2);
+  const rsrc_t rb = mg::make_rsrc(g.BT + n0 * g.k_pad, (uint64_t)cols * g.k_pad * 2);
+
+  // Direct load i of this wave writes the 1 KiB LDS block q = 4 i + wave:
+  // rows q*RPI + lane/CH, slot lane%CH.  The swizzle is an XOR, so slot s of
+  // a row holds logical chunk s ^ f(row): that is the chunk the lane fetches.
+  uint32_t voff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int row = (4 * i + wave) * RPI + lane / CH;
+    const int slot = lane % CH;
+    const int logical = (lswz<BK>(row, slot) - row * BK) >> 3;
+    voff[i] = (uint32_t)(((int64_t)row * g.k_pad + logical * 8) * 2);
+  }
+  auto issue = [&](int kt, int stage) {
+    unsigned char *sa = smem + stage * STAGE;
+    unsigned char *sb = sa + TILE;
+    const uint32_t koff = (uint32_t)kt * (BK * 2);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      lds_load16(ra, sa + (4 * i + wave) * 1024, voff[i] + koff);
+      lds_load16(rb, sb + (4 * i + wave) * 1024, voff[i] + koff);
+    }
+  };
+
+  f32x16_t acc[4][4];   // [n tile j][m tile i]: D = B_frag x A_frag^T
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
+
+  const int nk = (int)(g.k_pad / BK);
+  // Prologue: the first NST-1 tiles in flight.
+#pragma unroll
+  for (int p = 0; p < NST - 1; ++p)
+    if (p < nk) issue(p, p);
+
+  const int lrow = lane & 31, lk = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    // Tile kt has landed once at most (tiles issued after it) * 2*LPW loads remain.
+    const int after = (nk - 1 - kt) < (NST - 2) ? (nk - 1 - kt) : (NST - 2);
+    wait_vm(after * 2 * LPW);
+    __syncthreads();   // every wave's share of tile kt is in LDS; stage (kt-1)%NST is free
+    if (kt + NST - 1 < nk) issue(kt + NST - 1, (kt + NST - 1) % NST);
+    const uint16_t *As = reinterpret_cast<const uint16_t *>(smem + (kt % NST) * STAGE);
+    const uint16_t *Bs = As + 256 * BK;
+    bf16x8_t av[2][4], bv[2][4];
+    auto frags = [&](int ks, int slot) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        av[slot][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
+                                                       &As[lswz<BK>(wm * 128 + i * 32 + lrow, ks * 2 + lk)]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bv[slot][j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
+                                                       &Bs[lswz<BK>(wn * 128 + j * 32 + lrow, ks * 2 + lk)]));
+    };
+    frags(0, 0);
+#ifndef RMM_NT_IGLP
+#define RMM_NT_IGLP 0
+#endif
+#if RMM_NT_IGLP >= 0
+    // Let the scheduler interleave the fragment reads with the MFMAs.
+    __builtin_amdgcn_iglp_opt(RMM_NT_IGLP);
+#endif
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) frags(ks + 1, (ks + 1) & 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[ks & 1][j], av[ks & 1][i], acc[j][i], 0, 0, 0);
+    }
+  }
+  __syncthreads();   // all fragment reads done before the staging area is reused
+
+  // Epilogue.  acc[j][i] register r of lane l holds Y[row, col] with
+  // row = i*32 + l%32 and col = j*32 + 8*(r/4) + 4*(l/32) + r%4: four
+  // consecutive columns per (r/4).  Stage the wave's 128 x 128 bf16 tile in
+  // LDS ([row][128], 16-byte chunks XOR-swizzled by row) and write it back
+  // as 16-byte row segments.
+  uint16_t *stage = reinterpret_cast<uint16_t *>(smem) + wave * (128 * 128);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int row = i * 32 + lrow;
+        const int col = j * 32 + 8 * gq + 4 * lk;
+        const uint32_t lo = (uint32_t)f32_to_bf16(acc[j][i][4 * gq + 0]) |
+                            ((uint32_t)f32_to_bf16(acc[j][i][4 * gq + 1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(acc[j][i][4 * gq + 2]) |
+                            ((uint32_t)f32_to_bf16(acc[j][i][4 * gq + 3]) << 16);
+        const int chunk = (col >> 3) ^ (row & 15);
+        *reinterpret_cast<uint2 *>(&stage[row * 128 + chunk * 8 + (col & 7)]) = make_uint2(lo, hi);
+        // convert and park one 4-column group at a time (keeps the VGPR
+        // pressure of the epilogue low)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  const int64_t rbase = m0 + wm * 128, cbase = n0 + wn * 128;
+  const bool vec = (g.ldy % 8 == 0) && (reinterpret_cast<uintptr_t>(g.Y) % 16 == 0) && cbase + 128 <= g.n;
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int row = it * 4 + (lane >> 4);
+    const int ch = lane & 15;
+    const uint4 v = *reinterpret_cast<const uint4 *>(&stage[row * 128 + ((ch ^ (row & 15)) * 8)]);
+    const int64_t gr = rbase + row;
+    if (gr >= g.m) continue;
+    uint16_t *dst = g.Y + gr * g.ldy + cbase + ch * 8;
+    if (vec) {
+      *reinterpret_cast<uint4 *>(dst) = v;
+    } else {
+      const uint16_t e[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
+                             (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (cbase + ch * 8 + q < g.n) dst[q] = e[q];
+    }
+  }
+}
+
+#ifndef RMM_NT_BK
+#define RMM_NT_BK 64
+#define RMM_NT_NST 2
+#endif
+// Explicit instantiation of the configuration launched below.
+template __global__ void gemm_nt_kernel<RMM_NT_BK, RMM_NT_NST>(NtArgs);
+
+}  // namespace
+
+size_t gemm_nt_bt_bytes(int64_t n, int64_t k_pad) { return align_up((size_t)n * k_pad * 2, 256); }
+
+bool gemm_nt_ok(int64_t m, int64_t n, int64_t d, int64_t ldb, int64_t k_pad) {
+  return m >= 1024 && (uint64_t)256 * k_pad * 2 < mg::kMaxRecords &&
+         (uint64_t)((d - 1) * ldb + n) * 2 < mg::kMaxRecords;
+}
+
+hipError_t launch_gemm_nt(const void *A_packed, const int32_t *idx_clean, const void *B, int64_t ldb,
+                          int64_t d, void *BT_ws, void *Y, int64_t ldy, int64_t m, int64_t n,
+                          int64_t k_pad, hipStream_t st) {
+  const bool bvec = reinterpret_cast<uintptr_t>(B) % 16 == 0 && ldb % 8 == 0;
+  {
+    dim3 grid((unsigned)ceil_div(n, 256), (unsigned)(k_pad / kBK));
+    KernelTimer timer("bt_pack", st);
+    if (bvec)
+      hipLaunchKernelGGL(bt_pack_kernel<true>, grid, dim3(256), 0, st, static_cast<const uint16_t *>(B), ldb, d,
+                         n, idx_clean, k_pad, static_cast<uint16_t *>(BT_ws));
+    else
+      hipLaunchKernelGGL(bt_pack_kernel<false>, grid, dim3(256), 0, st, static_cast<const uint16_t *>(B), ldb,
+                         d, n, idx_clean, k_pad, static_cast<uint16_t *>(BT_ws));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  NtArgs g;
+  g.A = static_cast<const uint16_t *>(A_packed);
+  g.BT = static_cast<const uint16_t *>(BT_ws);
+  g.Y = static_cast<uint16_t *>(Y);
+  g.ldy = ldy;
+  g.m = m;
+  g.n = n;
+  g.k_pad = k_pad;
+  g.tiles_m = ceil_div(m, kBM);
+  g.tiles_n = ceil_div(n, kBN);
+  KernelTimer timer("gemm_nt", st);
+  hipLaunchKernelGGL((gemm_nt_kernel<RMM_NT_BK, RMM_NT_NST>), dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(256),
+                     0, st, g);
+  return hipGetLastError();
+}
+
+}  // namespace rmm

@@ -145,9 +145,16 @@ __global__ __launch_bounds__(256) void mfma_gemm(Args g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int64_t tm, tn;
-  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
-  // Causal P V: the last row blocks stream the most tiles, so start them first.
-  if (MODE == kMaskedTiles && g.causal) tm = g.tiles_m - 1 - tm;
+  if (MODE == kMaskedTiles && g.causal) {
+    // Causal P V: a row block streams about as many tiles as its index, so
+    // dispatch the heaviest first and deal consecutive ones to different
+    // XCDs (no XCD-contiguous ranges here: they would stack the heavy blocks
+    // of every head on the same XCD).
+    tm = g.tiles_m - 1 - (int64_t)blockIdx.x / g.tiles_n;
+    tn = (int64_t)blockIdx.x % g.tiles_n;
+  } else {
+    tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  }
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const int64_t b = blockIdx.z;
   const int64_t grp = (b * g.hkv) / g.hq;

@@ -73,6 +73,13 @@ enum class OutType { BF16, F32 };
 hipError_t launch_gemm_bf16(const GemmArgs &a, OutType out, hipStream_t stream);
 hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t stream);
 
+// ------------------------------------------------------------------ NT GEMM for many rows
+size_t gemm_nt_bt_bytes(int64_t n, int64_t k_pad);
+bool gemm_nt_ok(int64_t m, int64_t n, int64_t d, int64_t ldb, int64_t k_pad);
+hipError_t launch_gemm_nt(const void *A_packed, const int32_t *idx_clean, const void *B, int64_t ldb,
+                          int64_t d, void *BT_ws, void *Y, int64_t ldy, int64_t m, int64_t n,
+                          int64_t k_pad, hipStream_t stream);
+
 // ------------------------------------------------------------------ feature-reduced Q K^T
 bool qk_layout_ok(int64_t Lq, int64_t dh, int64_t ldkt, int64_t Lk, int64_t k_pad);
 hipError_t launch_qk(const void *Apacked, const int32_t *idx_clean, const void *Kt, int64_t kt_hs,
