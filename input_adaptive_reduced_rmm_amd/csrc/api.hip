@@ -56,18 +56,22 @@ struct Carve {
 };
 
 rmm::ColnormPlan plan_for(rmm_dtype_t dt, const void *A, int64_t m, int64_t d, int64_t lda,
-                          int64_t batch, int64_t bs) {
+                          int64_t batch, int64_t bs, bool causal = false) {
   const int64_t v = 16 / (int64_t)esize(dt);
   const bool vec = aligned(A, 16) && lda % v == 0 && (batch == 1 || bs % v == 0);
-  return rmm::colnorm_plan(dt, m, d, batch, vec);
+  return rmm::colnorm_plan(dt, m, d, batch, vec, causal);
 }
 
-// Worst case over alignments: the scalar plan has the most chunks only when
-// the vector plan does not; take the max of both.
+// Worst case over alignments and the causal / full plans (they may differ in
+// chunk count): the largest of the four.
 size_t colnorm_ws(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch) {
-  const size_t a = rmm::colnorm_ws_bytes(rmm::colnorm_plan(dt, m, d, batch, true), d, batch);
-  const size_t b = rmm::colnorm_ws_bytes(rmm::colnorm_plan(dt, m, d, batch, false), d, batch);
-  return a > b ? a : b;
+  size_t best = 0;
+  for (int v = 0; v < 2; ++v)
+    for (int c = 0; c < 2; ++c) {
+      const size_t b = rmm::colnorm_ws_bytes(rmm::colnorm_plan(dt, m, d, batch, v != 0, c != 0), d, batch);
+      if (b > best) best = b;
+    }
+  return best;
 }
 
 }  // namespace
@@ -329,7 +333,7 @@ RMM_API rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, i
   hipStream_t st = (hipStream_t)stream;
   const int64_t k_pad = rmm_k_pad(k);
 
-  const rmm::ColnormPlan p = plan_for(RMM_BF16, P, Lq, Lk, ldp, Hq, p_head_stride);
+  const rmm::ColnormPlan p = plan_for(RMM_BF16, P, Lq, Lk, ldp, Hq, p_head_stride, causal != 0);
   hipError_t he = rmm::launch_colnorm(RMM_BF16, P, Lq, Lk, ldp, Hq, p_head_stride, scores, w + o_part, p, st,
                                       causal != 0, Lk - Lq);
   if (he != hipSuccess) return hip_status(he, "pv colnorm launch");

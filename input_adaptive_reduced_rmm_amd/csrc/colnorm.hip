@@ -17,6 +17,13 @@ namespace rmm {
 namespace {
 
 constexpr int kThreads = 256;
+#ifndef RMM_CN_UNROLL
+#define RMM_CN_UNROLL 4
+#endif
+#ifndef RMM_CN_ROWS
+#define RMM_CN_ROWS 1024
+#endif
+constexpr int kUnroll = RMM_CN_UNROLL;
 constexpr int kWaves = kThreads / 64;
 
 template <typename T, int VEC>
@@ -114,20 +121,26 @@ __global__ __launch_bounds__(kThreads) void colnorm_kernel(const T *__restrict__
       // Rows i < col0 - coff reach no column of this tile; keep the lane's row phase.
       const int64_t first = col0 - coff;
       if (first > r_begin) r += ((first - r_begin) / RPB) * RPB;
+      // Rows that cut through the tile's columns: per-element limits.  From
+      // row col0 + CT - 1 - coff on, every column of the tile is kept and the
+      // plain loop below takes over.
+      int64_t band = col0 + CT - 1 - coff;
+      if (band > r_end) band = r_end;
+      for (; r + (kUnroll - 1) * RPB < band; r += kUnroll * RPB) {
+        const T *p = Ab + r * lda;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+          Loader<T, VEC>::load_sq(p + u * RPB * lda, c0, min(d, r + u * RPB + coff + 1), acc, d);
+      }
+      for (; r < band; r += RPB) Loader<T, VEC>::load_sq(Ab + r * lda, c0, min(d, r + coff + 1), acc, d);
     }
-    auto lim = [&](int64_t row) -> int64_t {
-      if constexpr (CAUSAL) return min(d, row + coff + 1);
-      else return d;
-    };
-    // four rows in flight per lane
-    for (; r + 3 * RPB < r_end; r += 4 * RPB) {
+    // kUnroll rows in flight per lane
+    for (; r + (kUnroll - 1) * RPB < r_end; r += kUnroll * RPB) {
       const T *p = Ab + r * lda;
-      Loader<T, VEC>::load_sq(p, c0, lim(r), acc, d);
-      Loader<T, VEC>::load_sq(p + RPB * lda, c0, lim(r + RPB), acc, d);
-      Loader<T, VEC>::load_sq(p + 2 * RPB * lda, c0, lim(r + 2 * RPB), acc, d);
-      Loader<T, VEC>::load_sq(p + 3 * RPB * lda, c0, lim(r + 3 * RPB), acc, d);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) Loader<T, VEC>::load_sq(p + u * RPB * lda, c0, d, acc);
     }
-    for (; r < r_end; r += RPB) Loader<T, VEC>::load_sq(Ab + r * lda, c0, lim(r), acc, d);
+    for (; r < r_end; r += RPB) Loader<T, VEC>::load_sq(Ab + r * lda, c0, d, acc);
   }
 
   // Fold the lanes that share a column (lane, lane^TPR, lane^2TPR, ...).
@@ -205,13 +218,18 @@ hipError_t dispatch_tpr(int tpr, dim3 grid, const T *A, int64_t m, int64_t d, in
 
 }  // namespace
 
-ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch, bool vec_ok) {
+ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch, bool vec_ok, bool causal) {
   ColnormPlan p;
   const int esz = dt == RMM_BF16 ? 2 : 4;
   p.vec = vec_ok ? 16 / esz : 1;
   const int64_t lanes_needed = ceil_div(d, p.vec);
+  // Causal: blocks on and above the diagonal carry less work or none, and a
+  // grid of uneven blocks ends in a ragged last round; narrower column tiles
+  // (16 lanes, 256-byte row segments) make the blocks small enough that the
+  // tail stays short.
+  const int max_tpr = causal ? 16 : 64;
   int tpr = 1;
-  while (tpr < 64 && tpr < lanes_needed) tpr <<= 1;
+  while (tpr < max_tpr && tpr < lanes_needed) tpr <<= 1;
   p.tpr = tpr;
   p.col_tiles = ceil_div(d, (int64_t)tpr * p.vec);
   const int64_t rpb = (int64_t)kWaves * (64 / tpr);
@@ -219,7 +237,7 @@ ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch, bo
   // 8 steps of rows.
   const int64_t tiles = p.col_tiles * batch;
   int64_t want_chunks = ceil_div(4096, tiles);
-  if (want_chunks < ceil_div(m, 1024)) want_chunks = ceil_div(m, 1024);
+  if (want_chunks < ceil_div(m, RMM_CN_ROWS)) want_chunks = ceil_div(m, RMM_CN_ROWS);
   if (want_chunks > 256) want_chunks = 256;
   int64_t max_chunks = ceil_div(m, rpb * 8);
   int64_t chunks = want_chunks < max_chunks ? want_chunks : max_chunks;

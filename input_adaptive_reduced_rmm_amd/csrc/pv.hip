@@ -79,6 +79,230 @@ __global__ __launch_bounds__(kPlanThreads) void pv_plan_kernel(const int32_t *__
   if (tid == 0) counts[h] = (int32_t)wsum[2 * kPlanWaves - 1];
 }
 
+
+struct PvArgs {
+  const uint16_t *P;       // [hq] x [Lq rows of ldp]
+  int64_t ldp, p_hs;
+  const uint16_t *V;       // [Lk tokens of v_ts] x [hkv of v_hs]
+  int64_t v_ts, v_hs;
+  uint16_t *O;             // [Lq tokens of o_ts] x [hq of o_hs]
+  int64_t o_ts, o_hs;
+  const int32_t *tiles;    // [hq][ntiles] ascending 64-token tiles with a kept token
+  const uint64_t *masks;   // keep mask of each listed tile
+  const int32_t *counts;   // listed tiles per head
+  int64_t ntiles, hq, hkv, Lq, Lk, dh;
+  int64_t tiles_m, tiles_n;
+  int causal;
+  int64_t coff;            // causal: token j is visible from query row i when j <= i + coff
+};
+
+constexpr int kBN = 128;     // output columns per block (head_dim 128 in one tile)
+constexpr int kEpiPitch = kBN + 8;
+
+// Reduced P V for one (row block, column block, head).  The 64-token tiles of
+// the head's list are streamed two ahead of the MFMA: the registers hold the
+// loads of tile q+1 and q+2 while tile q is multiplied from LDS, so each block
+// keeps two tiles of P (2 x BM x 128 B) in flight.  Dropped tokens are zeroed
+// in both the P tile and the V rows (their V rows are not even loaded), and
+// on tiles that straddle the causal diagonal the entries above it are zeroed
+// per row, so the values stored there are never used.
+template <int BM, bool AVEC, bool BVEC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void pv_kernel(PvArgs g) {
+  constexpr int WTM = BM / 2;                 // wave tile rows (2 x 2 waves)
+  constexpr int TM = WTM / 32, TN = 2;        // 32 x 32 MFMA tiles per wave
+  constexpr int A_CH = BM / 32;               // 16-byte P chunks per thread per tile
+  constexpr int KB = 4;                       // V rows per thread per tile (x 8 columns)
+  constexpr int NB = kBN / 8;                 // threads across a V row
+  constexpr int kStage = (BM + kBN) * mg::kBK;
+  static_assert(BM * kEpiPitch <= 2 * kStage, "epilogue staging must fit the operand buffers");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  // Block order: rounds of one row block over every (head, column block); in
+  // causal mode the heaviest row blocks (the most tiles) come first across all
+  // heads, so the lightest ones fill the tail.  Within a round, workgroups are
+  // dealt round-robin to the 8 XCDs: give each XCD a contiguous run of heads,
+  // i.e. whole KV groups, so its L2 holds the V rows of few groups.
+  const int64_t per_round = g.hq * g.tiles_n;
+  const int64_t rnd = (int64_t)blockIdx.x / per_round, w = (int64_t)blockIdx.x % per_round;
+  const int64_t hw = per_round % 8 == 0 ? (w % 8) * (per_round / 8) + w / 8 : w;
+  const int64_t h = hw / g.tiles_n, tn = hw % g.tiles_n;
+  const int64_t tm = g.causal ? g.tiles_m - 1 - rnd : rnd;
+  const int64_t m0 = tm * BM, n0 = tn * kBN;
+  const int64_t grp = (h * g.hkv) / g.hq;
+  const int64_t rows = g.Lq - m0 < BM ? g.Lq - m0 : BM;
+
+  const uint16_t *Pb = g.P + h * g.p_hs + m0 * g.ldp;
+  const mg::rsrc_t rp = mg::make_rsrc(Pb, ((uint64_t)(rows - 1) * g.ldp + g.Lk) * 2);
+  const uint16_t *Vb = g.V + grp * g.v_hs + n0;
+  const mg::rsrc_t rv = mg::make_rsrc(Vb, ((uint64_t)(g.Lk - 1) * g.v_ts + (g.dh - n0)) * 2);
+
+  const int akc = tid & 7;                    // P chunk column within a tile
+  const int bnb = tid % NB, bkb = tid / NB;   // V block: tokens bkb*KB.., columns bnb*8..
+  const int32_t *tl = g.tiles + h * g.ntiles;
+  const uint64_t *ml = g.masks + h * g.ntiles;
+  int nk = g.counts[h];
+  if (g.causal) {
+    // keep the listed tiles that start at or before the block's last visible column
+    const int64_t last_col = m0 + rows - 1 + g.coff;
+    int lo = 0, hi = nk;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)tl[mid] * mg::kBK <= last_col) lo = mid + 1;
+      else hi = mid;
+    }
+    nk = lo;
+  }
+
+  uint4 ra[2][A_CH], rb[2][KB];
+  uint64_t mk[2] = {0, 0};
+  int64_t cc[2] = {0, 0};
+
+  // Loads of listed tile q into register slot S (no use of the data here).
+  auto issue = [&](auto slot, int q) {
+    constexpr int S = decltype(slot)::value;
+    const uint64_t m = ml[q];
+    const int64_t c0 = (int64_t)tl[q] * mg::kBK;
+    mk[S] = m;
+    cc[S] = c0;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int row = (tid >> 3) + 32 * i;
+      ra[S][i] = mg::load_chunk<AVEC>(rp, (uint32_t)(((int64_t)row * g.ldp + c0 + akc * 8) * 2));
+    }
+#pragma unroll
+    for (int r = 0; r < KB; ++r) {
+      const int t = bkb * KB + r;
+      const uint32_t off = ((m >> t) & 1ull) ? (uint32_t)(((c0 + t) * g.v_ts + bnb * 8) * 2) : mg::kOOB;
+      rb[S][r] = mg::load_chunk<BVEC>(rv, off);
+    }
+  };
+
+  // Mask register slot S and write it into LDS buffer S.
+  auto stage = [&](auto slot) {
+    constexpr int S = decltype(slot)::value;
+    uint16_t *As = smem + S * kStage;
+    uint16_t *Bs = As + BM * mg::kBK;
+    const uint64_t m = mk[S];
+    const int64_t c0 = cc[S];
+    const bool diag = g.causal && c0 + mg::kBK - 1 > m0 + g.coff;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int row = (tid >> 3) + 32 * i;
+      uint32_t bits = (uint32_t)(m >> (akc * 8)) & 0xFFu;
+      if (diag) {
+        // columns c0 + akc*8 + e are visible only while <= m0 + row + coff
+        const int64_t allow = m0 + row + g.coff - (c0 + akc * 8) + 1;
+        bits &= allow >= 8 ? 0xFFu : allow <= 0 ? 0u : ((1u << allow) - 1u);
+      }
+      *reinterpret_cast<uint4 *>(&As[mg::swz(row, akc)]) = mg::mask8(ra[S][i], bits);
+    }
+    // 4 tokens x 8 columns per thread -> each column gets an 8-byte half K-run.
+    const int kc = bkb >> 1, half = (bkb & 1) * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t w[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = mg::u4get(rb[S][r], q);
+      const uint2 ev = make_uint2((w[0] & 0xFFFFu) | (w[1] << 16), (w[2] & 0xFFFFu) | (w[3] << 16));
+      const uint2 od = make_uint2((w[0] >> 16) | (w[1] & 0xFFFF0000u), (w[2] >> 16) | (w[3] & 0xFFFF0000u));
+      const int n_ev = bnb * 8 + 2 * q;
+      *reinterpret_cast<uint2 *>(&Bs[mg::swz(n_ev, kc) + half]) = ev;
+      *reinterpret_cast<uint2 *>(&Bs[mg::swz(n_ev + 1, kc) + half]) = od;
+    }
+  };
+
+  mg::f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int lrow = lane & 31, lk = lane >> 5;
+  auto mma = [&](auto slot) {
+    constexpr int S = decltype(slot)::value;
+    const uint16_t *As = smem + S * kStage;
+    const uint16_t *Bs = As + BM * mg::kBK;
+#pragma unroll
+    for (int ks = 0; ks < mg::kBK / 16; ++ks) {
+      mg::bf16x8_t av[TM], bv[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        av[i] = __builtin_bit_cast(mg::bf16x8_t, *reinterpret_cast<const uint4 *>(
+                                                      &As[mg::swz(wm * WTM + i * 32 + lrow, ks * 2 + lk)]));
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bv[j] = __builtin_bit_cast(mg::bf16x8_t, *reinterpret_cast<const uint4 *>(
+                                                      &Bs[mg::swz(wn * 64 + j * 32 + lrow, ks * 2 + lk)]));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Tile q sits in LDS buffer q & 1; registers of slot (q + 1) & 1 hold tile q + 1.
+  auto step = [&](auto par, int q) {
+    constexpr int S = decltype(par)::value;
+    using Other = std::integral_constant<int, 1 - S>;
+    if (q + 2 < nk) issue(par, q + 2);
+    mma(par);
+    if (q + 1 < nk) stage(Other{});
+    __syncthreads();
+  };
+
+  using Zero = std::integral_constant<int, 0>;
+  using One = std::integral_constant<int, 1>;
+  if (nk > 0) {
+    issue(Zero{}, 0);
+    if (nk > 1) issue(One{}, 1);
+    stage(Zero{});
+    __syncthreads();
+  }
+  for (int q = 0; q < nk; q += 2) {
+    step(Zero{}, q);
+    if (q + 1 < nk) step(One{}, q + 1);
+  }
+
+  // Epilogue: bf16 tile through LDS (the operand buffers are free after the
+  // loop's last barrier), then 16-byte row segments.  D of a 32x32 tile:
+  // lane l holds column l%32; register r holds row 8*(r/4) + 4*(l/32) + r%4.
+  uint16_t *E = smem;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
+        E[row * kEpiPitch + wn * 64 + j * 32 + lrow] = f32_to_bf16(acc[i][j][r]);
+      }
+  __syncthreads();
+  uint16_t *Oh = g.O + h * g.o_hs;
+  const int cch = tid & 15;                  // 16-byte chunk of a 128-column row
+  const int64_t col = n0 + cch * 8;
+  const bool vec = col + 8 <= g.dh && g.o_ts % 8 == 0 && g.o_hs % 8 == 0 &&
+                   reinterpret_cast<uintptr_t>(g.O) % 16 == 0;
+#pragma unroll
+  for (int it = 0; it < BM / 16; ++it) {
+    const int row = it * 16 + (tid >> 4);
+    if (row >= rows) break;
+    const uint16_t *src = &E[row * kEpiPitch + cch * 8];
+    uint16_t *dst = Oh + (m0 + row) * g.o_ts + col;
+    if (vec) {
+      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (col + e < g.dh) dst[e] = src[e];
+    }
+  }
+}
+
 }  // namespace
 
 int64_t pv_max_tokens() { return (int64_t)kMaxTiles * 64; }
@@ -108,51 +332,42 @@ hipError_t launch_pv(const void *P, int64_t ldp, int64_t p_hs, const void *V, in
 #ifndef RMM_PV_BM
 #define RMM_PV_BM 128
 #endif
-#ifndef RMM_PV_STAGES
-#define RMM_PV_STAGES 2
-#endif
-  constexpr int BM = RMM_PV_BM, BN = 128, STG = RMM_PV_STAGES;
-  mg::Args a{};
-  a.A = static_cast<const uint16_t *>(P);
-  a.lda = ldp;
-  a.a_bs = p_hs;
-  a.a_cols = Lk;
-  a.B = static_cast<const uint16_t *>(V);
-  a.ldb = v_ts;
-  a.b_bs = v_hs;
+  constexpr int BM = RMM_PV_BM;
+  PvArgs a{};
+  a.P = static_cast<const uint16_t *>(P);
+  a.ldp = ldp;
+  a.p_hs = p_hs;
+  a.V = static_cast<const uint16_t *>(V);
+  a.v_ts = v_ts;
+  a.v_hs = v_hs;
+  a.O = static_cast<uint16_t *>(O);
+  a.o_ts = o_ts;
+  a.o_hs = o_hs;
   a.tiles = tiles;
   a.masks = masks;
   a.counts = counts;
   a.ntiles = nt;
-  a.Y = O;
-  a.ldy = o_ts;
-  a.y_bs = o_hs;
-  a.batch = hq;
   a.hq = hq;
   a.hkv = hkv;
-  a.m = Lq;
-  a.n = dh;
-  a.d = Lk;
+  a.Lq = Lq;
+  a.Lk = Lk;
+  a.dh = dh;
   a.tiles_m = ceil_div(Lq, BM);
-  a.tiles_n = ceil_div(dh, BN);
+  a.tiles_n = ceil_div(dh, kBN);
   a.causal = causal ? 1 : 0;
-  a.causal_off = Lk - Lq;
-  dim3 grid((unsigned)(a.tiles_m * a.tiles_n), 1, (unsigned)hq);
+  a.coff = Lk - Lq;
+  dim3 grid((unsigned)(a.tiles_m * a.tiles_n * hq));
   KernelTimer timer("pv_gemm", st);
   const bool avec = reinterpret_cast<uintptr_t>(P) % 16 == 0 && ldp % 8 == 0 && p_hs % 8 == 0;
   const bool bvec = reinterpret_cast<uintptr_t>(V) % 16 == 0 && v_ts % 8 == 0 && v_hs % 8 == 0;
   if (avec && bvec)
-    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, mg::kMaskedTiles, uint16_t, STG, true, true>), grid, dim3(256), 0,
-                       st, a);
+    hipLaunchKernelGGL((pv_kernel<BM, true, true>), grid, dim3(256), 0, st, a);
   else if (avec)
-    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, mg::kMaskedTiles, uint16_t, STG, true, false>), grid, dim3(256), 0,
-                       st, a);
+    hipLaunchKernelGGL((pv_kernel<BM, true, false>), grid, dim3(256), 0, st, a);
   else if (bvec)
-    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, mg::kMaskedTiles, uint16_t, STG, false, true>), grid, dim3(256), 0,
-                       st, a);
+    hipLaunchKernelGGL((pv_kernel<BM, false, true>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, mg::kMaskedTiles, uint16_t, STG, false, false>), grid, dim3(256),
-                       0, st, a);
+    hipLaunchKernelGGL((pv_kernel<BM, false, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -56,6 +56,11 @@ constexpr int kOperandBytes = 2 * kT * mg::kBK * 2;        // A and B tiles
 constexpr int kStageBytes = 4 * 32 * kPitch * 4;           // 4 waves x 32 rows
 constexpr int kSmemBytes = kOperandBytes > kStageBytes ? kOperandBytes : kStageBytes;
 
+// Resident workgroups per CU (four waves each; the register count allows two).
+#ifndef RMM_QK_BPC
+#define RMM_QK_BPC 2
+#endif
+
 template <bool BVEC>
 __global__ __launch_bounds__(256) void qk_persistent(QkArgs g) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
@@ -68,9 +73,13 @@ __global__ __launch_bounds__(256) void qk_persistent(QkArgs g) {
   const int bnb = tid & 15, bkb = tid >> 4;   // B block: k rows bkb*4.., columns bnb*8..
   const int nk = (int)(g.k_pad / mg::kBK);
 
-  for (int64_t t = blockIdx.x; t < g.total; t += gridDim.x) {
-    const int64_t h = t / g.per_head;
-    const int64_t loc = t - h * g.per_head;
+  struct Tile {
+    int64_t h, m0, n0, grp, rows;
+  };
+  auto tile_at = [&](int64_t t) -> Tile {
+    Tile ti;
+    ti.h = t / g.per_head;
+    const int64_t loc = t - ti.h * g.per_head;
     // row of tiles holding `loc`: largest tm with tiles_before(tm) <= loc
     int64_t lo = 0, hi = g.tiles_m - 1;
     while (lo < hi) {
@@ -78,16 +87,38 @@ __global__ __launch_bounds__(256) void qk_persistent(QkArgs g) {
       if (tiles_before(mid, g.c0, g.tiles_n) <= loc) lo = mid;
       else hi = mid - 1;
     }
-    const int64_t tm = lo;
-    const int64_t tn = loc - tiles_before(tm, g.c0, g.tiles_n);
-    const int64_t m0 = tm * kT, n0 = tn * kT;
-    const int64_t grp = (h * g.hkv) / g.hq;
-    const int64_t rows = g.Lq - m0 < kT ? g.Lq - m0 : kT;
-    const rsrc_t ra = mg::make_rsrc(g.A + (h * g.Lq + m0) * g.k_pad, (uint64_t)rows * g.k_pad * 2);
-    const uint16_t *Bb = g.Kt + grp * g.kt_hs + n0;
-    const rsrc_t rb = mg::make_rsrc(Bb, ((uint64_t)(g.dh - 1) * g.ldkt + (g.Lk - n0)) * 2);
-    const int32_t *ib = g.idx + h * g.k_pad;
+    ti.m0 = lo * kT;
+    ti.n0 = (loc - tiles_before(lo, g.c0, g.tiles_n)) * kT;
+    ti.grp = (ti.h * g.hkv) / g.hq;
+    ti.rows = g.Lq - ti.m0 < kT ? g.Lq - ti.m0 : kT;
+    return ti;
+  };
 
+  uint4 ra4[4], rb4[4];
+  // Issue the loads of K tile q of output tile `ti` into ra4/rb4.
+  auto issue = [&](const Tile &ti, int q) {
+    const int64_t c0 = (int64_t)q * mg::kBK;
+    const rsrc_t ra = mg::make_rsrc(g.A + (ti.h * g.Lq + ti.m0) * g.k_pad, (uint64_t)ti.rows * g.k_pad * 2);
+    const rsrc_t rb = mg::make_rsrc(g.Kt + ti.grp * g.kt_hs + ti.n0,
+                                    ((uint64_t)(g.dh - 1) * g.ldkt + (g.Lk - ti.n0)) * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (tid >> 3) + 32 * i;
+      ra4[i] = mg::bload16(ra, (uint32_t)(((int64_t)row * g.k_pad + c0 + akc * 8) * 2));
+    }
+    const int4 src = *reinterpret_cast<const int4 *>(g.idx + ti.h * g.k_pad + c0 + bkb * 4);
+    const int32_t s4[4] = {src.x, src.y, src.z, src.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t off = s4[r] >= 0 ? (uint32_t)(((int64_t)s4[r] * g.ldkt + bnb * 8) * 2) : mg::kOOB;
+      rb4[r] = mg::load_chunk<BVEC>(rb, off);
+    }
+  };
+
+  int64_t t = blockIdx.x;
+  Tile cur = tile_at(t < g.total ? t : 0);
+  if (t < g.total) issue(cur, 0);
+  for (; t < g.total; t += gridDim.x) {
     f32x16_t acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -97,21 +128,8 @@ __global__ __launch_bounds__(256) void qk_persistent(QkArgs g) {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     for (int q = 0; q < nk; ++q) {
-      const int64_t c0 = (int64_t)q * mg::kBK;
-      uint4 ra4[4], rb4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = (tid >> 3) + 32 * i;
-        ra4[i] = mg::bload16(ra, (uint32_t)(((int64_t)row * g.k_pad + c0 + akc * 8) * 2));
-      }
-      const int4 src = *reinterpret_cast<const int4 *>(ib + c0 + bkb * 4);
-      const int32_t s4[4] = {src.x, src.y, src.z, src.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t off = s4[r] >= 0 ? (uint32_t)(((int64_t)s4[r] * g.ldkt + bnb * 8) * 2) : mg::kOOB;
-        rb4[r] = mg::load_chunk<BVEC>(rb, off);
-      }
-      if (q > 0) __syncthreads();   // the previous K tile has been consumed
+      if (q > 0) issue(cur, q);
+      __syncthreads();   // previous users of the LDS (operands or staging) are done
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = (tid >> 3) + 32 * i;
@@ -150,15 +168,22 @@ __global__ __launch_bounds__(256) void qk_persistent(QkArgs g) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
       }
     }
+    // Prefetch the next output tile's first K tile before this tile's stores:
+    // on this architecture one counter tracks loads and stores in issue order,
+    // so loads issued after the stores would also wait for them.
+    const Tile ti = cur;
+    const bool more = t + gridDim.x < g.total;
+    if (more) cur = tile_at(t + gridDim.x);
+    if (more) issue(cur, 0);
     __syncthreads();   // every wave is done reading the operand tiles
 
     // Epilogue through LDS: each wave parks 32 x 64 floats of its tile at a
     // time (row pitch 68 floats keeps the column-strided writes and the
     // row-wise reads on distinct banks), then writes them back as 16-byte
     // row segments: one store instruction covers 4 rows x 256 bytes.
-    float *Sh = g.S + h * g.s_hs;
+    float *Sh = g.S + ti.h * g.s_hs;
     float *stage = reinterpret_cast<float *>(smem) + wave * (32 * kPitch);
-    const bool full_cols = n0 + kT <= g.Lk && (g.lds % 4 == 0) &&
+    const bool full_cols = ti.n0 + kT <= g.Lk && (g.lds % 4 == 0) &&
                            (reinterpret_cast<uintptr_t>(Sh) % 16 == 0);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -169,8 +194,8 @@ __global__ __launch_bounds__(256) void qk_persistent(QkArgs g) {
           stage[(8 * (r >> 2) + 4 * lk + (r & 3)) * kPitch + j * 32 + lrow] = acc[i][j][r];
       __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's LDS writes are done
       __builtin_amdgcn_wave_barrier();
-      const int64_t rbase = m0 + wm * 64 + i * 32;
-      const int64_t cbase = n0 + wn * 64;
+      const int64_t rbase = ti.m0 + wm * 64 + i * 32;
+      const int64_t cbase = ti.n0 + wn * 64;
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
         const int rr = it * 4 + (lane >> 4);
@@ -191,7 +216,6 @@ __global__ __launch_bounds__(256) void qk_persistent(QkArgs g) {
       }
       __builtin_amdgcn_wave_barrier();
     }
-    __syncthreads();   // staging area reused as operand tiles by the next tile
   }
 }
 
@@ -243,8 +267,7 @@ hipError_t launch_qk(const void *Apacked, const int32_t *idx_clean, const void *
   g.total = g.per_head * hq;
   if (g.total == 0) return hipSuccess;
   const bool bvec = reinterpret_cast<uintptr_t>(Kt) % 16 == 0 && ldkt % 8 == 0 && kt_hs % 8 == 0;
-  // Three resident workgroups per CU on 256 CUs.
-  int64_t grid = 256 * 3;
+  int64_t grid = 256 * RMM_QK_BPC;
   if (grid > g.total) grid = g.total;
   KernelTimer timer("qk_gemm", st);
   if (bvec)

@@ -35,7 +35,8 @@ struct ColnormPlan {
   int64_t rows_per_chunk;
   int64_t chunks;        // row chunks; partial sums per chunk when > 1
 };
-ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch, bool vec_ok);
+ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch, bool vec_ok,
+                         bool causal = false);
 size_t colnorm_ws_bytes(const ColnormPlan &p, int64_t d, int64_t batch);
 // causal (bf16 only): entry (i, j) is zero and not read when j > i + coff.
 hipError_t launch_colnorm(rmm_dtype_t dt, const void *A, int64_t m, int64_t d, int64_t lda,
