@@ -294,7 +294,6 @@ hipError_t launch_core(const GemmArgs &g, const char *name, hipStream_t st) {
   a.A = static_cast<const uint16_t *>(g.A);
   a.lda = g.k_pad;
   a.a_bs = g.m * g.k_pad;
-  a.a_cols = g.k_pad;
   a.B = static_cast<const uint16_t *>(g.B);
   a.ldb = g.ldb;
   a.b_bs = g.b_batch_stride;
@@ -312,15 +311,13 @@ hipError_t launch_core(const GemmArgs &g, const char *name, hipStream_t st) {
   a.k_pad = g.k_pad;
   a.tiles_m = (g.m + BM - 1) / BM;
   a.tiles_n = (g.n + BN - 1) / BN;
-  a.causal = g.causal;
-  a.causal_off = g.causal_off;
   dim3 grid((unsigned)(a.tiles_m * a.tiles_n), 1, (unsigned)g.batch);
   KernelTimer timer(name, st);
   if (bvec)
-    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, mg::kGatherRows, OUT, STAGES, true, true>), grid, dim3(256), 0,
+    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, OUT, STAGES, true, true>), grid, dim3(256), 0,
                        st, a);
   else
-    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, mg::kGatherRows, OUT, STAGES, true, false>), grid, dim3(256), 0,
+    hipLaunchKernelGGL((mg::mfma_gemm<BM, BN, OUT, STAGES, true, false>), grid, dim3(256), 0,
                        st, a);
   return hipGetLastError();
 }

@@ -33,6 +33,18 @@ using mg::rsrc_t;
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;   // kBK: slot granularity of the packed operands
 
+// Pipeline shape of the GEMM below: K-tile depth and LDS stages.
+#ifndef RMM_NT_BK
+#define RMM_NT_BK 64
+#define RMM_NT_NST 2
+#endif
+#ifndef RMM_NT_PIN
+#define RMM_NT_PIN 1
+#endif
+#ifndef RMM_NT_IGLP
+#define RMM_NT_IGLP 1   // scheduling hint for the MFMA / LDS-read interleave (-1: none)
+#endif
+
 // ---------------------------------------------------------------- B_I^T pack
 // grid: x = 256-wide column block of B, y = 64-wide block of kept slots.
 // Each thread loads an 8 (slots) x 8 (columns) block, transposes it in
@@ -109,14 +121,14 @@ __device__ __forceinline__ void lds_load16(rsrc_t r, unsigned char *lds, uint32_
 
 // s_waitcnt vmcnt(n) for the counts the pipelines below use (lgkmcnt and
 // expcnt untouched); encoding: vmcnt[3:0] | vmcnt[5:4] << 14.
+constexpr int vm_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-    case 16: __builtin_amdgcn_s_waitcnt(0x4F70); break;
-    case 24: __builtin_amdgcn_s_waitcnt(0x4F78); break;
-    case 32: __builtin_amdgcn_s_waitcnt(0x8F70); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+#define RMM_VM(N) \
+  case N: __builtin_amdgcn_s_waitcnt(vm_imm(N)); break;
+    RMM_VM(0) RMM_VM(8) RMM_VM(16) RMM_VM(24) RMM_VM(32) RMM_VM(40) RMM_VM(48) RMM_VM(56)
+#undef RMM_VM
+    default: __builtin_amdgcn_s_waitcnt(vm_imm(0)); break;
   }
 }
 
@@ -171,49 +183,79 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(NtArgs g) {
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
 
   const int nk = (int)(g.k_pad / BK);
-  // Prologue: the first NST-1 tiles in flight.
-#pragma unroll
-  for (int p = 0; p < NST - 1; ++p)
-    if (p < nk) issue(p, p);
-
   const int lrow = lane & 31, lk = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    // Tile kt has landed once at most (tiles issued after it) * 2*LPW loads remain.
-    const int after = (nk - 1 - kt) < (NST - 2) ? (nk - 1 - kt) : (NST - 2);
-    wait_vm(after * 2 * LPW);
-    __syncthreads();   // every wave's share of tile kt is in LDS; stage (kt-1)%NST is free
-    if (kt + NST - 1 < nk) issue(kt + NST - 1, (kt + NST - 1) % NST);
+  bf16x8_t av[2][4], bv[2][4];
+  auto frags = [&](int kt, int ks, int slot) {
     const uint16_t *As = reinterpret_cast<const uint16_t *>(smem + (kt % NST) * STAGE);
     const uint16_t *Bs = As + 256 * BK;
-    bf16x8_t av[2][4], bv[2][4];
-    auto frags = [&](int ks, int slot) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      av[slot][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
+                                                     &As[lswz<BK>(wm * 128 + i * 32 + lrow, ks * 2 + lk)]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bv[slot][j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
+                                                     &Bs[lswz<BK>(wn * 128 + j * 32 + lrow, ks * 2 + lk)]));
+  };
+  auto mfmas = [&](int slot) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        av[slot][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
-                                                       &As[lswz<BK>(wm * 128 + i * 32 + lrow, ks * 2 + lk)]));
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[slot][j], av[slot][i], acc[j][i], 0, 0, 0);
+  };
+  // NST stages hold tiles kt .. kt+NST-1.  The barrier sits ahead of each
+  // tile's last K-slice: once every wave holds tile kt's last fragments in
+  // registers, tile kt+NST may overwrite its stage, and the first fragments of
+  // tile kt+1 are read while the last MFMAs of tile kt run.  Each tile thus
+  // has NST-1 K-steps to arrive.
+  constexpr int KS = BK / 16;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bv[slot][j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
-                                                       &Bs[lswz<BK>(wn * 128 + j * 32 + lrow, ks * 2 + lk)]));
-    };
-    frags(0, 0);
-#ifndef RMM_NT_IGLP
-#define RMM_NT_IGLP 0
-#endif
+  for (int p = 0; p < NST; ++p)
+    if (p < nk) issue(p, p);
+  {
+    const int c0 = (NST - 1) < (nk - 1) ? (NST - 1) : (nk - 1);
+    wait_vm((c0 > 0 ? c0 : 0) * 2 * LPW);
+  }
+  __syncthreads();
+  if (nk > 0) frags(0, 0, 0);
+  // One K-step; ISSUE is a compile-time flag so that the steady-state loop
+  // is a single basic block the scheduler can order as written.
+  auto step = [&](int kt, auto issue_flag) {
+    constexpr bool ISSUE = decltype(issue_flag)::value;
 #if RMM_NT_IGLP >= 0
-    // Let the scheduler interleave the fragment reads with the MFMAs.
     __builtin_amdgcn_iglp_opt(RMM_NT_IGLP);
 #endif
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) frags(ks + 1, (ks + 1) & 1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[ks & 1][j], av[ks & 1][i], acc[j][i], 0, 0, 0);
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      frags(kt, ks + 1, (ks + 1) & 1);
+      mfmas(ks & 1);
     }
-  }
+    // Tile kt+1 must have landed: tiles kt+2 .. min(kt+NST-1, nk-1) may still be in flight.
+    if constexpr (ISSUE) {
+      wait_vm((NST - 2) * 2 * LPW);
+    } else {
+      const int c = nk - 2 - kt < NST - 2 ? nk - 2 - kt : NST - 2;
+      wait_vm((c > 0 ? c : 0) * 2 * LPW);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): tile kt's fragment reads are done
+    __syncthreads();
+    if constexpr (ISSUE) {
+      issue(kt + NST, kt % NST);
+#if RMM_NT_PIN
+      // Keep the loads ahead of this slice's MFMAs: the scheduler would
+      // otherwise sink them below, cutting the time they have to arrive.
+      __builtin_amdgcn_sched_barrier(0);
+#endif
+      frags(kt + 1, 0, 0);
+    } else {
+      if (kt + 1 < nk) frags(kt + 1, 0, 0);
+    }
+    mfmas((KS - 1) & 1);
+  };
+  int kt = 0;
+  for (; kt + NST < nk; ++kt) step(kt, std::true_type{});
+  for (; kt < nk; ++kt) step(kt, std::false_type{});
   __syncthreads();   // all fragment reads done before the staging area is reused
 
   // Epilogue.  acc[j][i] register r of lane l holds Y[row, col] with
@@ -264,10 +306,6 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(NtArgs g) {
   }
 }
 
-#ifndef RMM_NT_BK
-#define RMM_NT_BK 64
-#define RMM_NT_NST 2
-#endif
 // Explicit instantiation of the configuration launched below.
 template __global__ void gemm_nt_kernel<RMM_NT_BK, RMM_NT_NST>(NtArgs);
 

@@ -1,15 +1,11 @@
-// Shared bf16 MFMA GEMM core for the reduced products.
+// Shared bf16 MFMA GEMM core for the reduced products, and the buffer-load,
+// swizzle and masking helpers the other MFMA kernels use.
 //
-// Y[b] = A_b[:, K-tiles] * B_g(b)[rows of those K-tiles, :], float32 accumulation,
-// on v_mfma_f32_32x32x16_bf16.  Two ways of naming the K-tiles:
-//
-//   kGatherRows  (X W projections, Q K^T): A is the packed kept-column slice
-//                [m][k_pad] (K-contiguous), K-tile q covers packed columns
-//                64q..64q+63, and B row t of the tile is B[idx[t], :] with idx
-//                a cleaned index list (-1 = contributes zero).
-//   kMaskedTiles (P V): A is P itself (token-contiguous rows), the K-tiles are
-//                the 64-token tiles listed for the batch entry, each with a
-//                64-bit keep mask; dropped tokens are zeroed in both A and B.
+// Y[b] = A_b[:, I] * B_g(b)[I, :], float32 accumulation, on
+// v_mfma_f32_32x32x16_bf16.  A is the packed kept-column slice [m][k_pad]
+// (K-contiguous); K-tile q covers packed columns 64q..64q+63, and B row t of
+// the tile is B[idx[t], :] with idx a cleaned index list (-1 = contributes
+// zero).
 //
 // Memory access: every global load is a raw buffer load whose resource covers
 // exactly the bytes the block may touch, so rows past the matrix end and the
@@ -37,28 +33,19 @@ constexpr int kBK = 64;
 constexpr uint32_t kOOB = 0xFFFFFFF0u;       // offset that always falls outside a resource
 constexpr uint64_t kMaxRecords = 0xFFFFFF00ull;
 
-enum Mode { kGatherRows = 0, kMaskedTiles = 1 };
-
 struct Args {
   const uint16_t *A;
   int64_t lda, a_bs;            // A row stride, batch stride (elements)
-  int64_t a_cols;               // valid columns of A (kMaskedTiles: Lk)
   const uint16_t *B;
   int64_t ldb, b_bs;            // B row stride, kv-group stride
-  const int32_t *idx;           // kGatherRows: cleaned [batch][k_pad]
+  const int32_t *idx;           // cleaned [batch][k_pad]
   int64_t idx_bs;
-  const int32_t *tiles;         // kMaskedTiles: [batch][ntiles]
-  const uint64_t *masks;
-  const int32_t *counts;
-  int64_t ntiles;
   void *Y;
   int64_t ldy, y_bs;
   int64_t batch, hq, hkv;       // batch entry b reads B group floor(b*hkv/hq)
   int64_t m, n, d;              // d = rows of B
-  int64_t k_pad;                // kGatherRows
+  int64_t k_pad;
   int64_t tiles_m, tiles_n;
-  int causal;                   // causal attention: only columns j <= row + causal_off matter
-  int64_t causal_off;
 };
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint64_t bytes) {
@@ -131,7 +118,7 @@ __device__ __forceinline__ void tile_of(int64_t w, int64_t tiles_m, int64_t tile
 }
 
 // AVEC / BVEC: 16-byte loads for A / B (rows 16-byte aligned), else 2-byte loads.
-template <int BM, int BN, int MODE, typename OUT, int STAGES, bool AVEC, bool BVEC>
+template <int BM, int BN, typename OUT, int STAGES, bool AVEC, bool BVEC>
 __global__ __launch_bounds__(256) void mfma_gemm(Args g) {
   constexpr int WTM = BM / 2, WTN = BN / 2;   // wave tile (2 x 2 waves)
   constexpr int TM = WTM / 32, TN = WTN / 32; // MFMA tiles per wave
@@ -145,29 +132,15 @@ __global__ __launch_bounds__(256) void mfma_gemm(Args g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int64_t tm, tn;
-  if (MODE == kMaskedTiles && g.causal) {
-    // Causal P V: a row block streams about as many tiles as its index, so
-    // dispatch the heaviest first and deal consecutive ones to different
-    // XCDs (no XCD-contiguous ranges here: they would stack the heavy blocks
-    // of every head on the same XCD).
-    tm = g.tiles_m - 1 - (int64_t)blockIdx.x / g.tiles_n;
-    tn = (int64_t)blockIdx.x % g.tiles_n;
-  } else {
-    tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
-  }
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const int64_t b = blockIdx.z;
   const int64_t grp = (b * g.hkv) / g.hq;
   const int64_t rows = g.m - m0 < BM ? g.m - m0 : BM;
-  // Causal Q K^T: an output tile whose every column lies above the diagonal is
-  // not needed by a causal softmax and is not computed.
-  if (MODE == kGatherRows && g.causal && n0 > m0 + rows - 1 + g.causal_off) return;
 
   // Resources: the block's A rows and its B column panel.
   const uint16_t *Ab = g.A + b * g.a_bs + m0 * g.lda;
-  const uint64_t a_bytes = MODE == kGatherRows ? (uint64_t)rows * g.lda * 2
-                                               : ((uint64_t)(rows - 1) * g.lda + g.a_cols) * 2;
-  const rsrc_t ra_r = make_rsrc(Ab, a_bytes);
+  const rsrc_t ra_r = make_rsrc(Ab, (uint64_t)rows * g.lda * 2);
   const uint16_t *Bb = g.B + grp * g.b_bs + n0;
   const rsrc_t rb_r = make_rsrc(Bb, ((uint64_t)(g.d - 1) * g.ldb + (g.n - n0)) * 2);
 
@@ -175,46 +148,26 @@ __global__ __launch_bounds__(256) void mfma_gemm(Args g) {
   const int bnb = tid % NB, bkb = tid / NB;   // B block: rows bkb*KB.., columns bnb*8..
 
   const int32_t *idxb = g.idx + b * g.idx_bs;
-  const int32_t *tl = g.tiles + b * g.ntiles;
-  const uint64_t *ml = g.masks + b * g.ntiles;
-  int nk = MODE == kGatherRows ? (int)(g.k_pad / kBK) : g.counts[b];
-  if (MODE == kMaskedTiles && g.causal) {
-    // Tiles are ascending: keep those that start at or before the block's last
-    // allowed column (binary search on the uniform tile list).
-    const int64_t last_col = m0 + rows - 1 + g.causal_off;
-    int lo = 0, hi = nk;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if ((int64_t)tl[mid] * kBK <= last_col) lo = mid + 1;
-      else hi = mid;
-    }
-    nk = lo;
-  }
+  const int nk = (int)(g.k_pad / kBK);
 
   uint4 ra[A_CH], rb[KB];
-  int32_t inext[KB];          // kGatherRows: source rows of the next tile to load
-  uint64_t mk_cur = 0, mk_next = 0;
-  int64_t c_cur = 0, c_next = 0;   // kMaskedTiles: first column of the current / next tile
+  int32_t inext[KB];          // source rows of the next tile to load
 
   auto load_idx = [&](int q, int32_t *dst) {
-    if constexpr (MODE == kGatherRows) {
-      const int4 *p = reinterpret_cast<const int4 *>(idxb + (int64_t)q * kBK + bkb * KB);
+    const int4 *p = reinterpret_cast<const int4 *>(idxb + (int64_t)q * kBK + bkb * KB);
 #pragma unroll
-      for (int v = 0; v < KB / 4; ++v) {
-        const int4 x = p[v];
-        dst[4 * v] = x.x;
-        dst[4 * v + 1] = x.y;
-        dst[4 * v + 2] = x.z;
-        dst[4 * v + 3] = x.w;
-      }
+    for (int v = 0; v < KB / 4; ++v) {
+      const int4 x = p[v];
+      dst[4 * v] = x.x;
+      dst[4 * v + 1] = x.y;
+      dst[4 * v + 2] = x.z;
+      dst[4 * v + 3] = x.w;
     }
   };
 
   // Issue the loads of K-tile q (registers only; no use of the data here).
-  auto load_tile = [&](int q, const int32_t *src_rows, uint64_t mk) {
-    int64_t c0;
-    if constexpr (MODE == kGatherRows) c0 = (int64_t)q * kBK;
-    else c0 = (int64_t)tl[q] * kBK;
+  auto load_tile = [&](int q, const int32_t *src_rows) {
+    const int64_t c0 = (int64_t)q * kBK;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int row = (tid >> 3) + 32 * i;
@@ -222,36 +175,18 @@ __global__ __launch_bounds__(256) void mfma_gemm(Args g) {
     }
 #pragma unroll
     for (int r = 0; r < KB; ++r) {
-      uint32_t off;
-      if constexpr (MODE == kGatherRows) {
-        const int32_t s = src_rows[r];
-        off = s >= 0 ? (uint32_t)(((int64_t)s * g.ldb + bnb * 8) * 2) : kOOB;
-      } else {
-        const int t = bkb * KB + r;
-        off = ((mk >> t) & 1ull) ? (uint32_t)(((c0 + t) * g.ldb + bnb * 8) * 2) : kOOB;
-      }
+      const int32_t s = src_rows[r];
+      const uint32_t off = s >= 0 ? (uint32_t)(((int64_t)s * g.ldb + bnb * 8) * 2) : kOOB;
       rb[r] = load_chunk<BVEC>(rb_r, off);
     }
   };
 
   // Write the loaded registers of a tile into LDS stage `buf`.
-  auto store_tile = [&](int buf, uint64_t mk, int64_t c0) {
-    // Causal: does this tile reach past the diagonal of the block's first row?
-    const bool diag = MODE == kMaskedTiles && g.causal && c0 + kBK - 1 > m0 + g.causal_off;
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int row = (tid >> 3) + 32 * i;
-      uint4 v = ra[i];
-      if constexpr (MODE == kMaskedTiles) {
-        uint32_t bits = (uint32_t)(mk >> (akc * 8)) & 0xFFu;
-        if (diag) {
-          // columns c0 + akc*8 + e are kept only while <= m0 + row + causal_off
-          const int64_t allow = m0 + row + g.causal_off - (c0 + akc * 8) + 1;
-          bits &= allow >= 8 ? 0xFFu : allow <= 0 ? 0u : ((1u << allow) - 1u);
-        }
-        v = mask8(v, bits);
-      }
-      *reinterpret_cast<uint4 *>(&As[buf][swz(row, akc)]) = v;
+      *reinterpret_cast<uint4 *>(&As[buf][swz(row, akc)]) = ra[i];
     }
     if constexpr (KB == 8) {
       // 8 x 8 block -> column e gets one full 16-byte K-run (r0[e] .. r7[e]).
@@ -293,23 +228,13 @@ __global__ __launch_bounds__(256) void mfma_gemm(Args g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Prologue: tile 0 into stage 0; indices (or mask) of tile 1 in flight.
+  // Prologue: tile 0 into stage 0; indices of tile 1 in flight.
   if (nk > 0) {
-    if constexpr (MODE == kGatherRows) {
-      int32_t i0[KB];
-      load_idx(0, i0);
-      load_tile(0, i0, 0);
-      if (nk > 1) load_idx(1, inext);
-    } else {
-      mk_cur = ml[0];
-      c_cur = (int64_t)tl[0] * kBK;
-      load_tile(0, nullptr, mk_cur);
-      if (nk > 1) {
-        mk_next = ml[1];
-        c_next = (int64_t)tl[1] * kBK;
-      }
-    }
-    store_tile(0, mk_cur, c_cur);
+    int32_t i0[KB];
+    load_idx(0, i0);
+    load_tile(0, i0);
+    if (nk > 1) load_idx(1, inext);
+    store_tile(0);
     __syncthreads();
   }
 
@@ -318,12 +243,8 @@ __global__ __launch_bounds__(256) void mfma_gemm(Args g) {
     const int buf = STAGES == 2 ? (q & 1) : 0;
     const bool more = q + 1 < nk;
     if (more) {
-      if constexpr (MODE == kGatherRows) {
-        load_tile(q + 1, inext, 0);
-        if (q + 2 < nk) load_idx(q + 2, inext);
-      } else {
-        load_tile(q + 1, nullptr, mk_next);
-      }
+      load_tile(q + 1, inext);
+      if (q + 2 < nk) load_idx(q + 2, inext);
     }
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
@@ -344,15 +265,7 @@ __global__ __launch_bounds__(256) void mfma_gemm(Args g) {
     }
     if (more) {
       if constexpr (STAGES == 1) __syncthreads();
-      store_tile(STAGES == 2 ? (buf ^ 1) : 0, mk_next, c_next);
-      if constexpr (MODE == kMaskedTiles) {
-        mk_cur = mk_next;
-        c_cur = c_next;
-        if (q + 2 < nk) {
-          mk_next = ml[q + 2];
-          c_next = (int64_t)tl[q + 2] * kBK;
-        }
-      }
+      store_tile(STAGES == 2 ? (buf ^ 1) : 0);
     }
     __syncthreads();
   }

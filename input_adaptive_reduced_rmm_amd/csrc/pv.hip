@@ -6,9 +6,9 @@
 // (a 128-byte line holds 64 tokens), so the product works at that granularity
 // instead of packing: a small plan kernel turns each head's kept-token list
 // into the ascending list of 64-token tiles that hold at least one kept token,
-// each with a 64-bit keep mask.  The MFMA core (mfma_gemm.h, kMaskedTiles)
-// then streams, for its block of query rows, only those tiles of P, zeroes
-// the dropped tokens in both P and V while staging, and multiplies.  Dropped
+// each with a 64-bit keep mask.  The MFMA kernel below then streams, for its
+// block of query rows, only those tiles of P, zeroes the dropped tokens in
+// both P and V while staging, and multiplies.  Dropped
 // tokens contribute exact zeros and tiles without a kept token are never
 // read: the result is exactly the reduced product, with P read once at line
 // granularity and no packed copy written.

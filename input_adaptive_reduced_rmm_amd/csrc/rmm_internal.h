@@ -67,8 +67,6 @@ struct GemmArgs {
   int64_t ldy, y_batch_stride;
   int64_t batch, hq, hkv; // batch b reads B group floor(b*hkv/hq)
   int64_t m, n, d, k, k_pad;
-  int causal;             // skip output tiles with every column > row + causal_off
-  int64_t causal_off;
 };
 enum class OutType { BF16, F32 };
 hipError_t launch_gemm_bf16(const GemmArgs &a, OutType out, hipStream_t stream);
