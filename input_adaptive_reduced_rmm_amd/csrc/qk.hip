@@ -115,10 +115,16 @@ __global__ __launch_bounds__(256) void qk_persistent(QkArgs g) {
     }
   };
 
+  // Workgroups are dealt round-robin to the 8 XCDs.  The grid walks the tile
+  // list in rounds of gridDim.x consecutive tiles; within a round, give each
+  // XCD a contiguous run (gridDim.x / 8 tiles of mostly one row) so that its
+  // L2 serves the Q_I rows and kept K rows those tiles share.
+  const int64_t t_step = gridDim.x, t_end = g.total;
   int64_t t = blockIdx.x;
-  Tile cur = tile_at(t < g.total ? t : 0);
-  if (t < g.total) issue(cur, 0);
-  for (; t < g.total; t += gridDim.x) {
+  if (gridDim.x % 8 == 0) t = (int64_t)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+  Tile cur = tile_at(t < t_end ? t : 0);
+  if (t < t_end) issue(cur, 0);
+  for (; t < t_end; t += t_step) {
     f32x16_t acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -172,8 +178,8 @@ __global__ __launch_bounds__(256) void qk_persistent(QkArgs g) {
     // on this architecture one counter tracks loads and stores in issue order,
     // so loads issued after the stores would also wait for them.
     const Tile ti = cur;
-    const bool more = t + gridDim.x < g.total;
-    if (more) cur = tile_at(t + gridDim.x);
+    const bool more = t + t_step < t_end;
+    if (more) cur = tile_at(t + t_step);
     if (more) issue(cur, 0);
     __syncthreads();   // every wave is done reading the operand tiles
 
