@@ -117,6 +117,20 @@ __device__ __forceinline__ void tile_of(int64_t w, int64_t tiles_m, int64_t tile
   tn = (lt % span) / gsz;
 }
 
+// The same mapping in 32-bit arithmetic (tile counts below 2^31): 64-bit
+// division is a long VALU sequence, too costly inside a persistent loop.
+__device__ __forceinline__ void tile_of32(uint32_t w, uint32_t tiles_m, uint32_t tiles_n, uint32_t &tm,
+                                          uint32_t &tn) {
+  const uint32_t ntiles = tiles_m * tiles_n;
+  uint32_t lt = w;
+  if ((ntiles & 7) == 0) lt = (w & 7) * (ntiles >> 3) + (w >> 3);
+  const uint32_t span = kGroupM * tiles_n;
+  const uint32_t first_m = (lt / span) * kGroupM;
+  const uint32_t gsz = tiles_m - first_m < (uint32_t)kGroupM ? tiles_m - first_m : (uint32_t)kGroupM;
+  tm = first_m + (lt % span) % gsz;
+  tn = (lt % span) / gsz;
+}
+
 // AVEC / BVEC: 16-byte loads for A / B (rows 16-byte aligned), else 2-byte loads.
 template <int BM, int BN, typename OUT, int STAGES, bool AVEC, bool BVEC>
 __global__ __launch_bounds__(256) void mfma_gemm(Args g) {
