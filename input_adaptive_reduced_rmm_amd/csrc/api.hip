@@ -335,7 +335,7 @@ RMM_API rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, i
 
   const rmm::ColnormPlan p = plan_for(RMM_BF16, P, Lq, Lk, ldp, Hq, p_head_stride, causal != 0);
   hipError_t he = rmm::launch_colnorm(RMM_BF16, P, Lq, Lk, ldp, Hq, p_head_stride, scores, w + o_part, p, st,
-                                      causal != 0, Lk - Lq);
+                                      causal != 0, Lk - Lq, /*stream_loads=*/true);
   if (he != hipSuccess) return hip_status(he, "pv colnorm launch");
   he = rmm::launch_topk(scores, Hq, Lk, k, k_pad, idx, st);
   if (he != hipSuccess) return hip_status(he, "pv topk launch");

@@ -32,12 +32,26 @@ struct Loader;
 // bf16, 8 per lane: one 16-byte load.  `d` is the row's column limit; with a
 // separate matrix width `w` >= d (causal rows), a lane whose 8 columns stay
 // inside the row still loads them as one vector and drops those >= d.
+// NT: streaming (non-temporal) 16-byte loads, for matrices read once here
+// and too large to stay in any cache (attention probabilities).
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const void *p) {
+  if constexpr (NT) {
+    const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(t[0], t[1], t[2], t[3]);
+  } else {
+    return *reinterpret_cast<const uint4 *>(p);
+  }
+}
+
 template <>
 struct Loader<uint16_t, 8> {
+  template <bool NT = false>
   __device__ static void load_sq(const uint16_t *p, int64_t c0, int64_t d, float *acc,
                                  int64_t w = -1) {
     if (c0 + 8 <= (w < 0 ? d : w) && c0 < d) {
-      uint4 v = *reinterpret_cast<const uint4 *>(p);
+      uint4 v = load16<NT>(p);
       float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                     bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
 #pragma unroll
@@ -59,9 +73,12 @@ struct Loader<uint16_t, 8> {
 // f32, 4 per lane: one 16-byte load.
 template <>
 struct Loader<float, 4> {
+  template <bool NT = false>
   __device__ static void load_sq(const float *p, int64_t c0, int64_t d, float *acc, int64_t = -1) {
     if (c0 + 4 <= d) {
-      float4 v = *reinterpret_cast<const float4 *>(p);
+      const uint4 u = load16<NT>(p);
+      const float4 v = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                                   __uint_as_float(u.w));
       acc[0] = fmaf(v.x, v.x, acc[0]);
       acc[1] = fmaf(v.y, v.y, acc[1]);
       acc[2] = fmaf(v.z, v.z, acc[2]);
@@ -77,6 +94,7 @@ struct Loader<float, 4> {
 // Scalar fallback for layouts that forbid 16-byte loads.
 template <typename T>
 struct Loader<T, 1> {
+  template <bool NT = false>
   __device__ static void load_sq(const T *p, int64_t c0, int64_t d, float *acc, int64_t = -1) {
     if (c0 < d) {
       float x;
@@ -91,7 +109,7 @@ struct Loader<T, 1> {
 // out: partial sums [chunk][batch][d] (or final scores when `final_sqrt`).
 // CAUSAL: entry (i, j) is taken as zero and not read when j > i + coff (a
 // causal attention matrix); rows that cannot reach a lane's columns are skipped.
-template <typename T, int VEC, int TPR, bool CAUSAL>
+template <typename T, int VEC, int TPR, bool CAUSAL, bool NT>
 __global__ __launch_bounds__(kThreads) void colnorm_kernel(const T *__restrict__ A, int64_t m,
                                                            int64_t d, int64_t lda,
                                                            int64_t batch_stride,
@@ -130,17 +148,17 @@ __global__ __launch_bounds__(kThreads) void colnorm_kernel(const T *__restrict__
         const T *p = Ab + r * lda;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-          Loader<T, VEC>::load_sq(p + u * RPB * lda, c0, min(d, r + u * RPB + coff + 1), acc, d);
+          Loader<T, VEC>::template load_sq<NT>(p + u * RPB * lda, c0, min(d, r + u * RPB + coff + 1), acc, d);
       }
-      for (; r < band; r += RPB) Loader<T, VEC>::load_sq(Ab + r * lda, c0, min(d, r + coff + 1), acc, d);
+      for (; r < band; r += RPB) Loader<T, VEC>::template load_sq<NT>(Ab + r * lda, c0, min(d, r + coff + 1), acc, d);
     }
     // kUnroll rows in flight per lane
     for (; r + (kUnroll - 1) * RPB < r_end; r += kUnroll * RPB) {
       const T *p = Ab + r * lda;
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) Loader<T, VEC>::load_sq(p + u * RPB * lda, c0, d, acc);
+      for (int u = 0; u < kUnroll; ++u) Loader<T, VEC>::template load_sq<NT>(p + u * RPB * lda, c0, d, acc);
     }
-    for (; r < r_end; r += RPB) Loader<T, VEC>::load_sq(Ab + r * lda, c0, d, acc);
+    for (; r < r_end; r += RPB) Loader<T, VEC>::template load_sq<NT>(Ab + r * lda, c0, d, acc);
   }
 
   // Fold the lanes that share a column (lane, lane^TPR, lane^2TPR, ...).
@@ -198,15 +216,15 @@ __global__ __launch_bounds__(kFinCols * kFinGroups) void colnorm_finish(const fl
   }
 }
 
-template <typename T, int VEC, bool CAUSAL>
+template <typename T, int VEC, bool CAUSAL, bool NT = false>
 hipError_t dispatch_tpr(int tpr, dim3 grid, const T *A, int64_t m, int64_t d, int64_t lda,
                         int64_t bs, int64_t rpc, float *out, int fin, int64_t coff, hipStream_t st) {
   KernelTimer timer("colnorm", st);
   switch (tpr) {
-#define RMM_CN(TP)                                                                          \
-  case TP:                                                                                  \
-    hipLaunchKernelGGL((colnorm_kernel<T, VEC, TP, CAUSAL>), grid, dim3(kThreads), 0, st, A, m, \
-                       d, lda, bs, rpc, out, fin, coff);                                    \
+#define RMM_CN(TP)                                                                                \
+  case TP:                                                                                        \
+    hipLaunchKernelGGL((colnorm_kernel<T, VEC, TP, CAUSAL, NT>), grid, dim3(kThreads), 0, st, A, m, \
+                       d, lda, bs, rpc, out, fin, coff);                                          \
     break;
     RMM_CN(1) RMM_CN(2) RMM_CN(4) RMM_CN(8) RMM_CN(16) RMM_CN(32) RMM_CN(64)
 #undef RMM_CN
@@ -255,7 +273,7 @@ size_t colnorm_ws_bytes(const ColnormPlan &p, int64_t d, int64_t batch) {
 
 hipError_t launch_colnorm(rmm_dtype_t dt, const void *A, int64_t m, int64_t d, int64_t lda,
                           int64_t batch, int64_t batch_stride, float *scores, void *ws,
-                          const ColnormPlan &p, hipStream_t st, bool causal, int64_t coff) {
+                          const ColnormPlan &p, hipStream_t st, bool causal, int64_t coff, bool stream) {
   const bool single = p.chunks == 1;
   float *out = single ? scores : static_cast<float *>(ws);
   dim3 grid((unsigned)p.col_tiles, (unsigned)p.chunks, (unsigned)batch);
@@ -263,12 +281,15 @@ hipError_t launch_colnorm(rmm_dtype_t dt, const void *A, int64_t m, int64_t d, i
   hipError_t e;
   if (dt == RMM_BF16) {
     const uint16_t *a = static_cast<const uint16_t *>(A);
-    if (causal)
-      e = p.vec == 8 ? dispatch_tpr<uint16_t, 8, true>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, coff, st)
-                     : dispatch_tpr<uint16_t, 1, true>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, coff, st);
+    if (p.vec != 8)
+      e = causal ? dispatch_tpr<uint16_t, 1, true>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, coff, st)
+                 : dispatch_tpr<uint16_t, 1, false>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, 0, st);
+    else if (causal)
+      e = stream ? dispatch_tpr<uint16_t, 8, true, true>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, coff, st)
+                 : dispatch_tpr<uint16_t, 8, true>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, coff, st);
     else
-      e = p.vec == 8 ? dispatch_tpr<uint16_t, 8, false>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, 0, st)
-                     : dispatch_tpr<uint16_t, 1, false>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, 0, st);
+      e = stream ? dispatch_tpr<uint16_t, 8, false, true>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, 0, st)
+                 : dispatch_tpr<uint16_t, 8, false>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, 0, st);
   } else {
     const float *a = static_cast<const float *>(A);
     e = p.vec == 4 ? dispatch_tpr<float, 4, false>(p.tpr, grid, a, m, d, lda, bs, rpc, out, single, 0, st)

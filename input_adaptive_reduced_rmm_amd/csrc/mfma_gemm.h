@@ -53,24 +53,30 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nr, 0x00020000);
 }
 
+// Cache policy of a buffer load: kNonTemporal streams data that is read once
+// and is far larger than the caches.
+constexpr int kCached = 0, kNonTemporal = 2;
+
+template <int POL = kCached>
 __device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POL));
 }
 
 // Eight 2-byte loads assembled into one 16-byte chunk (layouts whose rows are
 // not 16-byte aligned); each element is range-checked like the wide load.
+template <int POL = kCached>
 __device__ __forceinline__ uint4 bload16_e(rsrc_t r, uint32_t off) {
   uint32_t e[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q)
-    e[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)(off + 2u * q), 0, 0);
+    e[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)(off + 2u * q), 0, POL);
   return make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
 }
 
-template <bool VEC>
+template <bool VEC, int POL = kCached>
 __device__ __forceinline__ uint4 load_chunk(rsrc_t r, uint32_t off) {
-  if constexpr (VEC) return bload16(r, off);
-  else return bload16_e(r, off);
+  if constexpr (VEC) return bload16<POL>(r, off);
+  else return bload16_e<POL>(r, off);
 }
 
 __device__ __forceinline__ int swz(int row, int c) {

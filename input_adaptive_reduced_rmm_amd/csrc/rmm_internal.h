@@ -40,10 +40,11 @@ ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch, bo
                          bool causal = false);
 size_t colnorm_ws_bytes(const ColnormPlan &p, int64_t d, int64_t batch);
 // causal (bf16 only): entry (i, j) is zero and not read when j > i + coff.
+// stream (bf16): non-temporal loads, for a matrix far larger than the caches.
 hipError_t launch_colnorm(rmm_dtype_t dt, const void *A, int64_t m, int64_t d, int64_t lda,
                           int64_t batch, int64_t batch_stride, float *scores, void *ws,
                           const ColnormPlan &p, hipStream_t stream, bool causal = false,
-                          int64_t coff = 0);
+                          int64_t coff = 0, bool stream_loads = false);
 
 // ------------------------------------------------------------------ top-k
 hipError_t launch_topk(const float *scores, int64_t batch, int64_t d, int64_t k, int64_t k_pad,
