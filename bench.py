@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--m", type=int, default=None, help="token-count filter (multi-m workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the rho = 1 pass")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="one reduced product per weight instead of one per shared activation")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -71,9 +73,21 @@ def build_layer(wl, args, dev):
         key = synth.activation_key(wl, lin)
         if key not in acts:
             acts[key] = torch.from_numpy(synth.linear_activation(wl, lin)).to(dev, dt)
+        B = torch.from_numpy(synth.linear_weight(wl, lin)).to(dev, dt)
+        prev = [e for e in layer["linears"] if e["akey"] == key and e["rho"] == lin.rho]
+        if prev and not args.no_fuse:
+            # Same activation and ratio: the selection is the same, so the
+            # products are one reduced product over the weights side by side
+            # ([d][n1 + n2 ...]), as a fused q|k|v or up|gate projection.
+            e = prev[0]
+            e["B"] = torch.cat([e["B"], B], dim=1).contiguous()
+            e["n"] += lin.n
+            e["name"] = e["name"].split("@")[0] + "+" + lin.name
+            del B
+            continue
         layer["linears"].append({
             "name": lin.name, "m": lin.m, "d": lin.d, "n": lin.n, "rho": lin.rho,
-            "A": acts[key], "akey": key, "B": torch.from_numpy(synth.linear_weight(wl, lin)).to(dev, dt),
+            "A": acts[key], "akey": key, "B": B,
         })
     if wl.attention is not None and (wl.key != "llama3.1-70b-layer" or args.m in (None, 8192)):
         at = wl.attention
@@ -455,7 +469,18 @@ def _rho_desc(wl, args):
 
 
 def _products_desc(wl, args):
-    out = [f"{l.name.split('@')[0]} {l.m}x{l.d}x{l.n}" for l in _selected(wl, args)]
+    import synth
+
+    groups = []
+    for l in _selected(wl, args):
+        key = (synth.activation_key(wl, l), l.rho)
+        g = None if args.no_fuse else next((g for g in groups if g["key"] == key), None)
+        if g is None:
+            groups.append({"key": key, "names": [l.name.split("@")[0]], "m": l.m, "d": l.d, "n": l.n})
+        else:
+            g["names"].append(l.name.split("@")[0])
+            g["n"] += l.n
+    out = [f"{'|'.join(g['names'])} {g['m']}x{g['d']}x{g['n']}" for g in groups]
     if _has_attention(wl, args):
         at = wl.attention
         out.append(f"QK^T+PV L={at.L} Hq={at.Hq} Hkv={at.Hkv} dh={at.dh}")
