@@ -100,13 +100,22 @@ constexpr int kBN = 128;     // output columns per block (head_dim 128 in one ti
 constexpr int kEpiPitch = kBN + 8;
 
 // Reduced P V for one (row block, column block, head).  The 64-token tiles of
-// the head's list are streamed two ahead of the MFMA: the registers hold the
-// loads of tile q+1 and q+2 while tile q is multiplied from LDS, so each block
-// keeps two tiles of P (2 x BM x 128 B) in flight.  Dropped tokens are zeroed
+// the head's list are streamed PD ahead of the MFMA: the registers hold the
+// loads of tiles q+1 .. q+PD while tile q is multiplied from LDS, so each
+// block keeps PD tiles of P (PD x BM x 128 B) in flight.  Dropped tokens are zeroed
 // in both the P tile and the V rows (their V rows are not even loaded), and
 // on tiles that straddle the causal diagonal the entries above it are zeroed
 // per row, so the values stored there are never used.
-template <int BM, bool AVEC, bool BVEC>
+// Calls f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>) in order.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void template_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    template_for<N, I + 1>(f);
+  }
+}
+
+template <int BM, int PD, bool AVEC, bool BVEC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void pv_kernel(PvArgs g) {
   constexpr int WTM = BM / 2;                 // wave tile rows (2 x 2 waves)
   constexpr int TM = WTM / 32, TN = 2;        // 32 x 32 MFMA tiles per wave
@@ -155,9 +164,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     nk = lo;
   }
 
-  uint4 ra[2][A_CH], rb[2][KB];
-  uint64_t mk[2] = {0, 0};
-  int64_t cc[2] = {0, 0};
+  uint4 ra[PD][A_CH], rb[PD][KB];
+  uint64_t mk[PD];
+  int64_t cc[PD];
 
   // Loads of listed tile q into register slot S (no use of the data here).
   auto issue = [&](auto slot, int q) {
@@ -169,7 +178,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int row = (tid >> 3) + 32 * i;
-      ra[S][i] = mg::load_chunk<AVEC>(rp, (uint32_t)(((int64_t)row * g.ldp + c0 + akc * 8) * 2));
+#ifndef RMM_PV_POL
+#define RMM_PV_POL mg::kCached
+#endif
+      ra[S][i] = mg::load_chunk<AVEC, RMM_PV_POL>(rp, (uint32_t)(((int64_t)row * g.ldp + c0 + akc * 8) * 2));
     }
 #pragma unroll
     for (int r = 0; r < KB; ++r) {
@@ -180,9 +192,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   };
 
   // Mask register slot S and write it into LDS buffer S.
-  auto stage = [&](auto slot) {
+  auto stage = [&](auto slot, auto buf) {
     constexpr int S = decltype(slot)::value;
-    uint16_t *As = smem + S * kStage;
+    uint16_t *As = smem + decltype(buf)::value * kStage;
     uint16_t *Bs = As + BM * mg::kBK;
     const uint64_t m = mk[S];
     const int64_t c0 = cc[S];
@@ -222,9 +234,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int lrow = lane & 31, lk = lane >> 5;
-  auto mma = [&](auto slot) {
-    constexpr int S = decltype(slot)::value;
-    const uint16_t *As = smem + S * kStage;
+  auto mma = [&](auto buf) {
+    const uint16_t *As = smem + decltype(buf)::value * kStage;
     const uint16_t *Bs = As + BM * mg::kBK;
 #pragma unroll
     for (int ks = 0; ks < mg::kBK / 16; ++ks) {
@@ -245,27 +256,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
   };
 
-  // Tile q sits in LDS buffer q & 1; registers of slot (q + 1) & 1 hold tile q + 1.
-  auto step = [&](auto par, int q) {
-    constexpr int S = decltype(par)::value;
-    using Other = std::integral_constant<int, 1 - S>;
-    if (q + 2 < nk) issue(par, q + 2);
-    mma(par);
-    if (q + 1 < nk) stage(Other{});
+  // Tile q sits in LDS buffer q % 2; register slots (q + 1) % PD .. (q + PD - 1) % PD
+  // hold tiles q + 1 .. q + PD - 1 in flight, and slot q % PD is free.  The
+  // loop is unrolled by 2 PD so that every slot and buffer index is static.
+  auto step = [&](auto qm, int q) {
+    constexpr int QM = decltype(qm)::value;
+    using Free = std::integral_constant<int, QM % PD>;
+    using Next = std::integral_constant<int, (QM + 1) % PD>;
+    using Buf = std::integral_constant<int, QM % 2>;
+    using NBuf = std::integral_constant<int, (QM + 1) % 2>;
+    if (q + PD < nk) issue(Free{}, q + PD);
+    mma(Buf{});
+    if (q + 1 < nk) stage(Next{}, NBuf{});
     __syncthreads();
   };
-
-  using Zero = std::integral_constant<int, 0>;
-  using One = std::integral_constant<int, 1>;
+  template_for<PD>([&](auto p) {
+    if (decltype(p)::value < nk) issue(p, decltype(p)::value);
+  });
   if (nk > 0) {
-    issue(Zero{}, 0);
-    if (nk > 1) issue(One{}, 1);
-    stage(Zero{});
+    stage(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
     __syncthreads();
   }
-  for (int q = 0; q < nk; q += 2) {
-    step(Zero{}, q);
-    if (q + 1 < nk) step(One{}, q + 1);
+  for (int q = 0; q < nk; q += 2 * PD) {
+    template_for<2 * PD>([&](auto qm) {
+      if (q + decltype(qm)::value < nk) step(qm, q + decltype(qm)::value);
+    });
   }
 
   // Epilogue: bf16 tile through LDS (the operand buffers are free after the
@@ -332,7 +347,10 @@ hipError_t launch_pv(const void *P, int64_t ldp, int64_t p_hs, const void *V, in
 #ifndef RMM_PV_BM
 #define RMM_PV_BM 128
 #endif
-  constexpr int BM = RMM_PV_BM;
+#ifndef RMM_PV_PD
+#define RMM_PV_PD 2
+#endif
+  constexpr int BM = RMM_PV_BM, PD = RMM_PV_PD;
   PvArgs a{};
   a.P = static_cast<const uint16_t *>(P);
   a.ldp = ldp;
@@ -361,13 +379,13 @@ hipError_t launch_pv(const void *P, int64_t ldp, int64_t p_hs, const void *V, in
   const bool avec = reinterpret_cast<uintptr_t>(P) % 16 == 0 && ldp % 8 == 0 && p_hs % 8 == 0;
   const bool bvec = reinterpret_cast<uintptr_t>(V) % 16 == 0 && v_ts % 8 == 0 && v_hs % 8 == 0;
   if (avec && bvec)
-    hipLaunchKernelGGL((pv_kernel<BM, true, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pv_kernel<BM, PD, true, true>), grid, dim3(256), 0, st, a);
   else if (avec)
-    hipLaunchKernelGGL((pv_kernel<BM, true, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pv_kernel<BM, PD, true, false>), grid, dim3(256), 0, st, a);
   else if (bvec)
-    hipLaunchKernelGGL((pv_kernel<BM, false, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pv_kernel<BM, PD, false, true>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((pv_kernel<BM, false, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pv_kernel<BM, PD, false, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
