@@ -7,17 +7,16 @@
 // slots) into the workspace, the same way A_I is packed.  The weights
 // themselves are only read.  Both operand tiles then come straight from
 // memory into LDS with `buffer_load_dwordx4 ... lds` (no staging registers,
-// no in-loop transposes), which leaves the register file to the 256
-// accumulators of a 128 x 128 wave tile and to double-buffered MFMA
-// fragments.
+// no in-loop transposes), which leaves the register file to the accumulators
+// and to double-buffered MFMA fragments.
 //
-// Block tile 256 x 256 x 64, 4 waves of 128 x 128, two LDS stages (128 KiB).
-// LDS rows hold 64 bf16 with the 16-byte chunk index XOR-swizzled by the row;
-// since one direct load writes 64 consecutive 16-byte LDS chunks, each lane
-// fetches the global chunk that the swizzle maps onto its LDS slot.  The
-// MFMA takes the B fragment as its first operand so each lane ends up with
-// four consecutive output columns of one row, which the epilogue stages in
-// LDS and writes back as 16-byte row segments.
+// Block tile 256 x 256 x 64, eight waves of 128 x 64 (two per SIMD), two LDS
+// stages (128 KiB).  LDS rows hold 64 bf16 with the 16-byte chunk index
+// XOR-swizzled by the row; since one direct load writes 64 consecutive
+// 16-byte LDS chunks, each lane fetches the global chunk that the swizzle maps
+// onto its LDS slot.  The MFMA takes the B fragment as its first operand so
+// each lane ends up with four consecutive output columns of one row, which the
+// epilogue writes straight from registers with 8-byte buffer stores.
 #include "mfma_gemm.h"
 #include "rmm_internal.h"
 #include "timing.h"
@@ -32,24 +31,6 @@ using mg::f32x16_t;
 using mg::rsrc_t;
 
 constexpr int kBK = 64;   // slot granularity of the packed operands
-
-// Shape of the GEMM below: block tile, K-tile depth, LDS stages, waves per SIMD.
-#ifndef RMM_NT_BK
-#define RMM_NT_BM 256
-#define RMM_NT_BN 256
-#define RMM_NT_BK 64
-#define RMM_NT_NST 2
-#define RMM_NT_WPE 1
-#endif
-#ifndef RMM_NT_PERSIST
-#define RMM_NT_PERSIST 1
-#endif
-#ifndef RMM_NT_PIN
-#define RMM_NT_PIN 1
-#endif
-#ifndef RMM_NT_IGLP
-#define RMM_NT_IGLP 1   // scheduling hint for the MFMA / LDS-read interleave (-1: none)
-#endif
 
 // ---------------------------------------------------------------- B_I^T pack
 // grid: x = 256-wide column block of B, y = 64-wide block of kept slots.
@@ -108,15 +89,9 @@ struct NtArgs {
   int64_t ldy, m, n, k_pad, tiles_m, tiles_n;
 };
 
-// LDS operand tiles are [256 rows][BK] bf16: CH = BK/8 16-byte chunks per
-// row, the chunk index XOR-swizzled by the row so that the 32 consecutive
+// LDS operand tiles are [256 rows][64] bf16: 8 16-byte chunks per row, the
+// chunk index XOR-swizzled by (row ^ row/8) & 7 so that the 32 consecutive
 // rows an MFMA fragment read touches spread over the banks.
-template <int BK>
-__device__ __forceinline__ int lswz(int row, int c) {
-  constexpr int CH = BK / 8;
-  const int f = CH == 8 ? ((row ^ (row >> 3)) & 7) : ((row >> 2) & (CH - 1));
-  return row * BK + ((c ^ f) << 3);
-}
 
 // 16 bytes per lane from the buffer straight into LDS: the wave's 64 lanes
 // fill the 1 KiB at `lds` in lane order.  (A plain function, so that the
@@ -125,255 +100,70 @@ __device__ __forceinline__ void lds_load16(rsrc_t r, unsigned char *lds, uint32_
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void *)lds, 16, voff, soff, 0, 0);
 }
 
-// s_waitcnt vmcnt(n) for the counts the pipelines below use (lgkmcnt and
-// expcnt untouched); encoding: vmcnt[3:0] | vmcnt[5:4] << 14.
+// Immediate of s_waitcnt vmcnt(n) with lgkmcnt and expcnt left alone:
+// vmcnt[3:0] | vmcnt[5:4] << 14.
 constexpr int vm_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-#define RMM_VM(N) \
-  case N: __builtin_amdgcn_s_waitcnt(vm_imm(N)); break;
-#define RMM_VM8(B) RMM_VM(B) RMM_VM(B + 1) RMM_VM(B + 2) RMM_VM(B + 3) RMM_VM(B + 4) RMM_VM(B + 5) RMM_VM(B + 6) RMM_VM(B + 7)
-    RMM_VM8(0) RMM_VM8(8) RMM_VM8(16) RMM_VM8(24) RMM_VM8(32) RMM_VM8(40) RMM_VM8(48) RMM_VM8(56)
-#undef RMM_VM8
-#undef RMM_VM
-    default: __builtin_amdgcn_s_waitcnt(vm_imm(0)); break;
-  }
-}
 
-// BM x BN block tile of 4 waves (2 x 2), BK-deep K tiles, NST LDS stages;
-// WPE: waves per SIMD the register budget must allow.
-template <int BM, int BN, int BK, int NST, int WPE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void gemm_nt_kernel(NtArgs g) {
-  constexpr int WTM = BM / 2, WTN = BN / 2;        // wave tile
-  constexpr int TI = WTM / 32, TJ = WTN / 32;      // MFMA tiles per wave (m, n)
-  constexpr int CH = BK / 8;                       // chunks per LDS row
-  constexpr int TILE_A = BM * BK * 2, STAGE = (BM + BN) * BK * 2;
-  constexpr int LPA = BM * CH / 64 / 4;            // direct loads per wave, A tile
-  constexpr int LPB = BN * CH / 64 / 4;            // direct loads per wave, B tile
-  constexpr int LPT = LPA + LPB;                   // per K tile
-  constexpr int LPM = LPA > LPB ? LPA : LPB;
-  constexpr int RPI = 64 / CH;                     // rows covered by one wave load
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * STAGE];
-  static_assert(NST * STAGE >= 4 * WTM * WTN * 2, "epilogue staging must fit");
-  static_assert(LPT * NST <= 63, "vmcnt range");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  int64_t tm, tn;
-  mg::tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
-  const int64_t m0 = tm * BM, n0 = tn * BN;
-  const int64_t rows = g.m - m0 < BM ? g.m - m0 : BM;
-  const int64_t cols = g.n - n0 < BN ? g.n - n0 : BN;
-  const rsrc_t ra = mg::make_rsrc(g.A + m0 * g.k_pad, (uint64_t)rows * g.k_pad * 2);
-  const rsrc_t rb = mg::make_rsrc(g.BT + n0 * g.k_pad, (uint64_t)cols * g.k_pad * 2);
-
-  // Direct load i of this wave writes the 1 KiB LDS block q = 4 i + wave:
-  // rows q*RPI + lane/CH, slot lane%CH.  The swizzle is an XOR, so slot s of
-  // a row holds logical chunk s ^ f(row): that is the chunk the lane fetches.
-  uint32_t voff[LPM];
-#pragma unroll
-  for (int i = 0; i < LPM; ++i) {
-    const int row = (4 * i + wave) * RPI + lane / CH;
-    const int slot = lane % CH;
-    const int logical = (lswz<BK>(row, slot) - row * BK) >> 3;
-    voff[i] = (uint32_t)(((int64_t)row * g.k_pad + logical * 8) * 2);
-  }
-  auto issue = [&](int kt, int stage) {
-    unsigned char *sa = smem + stage * STAGE;
-    unsigned char *sb = sa + TILE_A;
-    const uint32_t koff = (uint32_t)kt * (BK * 2);
-#pragma unroll
-    for (int i = 0; i < LPM; ++i) {
-      if (i < LPA) lds_load16(ra, sa + (4 * i + wave) * 1024, voff[i] + koff);
-      if (i < LPB) lds_load16(rb, sb + (4 * i + wave) * 1024, voff[i] + koff);
-    }
-  };
-
-  f32x16_t acc[TJ][TI];   // [n tile j][m tile i]: D = B_frag x A_frag^T
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
-
-  const int nk = (int)(g.k_pad / BK);
-  const int lrow = lane & 31, lk = lane >> 5;
-  bf16x8_t av[2][TI], bv[2][TJ];
-  auto frags = [&](int kt, int ks, int slot) {
-    const uint16_t *As = reinterpret_cast<const uint16_t *>(smem + (kt % NST) * STAGE);
-    const uint16_t *Bs = As + BM * BK;
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-      av[slot][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
-                                                     &As[lswz<BK>(wm * WTM + i * 32 + lrow, ks * 2 + lk)]));
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-      bv[slot][j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
-                                                     &Bs[lswz<BK>(wn * WTN + j * 32 + lrow, ks * 2 + lk)]));
-  };
-  auto mfmas = [&](int slot) {
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[slot][j], av[slot][i], acc[j][i], 0, 0, 0);
-  };
-  // NST stages hold tiles kt .. kt+NST-1.  The barrier sits ahead of each
-  // tile's last K-slice: once every wave holds tile kt's last fragments in
-  // registers, tile kt+NST may overwrite its stage, and the first fragments of
-  // tile kt+1 are read while the last MFMAs of tile kt run.  Each tile thus
-  // has NST-1 K-steps to arrive.
-  constexpr int KS = BK / 16;
-#pragma unroll
-  for (int p = 0; p < NST; ++p)
-    if (p < nk) issue(p, p);
-  {
-    const int c0 = (NST - 1) < (nk - 1) ? (NST - 1) : (nk - 1);
-    wait_vm((c0 > 0 ? c0 : 0) * LPT);
-  }
-  __syncthreads();
-  if (nk > 0) frags(0, 0, 0);
-  // One K-step; ISSUE is a compile-time flag so that the steady-state loop
-  // is a single basic block the scheduler can order as written.
-  auto step = [&](int kt, auto issue_flag) {
-    constexpr bool ISSUE = decltype(issue_flag)::value;
-#if RMM_NT_IGLP >= 0
-    __builtin_amdgcn_iglp_opt(RMM_NT_IGLP);
-#endif
-#pragma unroll
-    for (int ks = 0; ks < KS - 1; ++ks) {
-      frags(kt, ks + 1, (ks + 1) & 1);
-      mfmas(ks & 1);
-    }
-    // Tile kt+1 must have landed: tiles kt+2 .. min(kt+NST-1, nk-1) may still be in flight.
-    if constexpr (ISSUE) {
-      wait_vm((NST - 2) * LPT);
-    } else {
-      const int c = nk - 2 - kt < NST - 2 ? nk - 2 - kt : NST - 2;
-      wait_vm((c > 0 ? c : 0) * LPT);
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): tile kt's fragment reads are done
-    __syncthreads();
-    if constexpr (ISSUE) {
-      issue(kt + NST, kt % NST);
-#if RMM_NT_PIN
-      // Keep the loads ahead of this slice's MFMAs: the scheduler would
-      // otherwise sink them below, cutting the time they have to arrive.
-      __builtin_amdgcn_sched_barrier(0);
-#endif
-      frags(kt + 1, 0, 0);
-    } else {
-      if (kt + 1 < nk) frags(kt + 1, 0, 0);
-    }
-    mfmas((KS - 1) & 1);
-  };
-  int kt = 0;
-  for (; kt + NST < nk; ++kt) step(kt, std::true_type{});
-  for (; kt < nk; ++kt) step(kt, std::false_type{});
-  __syncthreads();   // all fragment reads done before the staging area is reused
-
-  // Epilogue.  acc[j][i] register r of lane l holds Y[row, col] with
-  // row = i*32 + l%32 and col = j*32 + 8*(r/4) + 4*(l/32) + r%4: four
-  // consecutive columns per (r/4).  Stage the wave's WTM x WTN bf16 tile in
-  // LDS ([row][WTN], 16-byte chunks XOR-swizzled by row) and write it back
-  // as 16-byte row segments.
-  constexpr int CHN = WTN / 8;                      // 16-byte chunks per staged row
-  uint16_t *stage = reinterpret_cast<uint16_t *>(smem) + wave * (WTM * WTN);
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int row = i * 32 + lrow;
-        const int col = j * 32 + 8 * gq + 4 * lk;
-        const uint32_t lo = pack_bf16x2(acc[j][i][4 * gq + 0], acc[j][i][4 * gq + 1]);
-        const uint32_t hi = pack_bf16x2(acc[j][i][4 * gq + 2], acc[j][i][4 * gq + 3]);
-        const int chunk = (col >> 3) ^ (row & (CHN - 1));
-        *reinterpret_cast<uint2 *>(&stage[row * WTN + chunk * 8 + (col & 7)]) = make_uint2(lo, hi);
-        // convert and park one 4-column group at a time (keeps the VGPR
-        // pressure of the epilogue low)
-        __builtin_amdgcn_sched_barrier(0);
-      }
-  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-  __builtin_amdgcn_wave_barrier();
-  const int64_t rbase = m0 + wm * WTM, cbase = n0 + wn * WTN;
-  const bool vec = (g.ldy % 8 == 0) && (reinterpret_cast<uintptr_t>(g.Y) % 16 == 0) && cbase + WTN <= g.n;
-  constexpr int RPS = 64 / CHN;                     // rows per store instruction
-#pragma unroll 4
-  for (int it = 0; it < WTM / RPS; ++it) {
-    const int row = it * RPS + lane / CHN;
-    const int ch = lane % CHN;
-    const uint4 v = *reinterpret_cast<const uint4 *>(&stage[row * WTN + ((ch ^ (row & (CHN - 1))) * 8)]);
-    const int64_t gr = rbase + row;
-    if (gr >= g.m) continue;
-    uint16_t *dst = g.Y + gr * g.ldy + cbase + ch * 8;
-    if (vec) {
-      *reinterpret_cast<uint4 *>(dst) = v;
-    } else {
-      const uint16_t e[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
-                             (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (cbase + ch * 8 + q < g.n) dst[q] = e[q];
-    }
-  }
-}
-
-// Persistent form of the kernel above for 256 x 256 x 64 tiles and two LDS
-// stages: one workgroup per CU walks its XCD's tile range.  After the last
-// K-step's barrier (every wave is done reading LDS) it issues the first two
-// K-tiles of its next output tile, and only then converts and stores the
-// finished accumulators straight from registers, so the next tile's loads fly
-// while the epilogue runs and the pipeline never drains between tiles.  The
-// stores come after those loads in issue order, so waiting for the loads does
-// not wait for them.
+// 256 x 256 x 64 tiles, two LDS stages, persistent: one workgroup per CU
+// walks its XCD's tile range.  After the last K-step's barrier (every wave is
+// done reading LDS) it issues the first two K-tiles of its next output tile,
+// and only then converts and stores the finished accumulators straight from
+// registers, so the next tile's loads fly while the epilogue runs and the
+// pipeline never drains between tiles.  The stores come after those loads in
+// issue order, so waiting for the loads does not wait for them.
 //
-// Register budget: the 256 accumulators fill the AGPRs, so the VGPRs must
-// hold only fragments and a few addresses.  The LDS fragment addresses are
-// built by hand: with the XOR swizzle, the byte offset of fragment (i, ks) of
-// a lane is rowbase + 4096 i + 16 (e ^ c) with e a per-lane constant and
-// c = 2 ks ^ 4 (i & 1) one of four compile-time values; the K loop is unrolled
-// by the stage count so the stage offset is compile-time too.  Eight base
-// registers thus address every fragment read through ds_read's immediate
-// offset, and they are passed through an empty asm each step so the compiler
+// Register budget: the accumulators take half the register file, so the rest
+// must hold only fragments and a few addresses.  The LDS fragment addresses
+// are built by hand: with the XOR swizzle, the byte offset of fragment (i, ks)
+// of a lane is rowbase + 4096 i + 16 (e ^ c), with e a per-lane constant and
+// c = 2 ks ^ 4 (i & 1) one of four compile-time values, plus the stage offset.
+// Eight base registers thus address every fragment read through ds_read's
+// immediate offset; they pass through an empty asm each step so the compiler
 // cannot hoist one register per (fragment, stage) out of the loop.
-__global__ __launch_bounds__(256) void gemm_nt_persistent(NtArgs g) {
+//
+// WGN: waves across the tile's columns (2: four waves of 128 x 128, one per
+// SIMD; 4: eight waves of 128 x 64, two per SIMD, so that one wave's MFMAs
+// run while the other waits on LDS or on the barrier: about 10 % faster).
+template <int WGN>
+__global__ __launch_bounds__(128 * WGN) __attribute__((amdgpu_waves_per_eu(WGN / 2))) void gemm_nt_persistent(
+    NtArgs g) {
   constexpr int BM = 256, BN = 256, BK = 64, NST = 2;
-  constexpr int TI = 4, TJ = 4;
+  constexpr int NWAVE = 2 * WGN;
+  constexpr int WTN = BN / WGN;                      // wave tile columns (rows: 128)
+  constexpr int TI = 4, TJ = WTN / 32;
   constexpr int TILE = 256 * BK * 2;                 // one operand tile, 32 KiB
-  constexpr int LPW = 8;                             // direct loads per wave per operand
+  constexpr int LPW = 32 / NWAVE;                    // direct loads per wave per operand
   constexpr int KS = BK / 16;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * NST * TILE];   // [A0 | A1 | B0 | B1]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int lrow = lane & 31, lk = lane >> 5;
   const int64_t total = g.tiles_m * g.tiles_n;
   const int nk = (int)(g.k_pad / BK);
 
-  // Direct load i of this wave writes the 1 KiB LDS block q = 4 i + wave:
+  // Direct load i of this wave writes the 1 KiB LDS block q = NWAVE i + wave:
   // rows 8 q + lane/8, slot lane%8, holding logical chunk slot ^ f(row) with
-  // f(row) = (row ^ row/8) & 7 = (lane/8) ^ ((4 i + wave) & 7).  The lane part
-  // of the byte offset depends on i only through i & 1; the rest (32 i rows
-  // and the K offset) is uniform and goes in the scalar offset.
+  // f(row) = (row ^ row/8) & 7 = (lane/8) ^ ((NWAVE i + wave) & 7).  The lane
+  // part of the byte offset depends on i at most through i & 1; the rest
+  // (8 NWAVE i rows and the K offset) is uniform and goes in the scalar offset.
   uint32_t vbase[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const int logical = (lane & 7) ^ (lane >> 3) ^ ((wave + 4 * p) & 7);
+    const int logical = (lane & 7) ^ (lane >> 3) ^ ((wave + NWAVE * p) & 7);
     vbase[p] = (uint32_t)((((int64_t)wave * 8 + (lane >> 3)) * g.k_pad + logical * 8) * 2);
   }
-  const uint32_t srow = (uint32_t)(32 * g.k_pad * 2);   // bytes of 32 rows
+  const uint32_t srow = (uint32_t)(8 * NWAVE * g.k_pad * 2);   // bytes of 8 NWAVE rows
 
-  // Fragment read bases (see above): row lrow of the wave's 128-row slab,
-  // chunk e ^ c for c = 0, 2, 4, 6.
+  // Fragment read bases (see above): row lrow of the wave's row slab, chunk
+  // e ^ c for c = 0, 2, 4, 6.
   const int e = lk ^ (lrow & 7) ^ (lrow >> 3);
   uint32_t fa[4], fb[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const uint32_t off = (uint32_t)(lrow * 128 + ((e ^ (2 * c)) << 4));
     fa[c] = off + (uint32_t)(wm * 128 * 128);
-    fb[c] = off + (uint32_t)(NST * TILE + wn * 128 * 128);
+    fb[c] = off + (uint32_t)(NST * TILE + wn * WTN * 128);
   }
 
   struct Ctx {
@@ -398,8 +188,8 @@ __global__ __launch_bounds__(256) void gemm_nt_persistent(NtArgs g) {
     const uint32_t koff = (uint32_t)kt * (BK * 2);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      lds_load16(c.ra, sa + (4 * i + wave) * 1024, vbase[i & 1], i * srow + koff);
-      lds_load16(c.rb, sb + (4 * i + wave) * 1024, vbase[i & 1], i * srow + koff);
+      lds_load16(c.ra, sa + (NWAVE * i + wave) * 1024, vbase[i & 1], i * srow + koff);
+      lds_load16(c.rb, sb + (NWAVE * i + wave) * 1024, vbase[i & 1], i * srow + koff);
     }
   };
   auto prologue = [&](const Ctx &c) __attribute__((always_inline)) {
@@ -511,8 +301,8 @@ __global__ __launch_bounds__(256) void gemm_nt_persistent(NtArgs g) {
     // buffer stores: one lane offset, the column step in the immediate and
     // the 32-row step in the scalar offset; rows past m fall outside the
     // resource and are dropped.
-    const int64_t rbase = dm0 + wm * 128, cbase = dn0 + wn * 128;
-    const bool vec = (g.ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(g.Y) % 8 == 0) && cbase + 128 <= g.n;
+    const int64_t rbase = dm0 + wm * 128, cbase = dn0 + wn * WTN;
+    const bool vec = (g.ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(g.Y) % 8 == 0) && cbase + WTN <= g.n;
     // Opaque copies of the lane's row and half: keeps the per-store address
     // arithmetic below inside the loop (folded into immediate offsets)
     // instead of 64 hoisted registers.
@@ -523,7 +313,7 @@ __global__ __launch_bounds__(256) void gemm_nt_persistent(NtArgs g) {
       const int64_t rows_left = g.m - rbase;
       if (rows_left > 0) {
         const rsrc_t ry = mg::make_rsrc(g.Y + rbase * g.ldy + cbase,
-                                        (uint64_t)((rows_left < 128 ? rows_left : 128) - 1) * g.ldy * 2 + 256);
+                                        (uint64_t)((rows_left < 128 ? rows_left : 128) - 1) * g.ldy * 2 + WTN * 2);
         const uint32_t vo = (uint32_t)((er * g.ldy + 4 * ek) * 2);
         const uint32_t s32 = (uint32_t)(32 * g.ldy * 2);
 #pragma unroll
@@ -569,10 +359,8 @@ __global__ __launch_bounds__(256) void gemm_nt_persistent(NtArgs g) {
   }
 }
 
-// Explicit instantiation of the configuration launched below.
-#if !RMM_NT_PERSIST
-template __global__ void gemm_nt_kernel<RMM_NT_BM, RMM_NT_BN, RMM_NT_BK, RMM_NT_NST, RMM_NT_WPE>(NtArgs);
-#endif
+
+constexpr int kWGN = 4;
 
 }  // namespace
 
@@ -607,19 +395,14 @@ hipError_t launch_gemm_nt(const void *A_packed, const int32_t *idx_clean, const 
   g.m = m;
   g.n = n;
   g.k_pad = k_pad;
-  g.tiles_m = ceil_div(m, RMM_NT_BM);
-  g.tiles_n = ceil_div(n, RMM_NT_BN);
+  g.tiles_m = ceil_div(m, 256);
+  g.tiles_n = ceil_div(n, 256);
   KernelTimer timer("gemm_nt", st);
-#if RMM_NT_PERSIST
   {
     const int64_t tiles = g.tiles_m * g.tiles_n;
     const int64_t grid = tiles < 256 ? tiles : 256;
-    hipLaunchKernelGGL(gemm_nt_persistent, dim3((unsigned)grid), dim3(256), 0, st, g);
+    hipLaunchKernelGGL(gemm_nt_persistent<kWGN>, dim3((unsigned)grid), dim3(128 * kWGN), 0, st, g);
   }
-#else
-  hipLaunchKernelGGL((gemm_nt_kernel<RMM_NT_BM, RMM_NT_BN, RMM_NT_BK, RMM_NT_NST, RMM_NT_WPE>), dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(256),
-                     0, st, g);
-#endif
   return hipGetLastError();
 }
 
