@@ -55,6 +55,10 @@ struct Carve {
   }
 };
 
+// Read-once matrices above this size go through non-temporal loads (the
+// MI355X memory-side cache holds 256 MB).
+constexpr double kStreamBytes = 192.0 * 1024 * 1024;
+
 rmm::ColnormPlan plan_for(rmm_dtype_t dt, const void *A, int64_t m, int64_t d, int64_t lda,
                           int64_t batch, int64_t bs, bool causal = false) {
   const int64_t v = 16 / (int64_t)esize(dt);
@@ -150,8 +154,12 @@ RMM_API rmm_status_t rmm_colnorm(rmm_dtype_t dt, const void *A, int64_t m, int64
   const rmm::ColnormPlan p = plan_for(dt, A, m, d, lda, batch, bs);
   const size_t need = rmm::colnorm_ws_bytes(p, d, batch);
   if (need > ws_bytes || (need && !ws)) return fail(RMM_ERR_WORKSPACE, "colnorm: workspace needs %zu bytes", need);
+  // A matrix larger than the memory-side cache is streamed with
+  // non-temporal loads (faster); a smaller one is read through the caches so
+  // that the gather of its kept columns that follows can hit them.
+  const bool big = (double)m * (double)d * (double)esize(dt) * (double)batch > kStreamBytes;
   return hip_status(rmm::launch_colnorm(dt, A, m, d, lda, batch, batch > 1 ? bs : 0, scores, ws, p,
-                                        (hipStream_t)stream),
+                                        (hipStream_t)stream, false, 0, big),
                     "colnorm launch");
 }
 
