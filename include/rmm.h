@@ -200,6 +200,43 @@ rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, int64_t p
                     rmm_stream_t stream);
 
 /*
+ * rmm_attention - fused reduced attention of one layer (bf16 in and out):
+ * the feature-reduced Q K^T, the softmax and the token-reduced P V without
+ * writing the score or probability matrices.  Source: "Alcance de
+ * Aplicación" (reduce the feature dimension of Q K^T and the token dimension
+ * of P V) with "Estrategia de Selección" (scores are column norms).  For query
+ * head h with kv head g = floor(h*Hkv/Hq):
+ *   I_h = top-k_feat features of Q_h by column norm (as rmm_qk),
+ *   S_h = Q_h[:, I_h] Kt_g[I_h, :],
+ *   P_h = softmax of S_h / sqrt(dh) over each row, causal: key u is visible
+ *         from query t when u <= t + (Lk - Lq); others are exact zeros,
+ *   J_h = top-k_tok tokens by column norm of P_h (as rmm_pv, the scores taken
+ *         from float32 probabilities),
+ *   O_h = P_h[:, J_h] V_g[J_h, :]   (P rounded to bf16 as the MFMA operand,
+ *         float32 accumulation, bf16 output).
+ *   Q, Kt, V, O: layouts as in rmm_qk and rmm_pv.  dh must be 128 and
+ *   1 <= k_feat <= 128, 1 <= k_tok <= Lk (RMM_ERR_UNSUPPORTED for other dh);
+ *   causal != 0 needs Lq <= Lk (every query sees its diagonal key).
+ *   idx_feat (device, int32) [Hq][rmm_k_pad(k_feat)], idx_tok [Hq][rmm_k_pad(k_tok)]:
+ *   the selections, written as by rmm_topk.
+ *   tok_scores (device, float, optional) [Hq][Lk]: the token scores; NULL keeps
+ *   them in the workspace.
+ * S and P are recomputed tile by tile in three passes (row max and sum,
+ * column sums of squares, output over the kept tokens); the workspace holds
+ * the packed Q[:, I], K[:, I] and the kept keys and values
+ * (rmm_attention_workspace_bytes).
+ */
+size_t rmm_attention_workspace_bytes(int64_t Lq, int64_t Lk, int64_t Hq, int64_t dh, int64_t k_feat,
+                                     int64_t k_tok);
+rmm_status_t rmm_attention(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, int64_t q_tok_stride,
+                           int64_t q_head_stride, const void *Kt, int64_t Lk, int64_t Hkv,
+                           int64_t kt_head_stride, int64_t ldkt, const void *V, int64_t v_tok_stride,
+                           int64_t v_head_stride, int64_t k_feat, int64_t k_tok, int causal, void *O,
+                           int64_t o_tok_stride, int64_t o_head_stride, int32_t *idx_feat,
+                           int32_t *idx_tok, float *tok_scores, void *ws, size_t ws_bytes,
+                           rmm_stream_t stream);
+
+/*
  * Per-kernel timing diagnostics (not part of the method; for measurement).
  * When enabled, each kernel the library enqueues is bracketed by two HIP
  * events recorded on its launch stream and filed under "<tag>/<kernel>"

@@ -16,9 +16,9 @@ import torch
 __all__ = [
     "RMMError", "load", "lib_path",
     "rmm_version", "rmm_k_from_rho", "rmm_k_pad",
-    "rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_qk", "rmm_pv",
+    "rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_qk", "rmm_pv", "rmm_attention",
     "rmm_colnorm_workspace_bytes", "rmm_topk_workspace_bytes", "rmm_gemm_workspace_bytes",
-    "rmm_qk_workspace_bytes", "rmm_pv_workspace_bytes",
+    "rmm_qk_workspace_bytes", "rmm_pv_workspace_bytes", "rmm_attention_workspace_bytes",
     "rmm_linear", "timing",
 ]
 
@@ -64,6 +64,10 @@ _PROTOS = {
     "rmm_timing_reset": (ctypes.c_int, []),
     "rmm_pv": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
                               ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "rmm_attention_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
+    "rmm_attention": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _vp,
+                                     _i64, _i64, _i64, _i64, ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _vp,
+                                     _vp, _sz, _vp]),
 }
 
 
@@ -279,6 +283,41 @@ def rmm_pv(P: torch.Tensor, V: torch.Tensor, k: int, O: torch.Tensor | None = No
                       _ptr(ws), wsb,
                       _stream(dev)))
     return O, idx
+
+
+def rmm_attention_workspace_bytes(Lq: int, Lk: int, Hq: int, dh: int, k_feat: int, k_tok: int) -> int:
+    return int(load().rmm_attention_workspace_bytes(Lq, Lk, Hq, dh, k_feat, k_tok))
+
+
+def rmm_attention(Q: torch.Tensor, Kt: torch.Tensor, V: torch.Tensor, k_feat: int, k_tok: int,
+                  O: torch.Tensor | None = None, idx_feat: torch.Tensor | None = None,
+                  idx_tok: torch.Tensor | None = None, tok_scores: torch.Tensor | None = None,
+                  ws: torch.Tensor | None = None, causal: bool = True):
+    """Fused reduced attention.  Q [Lq, Hq, dh], Kt [Hkv, dh, Lk], V [Lk, Hkv, dh] (bf16)
+    -> (O bf16 [Lq, Hq, dh], idx_feat int32 [Hq, k_pad(k_feat)], idx_tok int32 [Hq, k_pad(k_tok)]).
+    tok_scores (optional float32 [Hq, Lk]) receives the token scores."""
+    lib = load()
+    dev = _dev(Q, Kt, V)
+    if Q.dtype != torch.bfloat16 or Kt.dtype != torch.bfloat16 or V.dtype != torch.bfloat16:
+        raise TypeError("rmm_attention takes bfloat16 Q, Kt and V")
+    if Q.dim() != 3 or Kt.dim() != 3 or V.dim() != 3 or Q.stride(2) != 1 or Kt.stride(2) != 1 or V.stride(2) != 1:
+        raise ValueError("Q [Lq, Hq, dh], Kt [Hkv, dh, Lk], V [Lk, Hkv, dh] need unit innermost stride")
+    Lq, Hq, dh = Q.shape
+    Hkv, dh2, Lk = Kt.shape
+    if dh2 != dh or V.shape[0] != Lk or V.shape[1] != Hkv or V.shape[2] != dh:
+        raise ValueError("shapes of Q, Kt and V disagree")
+    if O is None:
+        O = torch.empty((Lq, Hq, dh), dtype=torch.bfloat16, device=dev)
+    if idx_feat is None:
+        idx_feat = torch.empty((Hq, rmm_k_pad(k_feat)), dtype=torch.int32, device=dev)
+    if idx_tok is None:
+        idx_tok = torch.empty((Hq, rmm_k_pad(k_tok)), dtype=torch.int32, device=dev)
+    ws, wsb = _ws(int(lib.rmm_attention_workspace_bytes(Lq, Lk, Hq, dh, int(k_feat), int(k_tok))), dev, ws)
+    _check(lib.rmm_attention(_ptr(Q), Lq, Hq, dh, Q.stride(0), Q.stride(1), _ptr(Kt), Lk, Hkv, Kt.stride(0),
+                             Kt.stride(1), _ptr(V), V.stride(0), V.stride(1), int(k_feat), int(k_tok),
+                             1 if causal else 0, _ptr(O), O.stride(0), O.stride(1), _ptr(idx_feat),
+                             _ptr(idx_tok), _ptr(tok_scores), _ptr(ws), wsb, _stream(dev)))
+    return O, idx_feat, idx_tok
 
 
 def rmm_linear(A: torch.Tensor, B: torch.Tensor, rho: float):

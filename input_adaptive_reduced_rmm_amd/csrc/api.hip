@@ -7,7 +7,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include "mfma_gemm.h"
 #include "rmm_internal.h"
+#include "timing.h"
 
 #define RMM_API extern "C" __attribute__((visibility("default")))
 
@@ -350,4 +352,125 @@ RMM_API rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, i
   he = rmm::launch_pv(P, ldp, p_head_stride, V, v_tok_stride, v_head_stride, O, o_tok_stride, o_head_stride,
                       idx, k_pad, k, Hq, Hkv, Lq, Lk, dh, causal != 0, w + o_plan, st);
   return hip_status(he, "pv gemm launch");
+}
+
+// ------------------------------------------------------------------ fused attention
+struct AttnLayout {
+  size_t sc, part, qi, idxf, ki, stats, tok, kj, vjt, total;
+};
+static AttnLayout attn_layout(int64_t Lq, int64_t Lk, int64_t Hq, int64_t dh, int64_t kf, int64_t kt) {
+  const size_t kfp = (size_t)rmm_k_pad(kf), ktp = (size_t)rmm_k_pad(kt);
+  AttnLayout L;
+  Carve c(nullptr);
+  L.sc = c.off;   c.take((size_t)Hq * dh * 4);
+  L.part = c.off; c.take(colnorm_ws(RMM_BF16, Lq, dh, Hq));
+  L.qi = c.off;   c.take((size_t)Hq * Lq * kfp * 2);
+  L.idxf = c.off; c.take((size_t)Hq * kfp * 4);
+  L.ki = c.off;   c.take((size_t)Hq * Lk * kfp * 2);
+  L.stats = c.off; c.take((size_t)4 * Hq * Lq * 4);
+  L.tok = c.off;  c.take((size_t)Hq * Lk * 4);
+  L.kj = c.off;   c.take((size_t)Hq * ktp * kfp * 2);
+  L.vjt = c.off;  c.take((size_t)Hq * dh * ktp * 2);
+  L.total = c.off;
+  return L;
+}
+
+RMM_API size_t rmm_attention_workspace_bytes(int64_t Lq, int64_t Lk, int64_t Hq, int64_t dh, int64_t k_feat,
+                                             int64_t k_tok) {
+  if (Lq < 1 || Lk < 1 || Hq < 1 || dh < 1 || k_feat < 1 || k_tok < 1) return 0;
+  return attn_layout(Lq, Lk, Hq, dh, k_feat, k_tok).total;
+}
+
+RMM_API rmm_status_t rmm_attention(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, int64_t q_tok_stride,
+                                   int64_t q_head_stride, const void *Kt, int64_t Lk, int64_t Hkv,
+                                   int64_t kt_head_stride, int64_t ldkt, const void *V, int64_t v_tok_stride,
+                                   int64_t v_head_stride, int64_t k_feat, int64_t k_tok, int causal, void *O,
+                                   int64_t o_tok_stride, int64_t o_head_stride, int32_t *idx_feat,
+                                   int32_t *idx_tok, float *tok_scores, void *ws, size_t ws_bytes,
+                                   rmm_stream_t stream) {
+  if (!Q || !Kt || !V || !O || !idx_feat || !idx_tok) return fail(RMM_ERR_INVALID_ARG, "attention: NULL pointer");
+  if (Lq < 1 || Lk < 1 || dh < 1 || Lk >= kMaxDim || Lq >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "attention: bad Lq, Lk or dh");
+  if (Hq < 1 || Hq > kMaxBatch || Hkv < 1 || Hkv > Hq || Hq % Hkv != 0)
+    return fail(RMM_ERR_INVALID_ARG, "attention: need 1 <= Hkv <= Hq <= 65535 and Hq %% Hkv == 0");
+  if (k_feat < 1 || k_feat > dh) return fail(RMM_ERR_INVALID_ARG, "attention: need 1 <= k_feat <= dh");
+  if (k_tok < 1 || k_tok > Lk) return fail(RMM_ERR_INVALID_ARG, "attention: need 1 <= k_tok <= Lk");
+  if (causal && Lq > Lk) return fail(RMM_ERR_INVALID_ARG, "attention: causal needs Lq <= Lk");
+  if (q_tok_stride < dh || ldkt < Lk || v_tok_stride < dh || o_tok_stride < dh || q_head_stride < 0 ||
+      kt_head_stride < 0 || v_head_stride < 0 || o_head_stride < 0)
+    return fail(RMM_ERR_INVALID_ARG, "attention: bad stride");
+  if (!aligned(Q, 2) || !aligned(Kt, 2) || !aligned(V, 2) || !aligned(O, 2) || !aligned(idx_feat, 4) ||
+      !aligned(idx_tok, 4) || (tok_scores && !aligned(tok_scores, 4)))
+    return fail(RMM_ERR_INVALID_ARG, "attention: misaligned pointer");
+  const int64_t kfp = rmm_k_pad(k_feat), ktp = rmm_k_pad(k_tok);
+  if (!rmm::attn_supported(dh, kfp)) return fail(RMM_ERR_UNSUPPORTED, "attention: needs dh == 128");
+  if ((uint64_t)((dh - 1) * ldkt + Lk) * 2 >= rmm::mg::kMaxRecords ||
+      (uint64_t)((Lk - 1) * v_tok_stride + dh) * 2 >= rmm::mg::kMaxRecords ||
+      (uint64_t)Lk * kfp * 2 >= rmm::mg::kMaxRecords)
+    return fail(RMM_ERR_UNSUPPORTED, "attention: a key or value head spans 4 GiB or more");
+  const AttnLayout L = attn_layout(Lq, Lk, Hq, dh, k_feat, k_tok);
+  if (!ws || ws_bytes < L.total || !aligned(ws, 256))
+    return fail(RMM_ERR_WORKSPACE, "attention: workspace needs %zu bytes (256-byte aligned)", L.total);
+  char *w = static_cast<char *>(ws);
+  hipStream_t st = (hipStream_t)stream;
+  float *tok = tok_scores ? tok_scores : reinterpret_cast<float *>(w + L.tok);
+  int32_t *idx_clean = reinterpret_cast<int32_t *>(w + L.idxf);
+
+  // feature selection and the packed Q[:, I] (as rmm_qk)
+  const rmm::ColnormPlan p = plan_for(RMM_BF16, Q, Lq, dh, q_tok_stride, Hq, q_head_stride);
+  hipError_t he = rmm::launch_colnorm(RMM_BF16, Q, Lq, dh, q_tok_stride, Hq, q_head_stride,
+                                      reinterpret_cast<float *>(w + L.sc), w + L.part, p, st);
+  if (he != hipSuccess) return hip_status(he, "attention colnorm launch");
+  he = rmm::launch_topk(reinterpret_cast<float *>(w + L.sc), Hq, dh, k_feat, kfp, idx_feat, st);
+  if (he != hipSuccess) return hip_status(he, "attention topk launch");
+  he = rmm::launch_pack(RMM_BF16, Q, q_tok_stride, q_head_stride, idx_feat, kfp, Hq, Lq, dh, k_feat, kfp,
+                        w + L.qi, idx_clean, st);
+  if (he != hipSuccess) return hip_status(he, "attention pack launch");
+  {
+    // K[:, I] per query head: K_I[h][u][f] = Kt_g[I_h[f]][u]
+    rmm::KernelTimer timer("attn_kpack", st);
+    he = rmm::launch_bt_pack(Kt, ldkt, dh, Lk, idx_clean, kfp, w + L.ki, Hq, Hq, Hkv, kt_head_stride, kfp,
+                             Lk * kfp, st);
+    if (he != hipSuccess) return hip_status(he, "attention key pack launch");
+  }
+  rmm::AttnDesc d{};
+  d.QI = w + L.qi;
+  d.KI = w + L.ki;
+  d.KJ = w + L.kj;
+  d.VJT = w + L.vjt;
+  d.J = idx_tok;
+  {
+    float *st4 = reinterpret_cast<float *>(w + L.stats);
+    d.nm = st4;
+    d.il = st4 + Hq * Lq;
+    d.n2m = st4 + 2 * Hq * Lq;
+    d.il2 = st4 + 3 * Hq * Lq;
+  }
+  d.tok = tok;
+  d.O = O;
+  d.o_ts = o_tok_stride;
+  d.o_hs = o_head_stride;
+  d.hq = Hq;
+  d.Lq = Lq;
+  d.Lk = Lk;
+  d.dh = dh;
+  d.kf_pad = kfp;
+  d.kt = k_tok;
+  d.kt_pad = ktp;
+  d.causal = causal != 0;
+  he = rmm::launch_attn_passes(0, d, st);
+  if (he != hipSuccess) return hip_status(he, "attention row statistics launch");
+  he = rmm::launch_attn_passes(1, d, st);
+  if (he != hipSuccess) return hip_status(he, "attention token scores launch");
+  he = rmm::launch_topk(tok, Hq, Lk, k_tok, ktp, idx_tok, st);
+  if (he != hipSuccess) return hip_status(he, "attention token topk launch");
+  he = rmm::launch_attn_passes(2, d, st);
+  if (he != hipSuccess) return hip_status(he, "attention key gather launch");
+  {
+    // V_J^T[h][j][u] = V_g[J_h[u]][j]
+    rmm::KernelTimer timer("attn_vpack", st);
+    he = rmm::launch_bt_pack(V, v_tok_stride, Lk, dh, idx_tok, ktp, w + L.vjt, Hq, Hq, Hkv, v_head_stride, ktp,
+                             dh * ktp, st);
+    if (he != hipSuccess) return hip_status(he, "attention value pack launch");
+  }
+  return hip_status(rmm::launch_attn_passes(3, d, st), "attention output launch");
 }

@@ -37,13 +37,24 @@ constexpr int kBK = 64;   // slot granularity of the packed operands
 // Each thread loads an 8 (slots) x 8 (columns) block, transposes it in
 // registers into eight 16-byte K-runs, parks them in LDS as [n][64], and the
 // block then writes 256 rows of 128 contiguous bytes.
+// grid.z = batch entry b (several packs in one launch): it reads B group
+// floor(b * hkv / hq) (group stride b_gs), index row b and writes BT entry b.
+struct BtBatch {
+  int64_t hq, hkv, b_gs, idx_bs, bt_bs;
+};
 template <bool BVEC>
 __global__ __launch_bounds__(256) void bt_pack_kernel(const uint16_t *__restrict__ B, int64_t ldb,
                                                       int64_t d, int64_t n,
                                                       const int32_t *__restrict__ idx_clean,
-                                                      int64_t k_pad, uint16_t *__restrict__ BT) {
+                                                      int64_t k_pad, uint16_t *__restrict__ BT, BtBatch bb) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[256 * kBK];
   const int tid = threadIdx.x;
+  {
+    const int64_t b = blockIdx.z;
+    B += (b * bb.hkv / bb.hq) * bb.b_gs;
+    idx_clean += b * bb.idx_bs;
+    BT += b * bb.bt_bs;
+  }
   const int64_t n0 = (int64_t)blockIdx.x * 256;
   const int64_t t0 = (int64_t)blockIdx.y * kBK;
   const int nb = tid & 31, tb = tid >> 5;          // columns nb*8.., slots tb*8..
@@ -376,20 +387,27 @@ bool gemm_nt_ok(int64_t m, int64_t n, int64_t d, int64_t ldb, int64_t k_pad) {
          (uint64_t)((d - 1) * ldb + n) * 2 < mg::kMaxRecords;
 }
 
+hipError_t launch_bt_pack(const void *B, int64_t ldb, int64_t d, int64_t n, const int32_t *idx_clean,
+                          int64_t k_pad, void *BT, int64_t batch, int64_t hq, int64_t hkv, int64_t b_gs,
+                          int64_t idx_bs, int64_t bt_bs, hipStream_t st) {
+  const bool bvec = reinterpret_cast<uintptr_t>(B) % 16 == 0 && ldb % 8 == 0 && b_gs % 8 == 0;
+  dim3 grid((unsigned)ceil_div(n, 256), (unsigned)(k_pad / kBK), (unsigned)batch);
+  const BtBatch bb{hq, hkv, b_gs, idx_bs, bt_bs};
+  if (bvec)
+    hipLaunchKernelGGL(bt_pack_kernel<true>, grid, dim3(256), 0, st, static_cast<const uint16_t *>(B), ldb, d, n,
+                       idx_clean, k_pad, static_cast<uint16_t *>(BT), bb);
+  else
+    hipLaunchKernelGGL(bt_pack_kernel<false>, grid, dim3(256), 0, st, static_cast<const uint16_t *>(B), ldb, d, n,
+                       idx_clean, k_pad, static_cast<uint16_t *>(BT), bb);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_nt(const void *A_packed, const int32_t *idx_clean, const void *B, int64_t ldb,
                           int64_t d, void *BT_ws, void *Y, int64_t ldy, int64_t m, int64_t n,
                           int64_t k_pad, hipStream_t st) {
-  const bool bvec = reinterpret_cast<uintptr_t>(B) % 16 == 0 && ldb % 8 == 0;
   {
-    dim3 grid((unsigned)ceil_div(n, 256), (unsigned)(k_pad / kBK));
     KernelTimer timer("bt_pack", st);
-    if (bvec)
-      hipLaunchKernelGGL(bt_pack_kernel<true>, grid, dim3(256), 0, st, static_cast<const uint16_t *>(B), ldb, d,
-                         n, idx_clean, k_pad, static_cast<uint16_t *>(BT_ws));
-    else
-      hipLaunchKernelGGL(bt_pack_kernel<false>, grid, dim3(256), 0, st, static_cast<const uint16_t *>(B), ldb,
-                         d, n, idx_clean, k_pad, static_cast<uint16_t *>(BT_ws));
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_bt_pack(B, ldb, d, n, idx_clean, k_pad, BT_ws, 1, 1, 1, 0, 0, 0, st);
     if (e != hipSuccess) return e;
   }
   NtArgs g;

@@ -76,6 +76,12 @@ hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t stream);
 
 // ------------------------------------------------------------------ NT GEMM for many rows
 size_t gemm_nt_bt_bytes(int64_t n, int64_t k_pad);
+// BT[b][c][t] = B_g[idx[b][t]][c] for c < n, t < k_pad (zero where idx < 0), batch
+// entry b reading group g = floor(b * hkv / hq) of B (group stride b_gs); B rows
+// have ldb elements, d rows.  BT entries are n x k_pad apart (bt_bs).
+hipError_t launch_bt_pack(const void *B, int64_t ldb, int64_t d, int64_t n, const int32_t *idx_clean,
+                          int64_t k_pad, void *BT, int64_t batch, int64_t hq, int64_t hkv, int64_t b_gs,
+                          int64_t idx_bs, int64_t bt_bs, hipStream_t stream);
 bool gemm_nt_ok(int64_t m, int64_t n, int64_t d, int64_t ldb, int64_t k_pad);
 hipError_t launch_gemm_nt(const void *A_packed, const int32_t *idx_clean, const void *B, int64_t ldb,
                           int64_t d, void *BT_ws, void *Y, int64_t ldy, int64_t m, int64_t n,
@@ -96,5 +102,24 @@ hipError_t launch_pv(const void *P, int64_t ldp, int64_t p_hs, const void *V, in
                      int64_t v_hs, void *O, int64_t o_ts, int64_t o_hs, const int32_t *idx,
                      int64_t idx_stride, int64_t k, int64_t hq, int64_t hkv, int64_t Lq, int64_t Lk,
                      int64_t dh, bool causal, void *plan_ws, hipStream_t stream);
+
+// ---------------------------------------------------------------- fused reduced attention
+// Device buffers of one fused call (packed operands in the workspace).
+struct AttnDesc {
+  const void *QI, *KI;   // [hq][Lq][kf_pad], [hq][Lk][kf_pad] bf16
+  void *KJ;              // [hq][kt_pad][kf_pad] bf16 (written by pass 2)
+  const void *VJT;       // [hq][dh][kt_pad] bf16
+  const int32_t *J;      // [hq][kt_pad]
+  float *nm, *il;        // [hq][Lq] -(row max of c S), 1 / row sum
+  float *n2m, *il2;      // [hq][Lq] -2 max, 1 / sum^2
+  float *tok;            // [hq][Lk]
+  void *O;               // bf16, [Lq tokens of o_ts] x [hq of o_hs] x dh
+  int64_t o_ts, o_hs;
+  int64_t hq, Lq, Lk, dh, kf_pad, kt, kt_pad;
+  bool causal;
+};
+bool attn_supported(int64_t dh, int64_t kf_pad);
+// pass 0: row statistics, 1: token scores, 2: gather of the kept K rows, 3: output
+hipError_t launch_attn_passes(int pass, const AttnDesc &d, hipStream_t stream);
 
 }  // namespace rmm
