@@ -64,7 +64,9 @@ __all__ = [
     "kv_head",
     "reduced_qk",
     "causal_softmax",
+    "full_softmax",
     "reduced_pv",
+    "reduced_attention",
     "attention_chain",
 ]
 
@@ -188,6 +190,19 @@ def causal_softmax(S, scale: float) -> np.ndarray:
     return P
 
 
+def full_softmax(S, scale: float) -> np.ndarray:
+    """P[h, i, j] = softmax_j(scale * S[h, i, j]) over every key (no mask).
+
+    The probabilities of attention without a causal mask (an encoder, or a
+    query block that follows its whole context).  Row max subtracted, float64.
+    """
+    S64 = np.asarray(S, dtype=np.float64)
+    z = S64 * scale
+    z = z - z.max(axis=2, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=2, keepdims=True)
+
+
 def reduced_pv(P, V, k: int):
     """Token-reduced attention output, per query head.
 
@@ -214,17 +229,34 @@ def reduced_pv(P, V, k: int):
     return O, J, sc
 
 
+def reduced_attention(Q, Kt, V, k_feat: int, k_tok: int, causal: bool = True,
+                      scale: float | None = None):
+    """Reduced Q K^T -> softmax -> reduced P V for one layer, float64.
+
+    "Alcance de Aplicación": the feature dimension of Q K^T keeps k_feat
+    indices per query head (scored on Q_h), the token dimension of P V keeps
+    k_tok tokens per query head (scored on P_h); "Estrategia de Selección"
+    scores both by column norms.  The softmax sits between the two products;
+    causal masks key u from query t when u > t + (Lk - Lq) (reading R8).
+
+    Returns dict with S, P, O, I, J and the token scores ("tok") [Hq][Lk].
+    """
+    Q64 = np.asarray(Q, dtype=np.float64)
+    dh = Q64.shape[2]
+    scale = 1.0 / math.sqrt(dh) if scale is None else scale
+    S, I, _ = reduced_qk(Q64, Kt, k_feat)
+    P = causal_softmax(S, scale) if causal else full_softmax(S, scale)
+    O, J, tok = reduced_pv(P, V, k_tok)
+    return {"S": S, "P": P, "O": O, "I": I, "J": J, "tok": tok}
+
+
 def attention_chain(Q, Kt, V, rho: float, scale: float | None = None):
     """Reduced QK^T -> causal softmax -> reduced PV for one layer, float64.
 
     k for the feature reduction is ceil(rho*dh), for the token reduction
-    ceil(rho*Lk).  Returns dict with S, P, O, I, J.
+    ceil(rho*Lk).  Returns dict with S, P, O, I, J (and the token scores).
     """
-    Q64 = np.asarray(Q, dtype=np.float64)
-    dh = Q64.shape[2]
+    dh = np.asarray(Q).shape[2]
     Lk = np.asarray(Kt).shape[2]
-    scale = 1.0 / math.sqrt(dh) if scale is None else scale
-    S, I, _ = reduced_qk(Q64, Kt, retained_count(rho, dh))
-    P = causal_softmax(S, scale)
-    O, J, _ = reduced_pv(P, V, retained_count(rho, Lk))
-    return {"S": S, "P": P, "O": O, "I": I, "J": J}
+    return reduced_attention(Q, Kt, V, retained_count(rho, dh), retained_count(rho, Lk),
+                             causal=True, scale=scale)

@@ -324,3 +324,62 @@ def test_rho_one_attention_is_textbook_causal_attention():
     vv = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
     ref = torch.nn.functional.scaled_dot_product_attention(q, kk, vv, is_causal=True)
     np.testing.assert_allclose(out["O"], ref.permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_full_softmax_closed_forms():
+    Hq, Lq, Lk = 2, 3, 5
+    P = O.full_softmax(np.zeros((Hq, Lq, Lk)), 0.9)
+    np.testing.assert_allclose(P, 1.0 / Lk, rtol=1e-15)          # uniform over every key
+    rng = np.random.default_rng(17)
+    S = rng.standard_normal((Hq, Lq, Lk)) * 3
+    P = O.full_softmax(S, 0.4)
+    np.testing.assert_allclose(P.sum(axis=2), 1.0, rtol=1e-14)
+    assert np.all(P > 0)                                           # nothing is masked
+    # two keys: p0 = 1 / (1 + exp(scale*(b - a)))
+    P2 = O.full_softmax(np.array([[[2.0, -1.0]]]), 0.4)
+    assert P2[0, 0, 0] == pytest.approx(1.0 / (1.0 + math.exp(0.4 * (-3.0))), rel=1e-14)
+    # the last query of a causal square block sees every key: the rows agree
+    Sq = rng.standard_normal((Hq, Lk, Lk))
+    np.testing.assert_allclose(O.full_softmax(Sq, 0.4)[:, -1], O.causal_softmax(Sq, 0.4)[:, -1], rtol=1e-14)
+
+
+def test_reduced_attention_separate_counts_closed_form():
+    # Q = 0 -> S = 0 whatever k_feat keeps; causal P[i, j] = 1/(i+1), so the
+    # token scores fall with j and J = [0, k_tok); O[i] = sum_{j<=min(i,k_tok-1)} V[j] / (i+1).
+    rng = np.random.default_rng(18)
+    L, Hq, Hkv, dh = 9, 2, 1, 6
+    Q = np.zeros((L, Hq, dh))
+    Kt = rng.standard_normal((Hkv, dh, L))
+    V = rng.standard_normal((L, Hkv, dh))
+    out = O.reduced_attention(Q, Kt, V, 2, 4, causal=True)
+    assert out["I"].shape == (Hq, 2) and out["J"].shape == (Hq, 4)
+    np.testing.assert_array_equal(out["I"], [[0, 1], [0, 1]])      # all-zero scores: lowest indices
+    for i in range(L):
+        want = V[: min(i, 3) + 1, 0, :].sum(axis=0) / (i + 1)
+        np.testing.assert_allclose(out["O"][i, 0], want, rtol=1e-13, atol=1e-15)
+    # token score of key j: sqrt(sum_{i >= j} (i+1)^-2)
+    tj = [math.sqrt(sum((i + 1) ** -2 for i in range(j, L))) for j in range(L)]
+    np.testing.assert_allclose(out["tok"][1], tj, rtol=1e-14)
+    # without the mask every query averages all keys: J keeps the first k_tok
+    # (equal scores, lower index first) and O[i] = sum_{j<k_tok} V[j] / L
+    out = O.reduced_attention(Q, Kt, V, 2, 4, causal=False)
+    np.testing.assert_array_equal(out["J"][0], np.arange(4))
+    np.testing.assert_allclose(out["O"][:, 1], np.broadcast_to(V[:4, 0].sum(axis=0) / L, (L, dh)), rtol=1e-13)
+
+
+def test_full_attention_is_textbook_attention():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(19)
+    Lq, Lk, Hq, Hkv, dh = 7, 11, 4, 2, 8
+    Q = rng.standard_normal((Lq, Hq, dh))
+    Kt = rng.standard_normal((Hkv, dh, Lk))
+    V = rng.standard_normal((Lk, Hkv, dh))
+    q = torch.from_numpy(Q).permute(1, 0, 2)
+    kk = torch.from_numpy(Kt).permute(0, 2, 1).repeat_interleave(Hq // Hkv, 0)
+    vv = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+    out = O.reduced_attention(Q, Kt, V, dh, Lk, causal=False)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, kk, vv, is_causal=False)
+    np.testing.assert_allclose(out["O"], ref.permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+    # a single causal query placed after its context sees every key
+    out1 = O.reduced_attention(Q[-1:], Kt, V, dh, Lk, causal=True)
+    np.testing.assert_allclose(out1["O"][0], ref.permute(1, 0, 2).numpy()[-1], rtol=1e-10, atol=1e-12)
