@@ -23,6 +23,7 @@ __all__ = [
 ]
 
 RMM_BF16, RMM_F32 = 0, 1
+RMM_OK, RMM_ERR_INVALID_ARG, RMM_ERR_UNSUPPORTED, RMM_ERR_WORKSPACE, RMM_ERR_HIP = 0, 1, 2, 3, 4
 _STATUS = {0: "RMM_OK", 1: "RMM_ERR_INVALID_ARG", 2: "RMM_ERR_UNSUPPORTED", 3: "RMM_ERR_WORKSPACE",
            4: "RMM_ERR_HIP"}
 
