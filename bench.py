@@ -13,6 +13,11 @@ layer's logits), like X.
 Prints one JSON line.  `value` is effective TFLOP/s: the dense-equivalent
 flops of the step (2 m d n per projection, 2 dh per causal query-key pair,
 per head, for each attention product) divided by the measured step time.
+
+`fused_attention` times, beside the step, the fused reduced attention
+(rmm_attention: Q, K, V -> O with the softmax, the token scores and both
+selections inside, S and P never written) on the same Q, K and V, at the
+layer's ratio and at rho = 1.
 """
 from __future__ import annotations
 
@@ -45,6 +50,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true", help="skip the rho = 1 pass")
     ap.add_argument("--no-fuse", action="store_true",
                     help="one reduced product per weight instead of one per shared activation")
+    ap.add_argument("--no-fused-attention", action="store_true",
+                    help="skip the separate timing of the fused reduced attention (rmm_attention)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -263,6 +270,65 @@ def algorithmic_work(runner, key):
     return None, 0, None
 
 
+def fused_attention(R, layer, steps, warmup, dense=True):
+    """Time rmm_attention on the layer's Q, K and V: the whole reduced chain
+    (feature selection, Q K^T, causal softmax, token scores, token selection,
+    P V) in one call that never writes S or P, at the layer's ratio and at
+    rho = 1 (every feature and token kept).  Effective TFLOP/s counts the same
+    dense-equivalent attention flops as the step."""
+    import numpy as np
+    import torch
+
+    at = layer["attention"]
+    L, Hq, dh = at["L"], at["Hq"], at["dh"]
+    fl = 2 * (2.0 * causal_pairs(L) * dh * Hq)
+    res = {}
+    ratios = [("rho", R.rmm_k_from_rho(at["rho"], dh), R.rmm_k_from_rho(at["rho"], L))]
+    if dense:
+        ratios.append(("rho1", dh, L))
+    for name, kf, kt in ratios:
+        dev = at["Q"].device
+        O = torch.empty((L, Hq, dh), dtype=torch.bfloat16, device=dev)
+        If = torch.empty((Hq, R.rmm_k_pad(kf)), dtype=torch.int32, device=dev)
+        It = torch.empty((Hq, R.rmm_k_pad(kt)), dtype=torch.int32, device=dev)
+        ws = torch.empty(R.rmm_attention_workspace_bytes(L, L, Hq, dh, kf, kt), dtype=torch.uint8, device=dev)
+
+        class _One:
+            def step(self, tagged=False):
+                R.rmm_attention(at["Q"], at["Kt"], at["V"], kf, kt, O=O, idx_feat=If, idx_tok=It, ws=ws,
+                                causal=True)
+
+        ms, _ = time_steps(_One(), steps, warmup)
+        res[name] = {"k_feat": kf, "k_tok": kt, "ms": round(ms, 4), "effective_tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
+        if name == "rho":
+            R.timing.reset()
+            R.timing.enable(True)
+            n = max(2, min(steps, 5))
+            for _ in range(n):
+                _One().step()
+            torch.cuda.synchronize()
+            R.timing.enable(False)
+            tot = R.timing.collect()
+            R.timing.reset()
+            # exponentials per pass: every visible (query, key) pair in the two
+            # statistics passes, every visible (query, kept token) pair in the output pass
+            J = It[:, :kt].cpu().numpy().astype(np.float64)
+            n_exp = {"attn_stats": Hq * causal_pairs(L), "attn_colsq": Hq * causal_pairs(L),
+                     "attn_out": float((L - J).sum())}
+            kern = {}
+            for key, v in tot.items():
+                e = {"avg_ms": round(v[0] / v[1], 4)}
+                if key in n_exp:
+                    e["gexp_per_s"] = round(n_exp[key] / (v[0] / v[1] * 1e-3) / 1e9, 1)
+                kern[key] = e
+            res[name]["kernels"] = kern
+        del O, If, It, ws
+        torch.cuda.empty_cache()
+    if "rho1" in res:
+        res["speedup_vs_rho1"] = round(res["rho1"]["ms"] / res["rho"]["ms"], 3)
+    return res
+
+
 def csrc_sha256():
     import glob
     import hashlib
@@ -405,9 +471,17 @@ def main():
             g_fl += amount * v["launches_per_step"]
             g_ms += v["avg_ms"] * v["launches_per_step"]
     mfma_frac = (g_fl / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS) if g_ms > 0 else None
+    # the step's own Q K^T and P V (P an input), for comparison with the fused call
+    qkpv_ms = sum(v["avg_ms"] * v["launches_per_step"] for k, v in kern.items() if k.split("/")[0] in ("qk", "pv"))
     run.free()
     del run
     torch.cuda.empty_cache()
+
+    fused = None
+    if layer["attention"] is not None and not args.no_fused_attention:
+        fused = fused_attention(R, layer, args.steps, args.warmup, dense=not args.no_dense)
+        fused["step_qk_pv_ms"] = round(qkpv_ms, 4)
+        print(f"[bench] fused attention {fused['rho']['ms']:.3f} ms", file=sys.stderr, flush=True)
 
     speedup = dense_ms = None
     if not args.no_dense:
@@ -438,7 +512,7 @@ def main():
         "speedup_vs_rho1": round(speedup, 3) if speedup else None,
         "rho1_ms_per_step": round(dense_ms, 4) if dense_ms else None,
         "gemm_kept_mfma_frac": round(mfma_frac, 4) if mfma_frac is not None else None,
-        "roofline": roof, "cpu_baseline": cpu, "kernels": detail,
+        "roofline": roof, "cpu_baseline": cpu, "kernels": detail, "fused_attention": fused,
     }
     print(json.dumps(out), flush=True)
 
