@@ -147,6 +147,29 @@ rmm_status_t rmm_gemm(rmm_dtype_t dt, const void *A, int64_t lda, const void *B,
                       int64_t ldy, void *ws, size_t ws_bytes, rmm_stream_t stream);
 
 /*
+ * rmm_gemm_w8 - the reduced product with INT8 weights: Y = A[:, I] (Bq[I, :] * scale),
+ * scale applied per output column.  Source: "Mecanismo Central" (the reduced
+ * product) with the compatibility with INT8 weights stated in the abstract;
+ * selection still reads A only.
+ *   A (device, bf16) m x d, leading dimension lda >= d.
+ *   Bq (device, int8) d x n quantized weight, contraction index as rows,
+ *                leading dimension ldb >= n; only read.
+ *   scale (device, float) [n]: column c of the weight is Bq[:, c] * scale[c].
+ *   idx (device, int32) the kept indices, as for rmm_gemm.
+ *   Y (device, bf16) m x n, leading dimension ldy >= n.
+ *   m <= 32 (decode batches): the kept int8 rows are read once, converted to
+ *   bf16 exactly, multiplied with float32 accumulation, and the sum is scaled;
+ *   this path needs 16-byte aligned weight rows (Bq and ldb multiples of 16)
+ *   spanning less than 4 GiB, else RMM_ERR_UNSUPPORTED.  m > 32: the kept rows
+ *   are dequantized once to bf16(q * scale) and multiplied by the bf16 path.
+ *   ws: at least rmm_gemm_w8_workspace_bytes(m, n, k) bytes, 256-byte aligned.
+ */
+size_t rmm_gemm_w8_workspace_bytes(int64_t m, int64_t n, int64_t k);
+rmm_status_t rmm_gemm_w8(const void *A, int64_t lda, const void *Bq, int64_t ldb, const float *scale,
+                         const int32_t *idx, int64_t m, int64_t d, int64_t n, int64_t k, void *Y,
+                         int64_t ldy, void *ws, size_t ws_bytes, rmm_stream_t stream);
+
+/*
  * rmm_qk - feature-reduced attention scores for every query head (bf16 in,
  * float32 out).  Source: "Alcance de Aplicación" (reduce the feature dimension
  * of Q K^T).  For query head h with kv head g = floor(h*Hkv/Hq):

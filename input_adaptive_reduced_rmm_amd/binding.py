@@ -16,9 +16,10 @@ import torch
 __all__ = [
     "RMMError", "load", "lib_path",
     "rmm_version", "rmm_k_from_rho", "rmm_k_pad",
-    "rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_qk", "rmm_pv", "rmm_attention",
+    "rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_gemm_w8", "rmm_qk", "rmm_pv", "rmm_attention",
     "rmm_colnorm_workspace_bytes", "rmm_topk_workspace_bytes", "rmm_gemm_workspace_bytes",
     "rmm_qk_workspace_bytes", "rmm_pv_workspace_bytes", "rmm_attention_workspace_bytes",
+    "rmm_gemm_w8_workspace_bytes",
     "rmm_linear", "timing",
 ]
 
@@ -66,6 +67,9 @@ _PROTOS = {
     "rmm_pv": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
                               ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
     "rmm_attention_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
+    "rmm_gemm_w8_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "rmm_gemm_w8": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _sz,
+                                   _vp]),
     "rmm_attention": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _vp,
                                      _i64, _i64, _i64, _i64, ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _vp,
                                      _vp, _sz, _vp]),
@@ -227,6 +231,33 @@ def rmm_gemm(A: torch.Tensor, B: torch.Tensor, idx: torch.Tensor, k: int, out: t
     ws, wsb = _ws(int(lib.rmm_gemm_workspace_bytes(dt, m, n, int(k))), dev, ws)
     _check(lib.rmm_gemm(dt, _ptr(A), A.stride(0), _ptr(B), B.stride(0), _ptr(idx), m, d, n, int(k), _ptr(out),
                         out.stride(0), _ptr(ws), wsb, _stream(dev)))
+    return out
+
+
+def rmm_gemm_w8_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(load().rmm_gemm_w8_workspace_bytes(m, n, k))
+
+
+def rmm_gemm_w8(A: torch.Tensor, Bq: torch.Tensor, scale: torch.Tensor, idx: torch.Tensor, k: int,
+                out: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """Y = A[:, idx[:k]] @ (Bq[idx[:k], :] * scale) for bf16 A [m, d], int8 Bq [d, n], float32 scale [n]."""
+    lib = load()
+    dev = _dev(A, Bq, scale, idx)
+    if A.dtype != torch.bfloat16 or Bq.dtype != torch.int8 or scale.dtype != torch.float32:
+        raise TypeError("rmm_gemm_w8 takes bfloat16 A, int8 Bq and float32 scale")
+    if A.dim() != 2 or Bq.dim() != 2 or A.stride(1) != 1 or Bq.stride(1) != 1 or not scale.is_contiguous():
+        raise ValueError("A [m, d] and Bq [d, n] must be 2-D with unit column stride, scale contiguous")
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be contiguous int32")
+    m, d = A.shape
+    d2, n = Bq.shape
+    if d2 != d or scale.numel() != n:
+        raise ValueError("shapes of A, Bq and scale disagree")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    ws, wsb = _ws(rmm_gemm_w8_workspace_bytes(m, n, int(k)), dev, ws)
+    _check(lib.rmm_gemm_w8(_ptr(A), A.stride(0), _ptr(Bq), Bq.stride(0), _ptr(scale), _ptr(idx), m, d, n, int(k),
+                           _ptr(out), out.stride(0), _ptr(ws), wsb, _stream(dev)))
     return out
 
 

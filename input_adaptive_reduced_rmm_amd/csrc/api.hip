@@ -188,6 +188,7 @@ RMM_API size_t rmm_gemm_workspace_bytes(rmm_dtype_t dt, int64_t m, int64_t n, in
   const int64_t k_pad = rmm_k_pad(k);
   size_t b = align256((size_t)m * (size_t)k_pad * esize(dt)) + align256((size_t)k_pad * 4);
   if (gemm_uses_nt(dt, m)) b += rmm::gemm_nt_bt_bytes(n, k_pad);
+  if (dt == RMM_BF16 && m <= 32) b += align256(rmm::skinny_part_bytes(false, m, n, k_pad));
   return b;
 }
 
@@ -215,6 +216,12 @@ RMM_API rmm_status_t rmm_gemm(rmm_dtype_t dt, const void *A, int64_t lda, const 
     return hip_status(rmm::launch_gemm_nt(ws, idx_clean, B, ldb, d, bt, Y, ldy, m, n, k_pad, st),
                       "gemm launch");
   }
+  if (dt == RMM_BF16 && rmm::skinny_ok(m, B, ldb, false, d, n)) {
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + align256((size_t)m * k_pad * e) +
+                                            align256((size_t)k_pad * 4));
+    return hip_status(rmm::launch_gemm_skinny(ws, idx_clean, B, false, nullptr, ldb, d, m, n, k_pad, Y, ldy, part, st),
+                      "gemm launch");
+  }
   rmm::GemmArgs g{};
   g.A = ws;
   g.idx = idx_clean;
@@ -235,6 +242,92 @@ RMM_API rmm_status_t rmm_gemm(rmm_dtype_t dt, const void *A, int64_t lda, const 
   g.k_pad = k_pad;
   he = dt == RMM_BF16 ? rmm::launch_gemm_bf16(g, rmm::OutType::BF16, st) : rmm::launch_gemm_f32(g, st);
   return hip_status(he, "gemm launch");
+}
+
+// ------------------------------------------------------------------ int8 weights
+// Workspace: packed A_I, cleaned indices, then for m <= 32 the partial sums of
+// the few-row kernel, else the dequantized kept rows Bd [k_pad][n], an index
+// list 0..k-1 over them and, for m >= 1024, the NT GEMM's B_I^T.
+struct W8Layout {
+  size_t a, idx, part, bd, iota, bt, total;
+};
+static W8Layout w8_layout(int64_t m, int64_t n, int64_t k) {
+  const int64_t k_pad = rmm_k_pad(k);
+  W8Layout L{};
+  Carve c(nullptr);
+  L.a = c.off;    c.take((size_t)m * k_pad * 2);
+  L.idx = c.off;  c.take((size_t)k_pad * 4);
+  if (m <= 32) {
+    L.part = c.off; c.take(rmm::skinny_part_bytes(true, m, n, k_pad));
+  } else {
+    L.bd = c.off;   c.take((size_t)k_pad * n * 2);
+    L.iota = c.off; c.take((size_t)k_pad * 4);
+    if (gemm_uses_nt(RMM_BF16, m)) {
+      L.bt = c.off;
+      c.take(rmm::gemm_nt_bt_bytes(n, k_pad));
+    }
+  }
+  L.total = c.off;
+  return L;
+}
+
+RMM_API size_t rmm_gemm_w8_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m < 1 || k < 1 || n < 1) return 0;
+  return w8_layout(m, n, k).total;
+}
+
+RMM_API rmm_status_t rmm_gemm_w8(const void *A, int64_t lda, const void *Bq, int64_t ldb, const float *scale,
+                                 const int32_t *idx, int64_t m, int64_t d, int64_t n, int64_t k, void *Y,
+                                 int64_t ldy, void *ws, size_t ws_bytes, rmm_stream_t stream) {
+  if (!A || !Bq || !scale || !idx || !Y) return fail(RMM_ERR_INVALID_ARG, "gemm_w8: NULL pointer");
+  if (m < 1 || n < 1 || d < 1 || d >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "gemm_w8: bad m, n or d");
+  if (k < 1 || k > d) return fail(RMM_ERR_INVALID_ARG, "gemm_w8: need 1 <= k <= d");
+  if (lda < d || ldb < n || ldy < n) return fail(RMM_ERR_INVALID_ARG, "gemm_w8: leading dimension too small");
+  if (!aligned(A, 2) || !aligned(Y, 2) || !aligned(scale, 4) || !aligned(idx, 4))
+    return fail(RMM_ERR_INVALID_ARG, "gemm_w8: misaligned pointer");
+  if (m <= 32 && !rmm::skinny_ok(m, Bq, ldb, true, d, n))
+    return fail(RMM_ERR_UNSUPPORTED, "gemm_w8: m <= 32 needs 16-byte aligned weight rows (Bq %% 16 == 0, ldb %% 16 == 0) "
+                "spanning less than 4 GiB");
+  const W8Layout L = w8_layout(m, n, k);
+  if (!ws || ws_bytes < L.total || !aligned(ws, 256))
+    return fail(RMM_ERR_WORKSPACE, "gemm_w8: workspace needs %zu bytes (256-byte aligned)", L.total);
+  const int64_t k_pad = rmm_k_pad(k);
+  hipStream_t st = (hipStream_t)stream;
+  char *w = static_cast<char *>(ws);
+  int32_t *idx_clean = reinterpret_cast<int32_t *>(w + L.idx);
+  hipError_t he = rmm::launch_pack(RMM_BF16, A, lda, 0, idx, 0, 1, m, d, k, k_pad, w + L.a, idx_clean, st);
+  if (he != hipSuccess) return hip_status(he, "gemm_w8 pack launch");
+  if (m <= 32)
+    return hip_status(rmm::launch_gemm_skinny(w + L.a, idx_clean, Bq, true, scale, ldb, d, m, n, k_pad, Y, ldy,
+                                              reinterpret_cast<float *>(w + L.part), st),
+                      "gemm_w8 launch");
+  // Many rows: the product is bound by MFMA, not by the weight bytes, so the
+  // kept rows are dequantized once and multiplied by the bf16 path.
+  he = rmm::launch_w8_dequant_rows(Bq, ldb, scale, idx_clean, k_pad, n, w + L.bd, st);
+  if (he != hipSuccess) return hip_status(he, "gemm_w8 dequant launch");
+  int32_t *iota = reinterpret_cast<int32_t *>(w + L.iota);
+  he = rmm::launch_topk(nullptr, 1, k, k, k_pad, iota, st);   // k == d: 0..k-1, then -1
+  if (he != hipSuccess) return hip_status(he, "gemm_w8 index launch");
+  if (gemm_uses_nt(RMM_BF16, m) && rmm::gemm_nt_ok(m, n, k_pad, n, k_pad))
+    return hip_status(rmm::launch_gemm_nt(w + L.a, iota, w + L.bd, n, k_pad, w + L.bt, Y, ldy, m, n, k_pad, st),
+                      "gemm_w8 launch");
+  rmm::GemmArgs g{};
+  g.A = w + L.a;
+  g.idx = iota;
+  g.idx_stride = k_pad;
+  g.B = w + L.bd;
+  g.ldb = n;
+  g.Y = Y;
+  g.ldy = ldy;
+  g.batch = 1;
+  g.hq = 1;
+  g.hkv = 1;
+  g.m = m;
+  g.n = n;
+  g.d = k_pad;
+  g.k = k;
+  g.k_pad = k_pad;
+  return hip_status(rmm::launch_gemm_bf16(g, rmm::OutType::BF16, st), "gemm_w8 launch");
 }
 
 // ------------------------------------------------------------------ attention

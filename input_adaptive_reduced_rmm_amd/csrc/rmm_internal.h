@@ -74,6 +74,18 @@ enum class OutType { BF16, F32 };
 hipError_t launch_gemm_bf16(const GemmArgs &a, OutType out, hipStream_t stream);
 hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t stream);
 
+// ------------------------------------------------------------------ GEMM for few rows (m <= 32)
+// B bf16 (w8 false) or int8 with a float scale per column (w8 true); rows of B
+// must be 16-byte aligned.  part: skinny_part_bytes of fp32 partial sums.
+bool skinny_ok(int64_t m, const void *B, int64_t ldb, bool w8, int64_t d, int64_t n);
+size_t skinny_part_bytes(bool w8, int64_t m, int64_t n, int64_t k_pad);
+hipError_t launch_gemm_skinny(const void *A_packed, const int32_t *idx_clean, const void *B, bool w8,
+                              const float *scale, int64_t ldb, int64_t d, int64_t m, int64_t n, int64_t k_pad,
+                              void *Y, int64_t ldy, float *part, hipStream_t stream);
+// Bd[t][c] = bf16(Bq[idx[t]][c] * scale[c]) for t < k_pad (zero where idx < 0); Bd is k_pad x n.
+hipError_t launch_w8_dequant_rows(const void *Bq, int64_t ldb, const float *scale, const int32_t *idx_clean,
+                                  int64_t k_pad, int64_t n, void *Bd, hipStream_t stream);
+
 // ------------------------------------------------------------------ NT GEMM for many rows
 size_t gemm_nt_bt_bytes(int64_t n, int64_t k_pad);
 // BT[b][c][t] = B_g[idx[b][t]][c] for c < n, t < k_pad (zero where idx < 0), batch

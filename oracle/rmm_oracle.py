@@ -60,6 +60,7 @@ __all__ = [
     "column_scores",
     "select_top",
     "reduced_product",
+    "reduced_product_w8",
     "rmm",
     "kv_head",
     "reduced_qk",
@@ -122,6 +123,18 @@ def reduced_product(A, B, I) -> np.ndarray:
     B64 = np.asarray(B, dtype=np.float64)
     I = np.asarray(I, dtype=np.int64)
     return A64[:, I] @ B64[I, :]
+
+
+def reduced_product_w8(A, Bq, scale, I) -> np.ndarray:
+    """A[:, I] @ (Bq[I, :] * scale) in float64, scale applied per output column.
+
+    The reduced product over a weight held as INT8 values with one scale per
+    output column; the abstract states that the method works with INT8
+    weights, and the selection (on A) does not change.  The weight entering
+    the product is exactly q * scale.
+    """
+    B = np.asarray(Bq, dtype=np.float64) * np.asarray(scale, dtype=np.float64)[None, :]
+    return reduced_product(A, B, I)
 
 
 def rmm(A, B, rho: float):

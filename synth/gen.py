@@ -20,6 +20,7 @@ __all__ = [
     "outlier_activations",
     "lognormal_col_activations",
     "weight",
+    "int8_per_column",
     "attention_qkv",
     "causal_probs",
 ]
@@ -85,6 +86,18 @@ def weight(rng: np.random.Generator, d_in: int, d_out: int, bf16: bool = True) -
     """
     w = normal(rng, (d_in, d_out), std=1.0 / np.sqrt(d_in))
     return bf16_round(w) if bf16 else w
+
+
+def int8_per_column(B: np.ndarray):
+    """Symmetric per-output-column INT8 form of a weight B [d][n]: scale[c] =
+    max_j |B[j, c]| / 127 (1 for an all-zero column), q = round(B / scale)
+    clipped to [-127, 127].  Returns (q int8 [d][n], scale float32 [n]).  This
+    is how the INT8 weight inputs are prepared; it is not part of the method."""
+    B = np.asarray(B, dtype=np.float32)
+    amax = np.abs(B).max(axis=0)
+    scale = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
+    q = np.clip(np.rint(B / scale[None, :]), -127, 127).astype(np.int8)
+    return q, scale
 
 
 def attention_qkv(seed: int, workload_id: int, L: int, Hq: int, Hkv: int, dh: int,

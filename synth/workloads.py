@@ -12,11 +12,11 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .gen import (attention_qkv, bf16_round, lognormal_col_activations, normal,
+from .gen import (attention_qkv, bf16_round, int8_per_column, lognormal_col_activations, normal,
                   outlier_activations, stream, weight)
 
 __all__ = ["Linear", "Attention", "Workload", "WORKLOADS", "linear_operands", "linear_activation",
-           "linear_weight", "activation_key", "attention_operands"]
+           "linear_weight", "linear_weight_int8", "activation_key", "attention_operands"]
 
 
 @dataclass(frozen=True)
@@ -124,6 +124,11 @@ def linear_weight(w: Workload, lin: Linear, seed: int = 0) -> np.ndarray:
     """B [d, n] of one projection (rows are the contraction index)."""
     return weight(stream(seed, w.wid, lin.tensor_b * 100003 + lin.d * 7 + lin.n), lin.d, lin.n,
                   bf16=w.dtype == "bf16")
+
+
+def linear_weight_int8(w: Workload, lin: Linear, seed: int = 0):
+    """(q int8 [d, n], scale float32 [n]): the projection's weight in per-column INT8 form."""
+    return int8_per_column(linear_weight(w, lin, seed))
 
 
 def activation_key(w: Workload, lin: Linear, m: int | None = None):

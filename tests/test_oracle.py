@@ -383,3 +383,40 @@ def test_full_attention_is_textbook_attention():
     # a single causal query placed after its context sees every key
     out1 = O.reduced_attention(Q[-1:], Kt, V, dh, Lk, causal=True)
     np.testing.assert_allclose(out1["O"][0], ref.permute(1, 0, 2).numpy()[-1], rtol=1e-10, atol=1e-12)
+
+
+def test_w8_product_worked_example():
+    # A = [1 2 3]; q rows (1, -2), (3, 4), (-5, 6); scales (0.5, 0.25); keep {0, 2}:
+    # column 0: 1*(1*0.5) + 3*(-5*0.5) = -7;  column 1: 1*(-2*0.25) + 3*(6*0.25) = 4.
+    A = np.array([[1.0, 2.0, 3.0]])
+    q = np.array([[1, -2], [3, 4], [-5, 6]], dtype=np.int8)
+    s = np.array([0.5, 0.25], dtype=np.float32)
+    np.testing.assert_array_equal(O.reduced_product_w8(A, q, s, [0, 2]), [[-7.0, 4.0]])
+
+
+def test_w8_product_scales_columns_and_drops_rows():
+    rng = np.random.default_rng(20)
+    m, d, n = 5, 9, 6
+    A = rng.standard_normal((m, d))
+    q = rng.integers(-127, 128, size=(d, n)).astype(np.int8)
+    s = rng.uniform(0.01, 0.1, size=n).astype(np.float32)
+    I = np.array([1, 4, 5, 8])
+    Y = O.reduced_product_w8(A, q, s, I)
+    # doubling one column's scale doubles that output column only (powers of two: exact)
+    s2 = s.copy()
+    s2[3] *= 2
+    Y2 = O.reduced_product_w8(A, q, s2, I)
+    np.testing.assert_array_equal(Y2[:, 3], 2 * Y[:, 3])
+    np.testing.assert_array_equal(np.delete(Y2, 3, axis=1), np.delete(Y, 3, axis=1))
+    # dropped rows of q do not matter: overwrite them and nothing changes
+    qx = q.copy()
+    qx[np.setdiff1d(np.arange(d), I)] = 99
+    np.testing.assert_array_equal(O.reduced_product_w8(A, qx, s, I), Y)
+    # element by element against the sum it stands for
+    for i in range(m):
+        for c in range(n):
+            want = sum(A[i, t] * (float(q[t, c]) * float(s[c])) for t in I)
+            assert Y[i, c] == pytest.approx(want, rel=1e-13, abs=1e-15)
+    # keeping every row and unit scales is the integer product
+    Yf = O.reduced_product_w8(A, q, np.ones(n, dtype=np.float32), np.arange(d))
+    np.testing.assert_allclose(Yf, A @ q.astype(np.int64), rtol=1e-13)

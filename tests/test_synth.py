@@ -49,3 +49,18 @@ def test_row_prefix_is_stable_across_m():
     a = synth.linear_activation(w, lin, m=40)
     b = synth.linear_activation(w, lin, m=13)
     np.testing.assert_array_equal(a[:13], b)
+
+
+def test_int8_per_column_form():
+    rng = np.random.default_rng(1)
+    B = (rng.standard_normal((300, 40)) * rng.uniform(0.01, 3.0, size=40)).astype(np.float32)
+    B[:, 7] = 0.0                                           # an all-zero column
+    q, s = synth.int8_per_column(B)
+    assert q.dtype == np.int8 and s.dtype == np.float32 and s.shape == (40,)
+    assert np.all(np.abs(q.astype(np.int32)) <= 127)
+    assert np.all(q[:, 7] == 0) and s[7] == 1.0
+    # each column's largest magnitude maps to +-127, and q * s is within half a step of B
+    # (plus the float32 rounding of B / s, at most 127 * 2^-23 steps)
+    cols = [c for c in range(40) if c != 7]
+    assert np.all(np.abs(q[:, cols]).max(axis=0) == 127)
+    assert np.all(np.abs(q.astype(np.float64) * s - B) <= (0.5 + 2e-5) * s.astype(np.float64))
