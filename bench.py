@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true", help="skip the rho = 1 pass")
     ap.add_argument("--no-fuse", action="store_true",
                     help="one reduced product per weight instead of one per shared activation")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step from a captured HIP graph (launch-bound shapes such as decode batches)")
     ap.add_argument("--no-fused-attention", action="store_true",
                     help="skip the separate timing of the fused reduced attention (rmm_attention)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -199,6 +201,28 @@ def dense_flops(layer):
     return f
 
 
+class GraphStep:
+    """One step of a runner captured into a HIP graph (torch.cuda.CUDAGraph); the
+    library launches on torch's current stream, which the capture redirects."""
+
+    def __init__(self, runner):
+        import torch
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            runner.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g):
+            runner.step()
+        torch.cuda.synchronize()
+
+    def step(self, tagged=False):
+        self.g.replay()
+
+
 def time_steps(runner, steps, warmup):
     import torch
 
@@ -259,7 +283,14 @@ def algorithmic_work(runner, key):
     p = plans[0]
     e = 4 if runner.layer["dtype"].itemsize == 4 else 2
     if kern.startswith("gemm"):
-        return "mfma", 2.0 * p["m"] * p["k"] * p["n"], "flops"
+        # MFMA-bound unless reading the operands once takes longer at peak
+        # bandwidth than the kept flops at peak rate (few rows: decode batches).
+        flops = 2.0 * p["m"] * p["k"] * p["n"]
+        byts = float(p["m"] * p["k"] * e + p["k"] * p["n"] * e + p["m"] * p["n"] * e)
+        peak_f = (PEAK_F32_TFLOPS if e == 4 else PEAK_BF16_TFLOPS) * 1e12
+        if byts / (PEAK_HBM_GBS * 1e9) > flops / peak_f:
+            return "hbm", byts, "bytes"
+        return "mfma", flops, "flops"
     if kern == "bt_pack":
         # kept weight rows read, their transposed copy written
         return "hbm", 2.0 * p["k"] * p["n"] * e, "bytes"
@@ -427,7 +458,7 @@ def main():
         copy_calibration(dev)
 
     run = Runner(R, layer, dev)
-    ms, wall = time_steps(run, args.steps, args.warmup)
+    ms, wall = time_steps(GraphStep(run) if args.graph else run, args.steps, args.warmup)
     print(f"[bench] rho step {ms:.3f} ms (wall {wall:.3f})", file=sys.stderr, flush=True)
     kern = kernel_breakdown(run, max(2, min(args.steps, 5)))
     flops = dense_flops(layer)
@@ -486,7 +517,7 @@ def main():
     speedup = dense_ms = None
     if not args.no_dense:
         run1 = Runner(R, layer, dev, rho_scale_one=True)
-        dense_ms, _ = time_steps(run1, args.steps, args.warmup)
+        dense_ms, _ = time_steps(GraphStep(run1) if args.graph else run1, args.steps, args.warmup)
         speedup = dense_ms / ms
         print(f"[bench] rho=1 step {dense_ms:.3f} ms", file=sys.stderr, flush=True)
         run1.free()
@@ -502,7 +533,7 @@ def main():
 
     value = flops / (ms * 1e-3) / 1e12
     cfg = {"workload": wl.key, "dtype": wl.dtype, "rho": _rho_desc(wl, args),
-           "products": _products_desc(wl, args)}
+           "products": _products_desc(wl, args), "launch": "hip graph replay" if args.graph else "eager"}
     out = {
         "metric": "effective TFLOP/s (dense-equivalent flops / RMM step time)",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

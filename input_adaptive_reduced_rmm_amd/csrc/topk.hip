@@ -6,10 +6,9 @@
 // k-th largest key T is found by MSD radix select: the bits every key shares
 // are skipped (found with a block OR/AND reduction), then <= 8-bit digits are
 // histogrammed in LDS and a single wave locates the digit that holds the k-th
-// key.  Emission is one ordered pass: each thread owns a contiguous index
-// segment, counts its keys > T and == T, and two block-wide exclusive scans
-// give every thread its output offset and how many of its == T keys it may
-// take (the lowest-index ones win).  All integer work: the result is exact.
+// key.  Emission walks the keys in index order, one contiguous run per wave:
+// keys > T are kept, and of the keys == T the lowest-index ones up to the
+// count still needed.  All integer work: the result is exact.
 #include "rmm_internal.h"
 #include "timing.h"
 
@@ -26,32 +25,9 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Block-wide exclusive prefix sum of one uint32 per thread; returns the block total in *total.
-__device__ uint32_t block_excl_scan(uint32_t v, uint32_t *wsum, uint32_t *total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t w = lane < kWaves ? wsum[lane] : 0u;
-#pragma unroll
-    for (int off = 1; off < kWaves; off <<= 1) {
-      uint32_t y = __shfl_up(w, off, 64);
-      if (lane >= off) w += y;
-    }
-    if (lane < kWaves) wsum[kWaves + lane] = w;  // inclusive wave prefix
-  }
-  __syncthreads();
-  const uint32_t before = wave ? wsum[kWaves + wave - 1] : 0u;
-  *total = wsum[2 * kWaves - 1];
-  const uint32_t r = before + x - v;
-  __syncthreads();
-  return r;
+// Set bits of a wave mask in lanes below this one.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 template <bool IN_LDS>
@@ -60,7 +36,6 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
                                                         int32_t *__restrict__ idx) {
   __shared__ uint32_t keys[IN_LDS ? kLdsKeys : 1];
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t wsum[2 * kWaves];
   __shared__ uint32_t red_or[kWaves], red_and[kWaves];
   __shared__ uint32_t sel_digit, sel_above;
 
@@ -73,12 +48,26 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
   };
 
   // Load keys; OR/AND over all keys gives the bits every key shares.
+  // Eight loads per thread are issued before any is used, so the pass costs
+  // about one memory latency per eight keys instead of one per key.
   uint32_t kor = 0u, kand = 0xFFFFFFFFu;
-  for (int64_t j = tid; j < d; j += kThreads) {
-    const uint32_t key = score_key(s[j]);
-    if constexpr (IN_LDS) keys[j] = key;
-    kor |= key;
-    kand &= key;
+  for (int64_t j0 = tid; j0 < d; j0 += 8 * kThreads) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t j = j0 + (int64_t)u * kThreads;
+      v[u] = j < d ? s[j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t j = j0 + (int64_t)u * kThreads;
+      if (j < d) {
+        const uint32_t key = score_key(v[u]);
+        if constexpr (IN_LDS) keys[j] = key;
+        kor |= key;
+        kand &= key;
+      }
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -110,9 +99,18 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
     const uint32_t dmask = (1u << width) - 1u;
     if (tid < 256) hist[tid] = 0u;
     __syncthreads();
-    for (int64_t j = tid; j < d; j += kThreads) {
-      const uint32_t key = key_at(j);
-      if ((key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+    for (int64_t j0 = tid; j0 < d; j0 += 8 * kThreads) {
+      uint32_t kk[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t j = j0 + (int64_t)u * kThreads;
+        kk[u] = j < d ? key_at(j) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t j = j0 + (int64_t)u * kThreads;
+        if (j < d && (kk[u] & hmask) == prefix) atomicAdd(&hist[(kk[u] >> shift) & dmask], 1u);
+      }
     }
     __syncthreads();
     if (wave == 0) {
@@ -145,27 +143,79 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
   }
 
   // prefix is now the k-th largest key T; krem of the keys equal to T are kept.
+  // Emission: each wave owns a contiguous run of indices and walks it 64 keys
+  // at a time (lane = key, conflict-free LDS reads).  A counting walk gives
+  // each wave its kept keys; the waves' output offsets and shares of the keys
+  // equal to T follow in index order; a second walk writes every kept index
+  // at its slot (ballot + lane prefix count), so the output is ascending.
   const uint32_t T = prefix;
-  const int64_t seg = (d + kThreads - 1) / kThreads;
-  const int64_t j0 = (int64_t)tid * seg;
-  const int64_t j1 = j0 + seg < d ? j0 + seg : d;
+  const int64_t per_wave = ((d + kWaves - 1) / kWaves + 63) / 64 * 64;
+  const int64_t w0 = (int64_t)wave * per_wave;
+  const int64_t w1 = w0 + per_wave < d ? w0 + per_wave : d;
+  // Both walks read eight 64-key chunks before using any (one LDS latency per
+  // eight chunks instead of one per chunk).
+  constexpr int U = 8;
   uint32_t gt = 0u, eq = 0u;
-  for (int64_t j = j0; j < j1; ++j) {
-    const uint32_t key = key_at(j);
-    gt += key > T;
-    eq += key == T;
+  for (int64_t c0 = w0; c0 < w1; c0 += 64 * U) {
+    uint32_t kk[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = c0 + 64 * u + lane;
+      kk[u] = j < w1 ? key_at(j) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool valid = c0 + 64 * u + lane < w1;
+      gt += valid && kk[u] > T;
+      eq += valid && kk[u] == T;
+    }
   }
-  uint32_t tot;
-  const uint32_t eq_before = block_excl_scan(eq, wsum, &tot);
-  const uint32_t take_eq =
-      krem > eq_before ? ((krem - eq_before) < eq ? (krem - eq_before) : eq) : 0u;
-  const uint32_t pos0 = block_excl_scan(gt + take_eq, wsum, &tot);
-  uint32_t pos = pos0, taken = 0u;
-  for (int64_t j = j0; j < j1; ++j) {
-    const uint32_t key = key_at(j);
-    if (key > T || (key == T && taken < take_eq)) {
-      out[pos++] = (int32_t)j;
-      taken += key == T;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    gt += __shfl_xor(gt, off, 64);
+    eq += __shfl_xor(eq, off, 64);
+  }
+  __syncthreads();   // the wave arrays are reused below
+  if (lane == 0) {
+    red_or[wave] = gt;
+    red_and[wave] = eq;
+  }
+  __syncthreads();
+  uint32_t my_take = 0u, my_pos = 0u;
+  {
+    uint32_t eq_acc = 0u, pos_acc = 0u;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t g_w = red_or[w], e_w = red_and[w];
+      const uint32_t take = krem > eq_acc ? ((krem - eq_acc) < e_w ? (krem - eq_acc) : e_w) : 0u;
+      if (w == wave) {
+        my_take = take;
+        my_pos = pos_acc;
+      }
+      eq_acc += e_w;
+      pos_acc += g_w + take;
+    }
+  }
+  uint32_t eq_seen = 0u, kept_seen = 0u;
+  for (int64_t c0 = w0; c0 < w1; c0 += 64 * U) {
+    uint32_t kk[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = c0 + 64 * u + lane;
+      kk[u] = j < w1 ? key_at(j) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = c0 + 64 * u + lane;
+      const bool valid = j < w1;
+      const bool is_eq = valid && kk[u] == T;
+      const uint64_t eqm = __ballot(is_eq);
+      const uint32_t eq_rank = eq_seen + lanes_below(eqm);
+      const bool keep = valid && (kk[u] > T || (is_eq && eq_rank < my_take));
+      const uint64_t km = __ballot(keep);
+      if (keep) out[my_pos + kept_seen + lanes_below(km)] = (int32_t)j;
+      eq_seen += (uint32_t)__popcll(eqm);
+      kept_seen += (uint32_t)__popcll(km);
     }
   }
   for (int64_t t = k + tid; t < k_pad; t += kThreads) out[t] = -1;

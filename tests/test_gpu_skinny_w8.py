@@ -133,3 +133,45 @@ def test_llama70b_decode_projection_int8(name):
     I = idx.cpu().numpy()[:k]
     assert rel_fro(Y.float().cpu().numpy(), oracle.reduced_product_w8(A, q, s, I)) < TOL_BF16
     torch.cuda.synchronize()
+
+
+def test_decode_chain_graph_replay_matches_eager():
+    """Scores -> top-k -> few-row GEMM captured in a HIP graph: every replay, with
+    eager work and synchronisations between them, equals the eager result."""
+    m, d, n, rho = 16, 8192, 4096, 0.5
+    A = dev_tensor(_acts(m, d, 21), BF)
+    B = dev_tensor(_weight(d, n, 22), BF)
+    k = R.rmm_k_from_rho(rho, d)
+    sc = torch.empty(d, dtype=torch.float32, device=DEV)
+    idx = torch.empty(R.rmm_k_pad(k), dtype=torch.int32, device=DEV)
+    Y = torch.empty((m, n), dtype=BF, device=DEV)
+    ws_c = torch.empty(max(R.rmm_colnorm_workspace_bytes(BF, m, d), 1), dtype=torch.uint8, device=DEV)
+    ws_g = torch.empty(R.rmm_gemm_workspace_bytes(BF, m, n, k), dtype=torch.uint8, device=DEV)
+
+    def chain():
+        R.rmm_colnorm(A, out=sc, ws=ws_c)
+        R.rmm_topk(sc, k, out=idx)
+        R.rmm_gemm(A, B, idx, k, out=Y, ws=ws_g)
+
+    chain()
+    torch.cuda.synchronize()
+    y_ref, i_ref = Y.clone(), idx.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        chain()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chain()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        Y.zero_()
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, i_ref), f"replay {rep}: indices differ"
+        assert torch.equal(Y, y_ref), f"replay {rep}: output differs"
+        _ = (B[:64].float() * 2).sum().item()                      # unrelated eager work
