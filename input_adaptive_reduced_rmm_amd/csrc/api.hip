@@ -460,7 +460,7 @@ static AttnLayout attn_layout(int64_t Lq, int64_t Lk, int64_t Hq, int64_t dh, in
   L.qi = c.off;   c.take((size_t)Hq * Lq * kfp * 2);
   L.idxf = c.off; c.take((size_t)Hq * kfp * 4);
   L.ki = c.off;   c.take((size_t)Hq * Lk * kfp * 2);
-  L.stats = c.off; c.take((size_t)4 * Hq * Lq * 4);
+  L.stats = c.off; c.take((size_t)2 * Hq * Lq * 4);
   L.tok = c.off;  c.take((size_t)Hq * Lk * 4);
   L.kj = c.off;   c.take((size_t)Hq * ktp * kfp * 2);
   L.vjt = c.off;  c.take((size_t)Hq * dh * ktp * 2);
@@ -532,11 +532,9 @@ RMM_API rmm_status_t rmm_attention(const void *Q, int64_t Lq, int64_t Hq, int64_
   d.VJT = w + L.vjt;
   d.J = idx_tok;
   {
-    float *st4 = reinterpret_cast<float *>(w + L.stats);
-    d.nm = st4;
-    d.il = st4 + Hq * Lq;
-    d.n2m = st4 + 2 * Hq * Lq;
-    d.il2 = st4 + 3 * Hq * Lq;
+    float *st2 = reinterpret_cast<float *>(w + L.stats);
+    d.nml = st2;
+    d.n2ml = st2 + Hq * Lq;
   }
   d.tok = tok;
   d.O = O;

@@ -7,7 +7,7 @@
 // The token scores need every row of P before any output can be formed, so
 // the work runs in passes over recomputed score tiles:
 //   A  (per query row)   m_i = max_j c S_ij,  l_i = sum_j 2^(c S_ij - m_i)
-//   B  (per key column)  s_j = sqrt(sum_i P_ij^2) with P_ij = 2^(c S_ij - m_i) / l_i
+//   B  (per key column)  s_j = sqrt(sum_i P_ij^2) with P_ij = 2^(c S_ij - m_i - log2 l_i)
 //   top-k of s           J (kept tokens, ascending)
 //   D  (per query row)   O_i = sum_{j in J} P_ij V_j
 // with c = log2(e) / sqrt(dh) and S_ij = Q_I[i] . K_I[j] over the kept
@@ -49,8 +49,8 @@ struct AttnArgs {
   const uint16_t *KJ;   // [hq][kt_pad][KF]
   const uint16_t *VJT;  // [hq][dh][kt_pad]
   const int32_t *J;     // [hq][kt_pad] kept tokens, ascending, -1 padded
-  float *nm, *il;       // [hq][Lq] -(row max of c S) and 1 / row sum (pass D)
-  float *n2m, *il2;     // [hq][Lq] the same as -2 max and 1 / sum^2 (pass B)
+  float *nml;           // [hq][Lq] -(row max of c S) - log2(row sum): P = 2^(c S + nml)
+  float *n2ml;          // [hq][Lq] 2 nml: P^2 = 2^(2 c S + n2ml)
   float *tok;           // [hq][Lk] token scores
   uint16_t *O;          // [Lq tokens of o_ts] x [hq of o_hs] x dh
   int64_t o_ts, o_hs;
@@ -89,11 +89,11 @@ struct Tile {
 // bf16 matrix (resource r) into `dst`.  Load i of a wave fills LDS block
 // q = i * kWaves + wave = (half, 8-row group): rows 8 g + lane/8 of that
 // half, slot lane%8, which holds logical chunk slot ^ f(row).
-template <int KF>
+template <int KF, int NW = kWaves>
 __device__ __forceinline__ void issue_tile(rsrc_t r, int64_t row0, unsigned char *dst, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < Tile<KF>::PER_WAVE; ++i) {
-    const int q = i * kWaves + wave;
+  for (int i = 0; i < Tile<KF>::BLOCKS / NW; ++i) {
+    const int q = i * NW + wave;
     const int half = q / 8, grp = q % 8;
     const int row = grp * 8 + lane / 8;
     const int slot = lane % 8;
@@ -206,12 +206,11 @@ __global__ __launch_bounds__(kThreads) void attn_stats_kernel(AttnArgs g) {
     l = (m_run == kNegInf ? 0.f : l_run * fexp2((m_run - m) * g.c2)) +
         (m_p == kNegInf ? 0.f : l_p * fexp2((m_p - m) * g.c2));
   if (lane < 32 && qi < g.Lq) {
-    const float mc = m * g.c2, inv = l > 0.f ? 1.f / l : 0.f;
+    // the normaliser folds into the exponent: P = 2^(c s - c max - log2 sum)
+    const float v = l > 0.f ? -m * g.c2 - log2f(l) : kNegInf;
     const int64_t o = h * g.Lq + qi;
-    g.nm[o] = -mc;
-    g.il[o] = inv;
-    g.n2m[o] = -2.f * mc;
-    g.il2[o] = inv * inv;
+    g.nml[o] = v;
+    g.n2ml[o] = 2.f * v;
   }
 }
 
@@ -221,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void attn_stats_kernel(AttnArgs g) {
 // holds for its key; lanes l and l+32 are merged at the end.
 template <int KF>
 __global__ __launch_bounds__(kThreads) void attn_colsq_kernel(AttnArgs g) {
-  constexpr int STAGE = Tile<KF>::BYTES + 2 * kT * 4;   // Q tile, then m2 and il of its rows
+  constexpr int STAGE = Tile<KF>::BYTES + kT * 4;   // Q tile, then n2ml of its rows
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -232,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void attn_colsq_kernel(AttnArgs g) {
   bf16x8_t kf[KF / 16];
   load_row_frags<KF>(g.KI + h * g.Lk * KF, g.Lk, k0l, lane, kf);
   const int Lq = (int)g.Lq, Lk = (int)g.Lk, off = (int)g.off, k0 = (int)k0l, key = k0 + (lane & 31);
-  const float c4 = 2.f * g.c2;   // p^2 = 2^(2 c s - 2 max) / sum^2
+  const float c4 = 2.f * g.c2;   // p^2 = 2^(2 c s + n2ml)
 
   // first query row any key of the block can be seen from
   const int64_t qfirst = g.causal ? max((int64_t)0, kb * kRows - g.off) : 0;
@@ -240,15 +239,13 @@ __global__ __launch_bounds__(kThreads) void attn_colsq_kernel(AttnArgs g) {
   const int64_t nt = cdiv(g.Lq, kT) - t_first;
   const int64_t wave_qfirst = g.causal ? k0l - g.off : 0;   // queries below this see no key of the wave
   const rsrc_t rq = mg::make_rsrc(g.QI + h * g.Lq * KF, (uint64_t)g.Lq * KF * 2);
-  const rsrc_t rm = mg::make_rsrc(g.n2m + h * g.Lq, (uint64_t)g.Lq * 4);
-  const rsrc_t ri = mg::make_rsrc(g.il2 + h * g.Lq, (uint64_t)g.Lq * 4);
+  const rsrc_t rm = mg::make_rsrc(g.n2ml + h * g.Lq, (uint64_t)g.Lq * 4);
 
   auto issue = [&](int64_t t, unsigned char *dst) {
     const int64_t row0 = (t_first + t) * kT;
     issue_tile<KF>(rq, row0, dst, wave, lane);
-    // row statistics: wave 0 loads 64 values of -2 max, wave 1 of 1 / sum^2 (4 bytes per lane)
+    // row statistics: wave 0 loads the 64 rows' n2ml (4 bytes per lane)
     if (wave == 0) lds_load4(rm, dst + Tile<KF>::BYTES, (uint32_t)((row0 + lane) * 4), 0);
-    if (wave == 1) lds_load4(ri, dst + Tile<KF>::BYTES + kT * 4, (uint32_t)((row0 + lane) * 4), 0);
   };
 
   float c_lane = 0.f;
@@ -257,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void attn_colsq_kernel(AttnArgs g) {
     unsigned char *cur = smem + (t & 1) * STAGE;
     if (t + 1 < nt) {
       issue(t + 1, smem + ((t + 1) & 1) * STAGE);
-      if (wave < 2) __builtin_amdgcn_s_waitcnt(vm_imm(Tile<KF>::PER_WAVE + 1));
+      if (wave == 0) __builtin_amdgcn_s_waitcnt(vm_imm(Tile<KF>::PER_WAVE + 1));
       else __builtin_amdgcn_s_waitcnt(vm_imm(Tile<KF>::PER_WAVE));
     } else {
       __builtin_amdgcn_s_waitcnt(vm_imm(0));
@@ -265,8 +262,7 @@ __global__ __launch_bounds__(kThreads) void attn_colsq_kernel(AttnArgs g) {
     __syncthreads();
     const int qt0 = (int)((t_first + t) * kT);
     if (qt0 + kT > wave_qfirst) {
-      const float *sm = reinterpret_cast<const float *>(cur + Tile<KF>::BYTES);   // -2 max
-      const float *si = sm + kT;                                                  // 1 / sum^2
+      const float *sm = reinterpret_cast<const float *>(cur + Tile<KF>::BYTES);   // n2ml
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         f32x16_t acc;
@@ -284,11 +280,10 @@ __global__ __launch_bounds__(kThreads) void attn_colsq_kernel(AttnArgs g) {
         for (int b4 = 0; b4 < 4; ++b4) {
           const int rr = sub * 32 + 8 * b4 + 4 * (lane >> 5);   // tile row of register 4*b4
           const float4 mv = *reinterpret_cast<const float4 *>(&sm[rr]);
-          const float4 iv = *reinterpret_cast<const float4 *>(&si[rr]);
-          const float mm[4] = {mv.x, mv.y, mv.z, mv.w}, ii[4] = {iv.x, iv.y, iv.z, iv.w};
+          const float mm[4] = {mv.x, mv.y, mv.z, mv.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float p2 = fexp2(fmaf(acc[4 * b4 + e], c4, mm[e])) * ii[e];
+            float p2 = fexp2(fmaf(acc[4 * b4 + e], c4, mm[e]));
             if (!full) {
               const int q = qt0 + rr + e;
               const bool ok = q < Lq && key < Lk && (!g.causal || key <= q + off);
@@ -324,8 +319,7 @@ __global__ __launch_bounds__(kThreads) void attn_out_kernel(AttnArgs g) {
   bf16x8_t qf[KF / 16];
   load_row_frags<KF>(g.QI + h * g.Lq * KF, g.Lq, q0l, lane, qf);
   const int off = (int)g.off, kt = (int)g.kt, q0 = (int)q0l, qi = q0 + (lane & 31);
-  const float nm = qi < g.Lq ? g.nm[h * g.Lq + qi] : 0.f;
-  const float il = qi < g.Lq ? g.il[h * g.Lq + qi] : 0.f;
+  const float nml = qi < g.Lq ? g.nml[h * g.Lq + qi] : kNegInf;
 
   // kept tokens the block can see: J is ascending, so count J < limit
   const int32_t *Jh = g.J + h * g.kt_pad;
@@ -396,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void attn_out_kernel(AttnArgs g) {
       const bool full = js0 + 31 < kt && (!g.causal || jt[sub * 32 + 31] <= q0 + off);
       float p[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = fexp2(fmaf(acc[r], g.c2, nm)) * il;
+      for (int r = 0; r < 16; ++r) p[r] = fexp2(fmaf(acc[r], g.c2, nml));
       if (!full) {
 #pragma unroll
         for (int b4 = 0; b4 < 4; ++b4) {
@@ -447,6 +441,183 @@ __global__ __launch_bounds__(kThreads) void attn_out_kernel(AttnArgs g) {
     }
 }
 
+// ---------------------------------------------------------------- pass D, 64 queries per wave
+// The same output pass with 4 waves of 64 queries (two 32-query groups) per
+// workgroup: every K_J and V_J^T fragment read from LDS feeds the MFMAs of
+// both groups, which halves the LDS traffic per product, and the two groups'
+// independent MFMA and exponential work can overlap within the wave.
+constexpr int kWaves2 = 4;
+constexpr int kThreads2 = 64 * kWaves2;
+
+#ifndef RMM_ATTN_OUT2_WPE
+#define RMM_ATTN_OUT2_WPE 2
+#endif
+#ifndef RMM_ATTN_OUT2_KCACHE
+#define RMM_ATTN_OUT2_KCACHE 0
+#endif
+template <int KF>
+__global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(RMM_ATTN_OUT2_WPE))) void attn_out2_kernel(AttnArgs g) {
+  constexpr int VT_BYTES = 128 * kT * 2;                      // V_J^T tile [128 d][64 kept]
+  constexpr int STAGE = Tile<KF>::BYTES + VT_BYTES + kT * 4;  // + kept token ids
+  constexpr int K_PER_WAVE = Tile<KF>::BLOCKS / kWaves2;
+  constexpr int VT_PER_WAVE = VT_BYTES / 1024 / kWaves2;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, lk = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t qb = g.blocks_q - 1 - (int64_t)blockIdx.x / g.hq;
+  const int64_t h = (int64_t)blockIdx.x % g.hq;
+  const int64_t q0l = qb * kRows + 64 * wave;
+  bf16x8_t qf[2][KF / 16];
+  load_row_frags<KF>(g.QI + h * g.Lq * KF, g.Lq, q0l, lane, qf[0]);
+  load_row_frags<KF>(g.QI + h * g.Lq * KF, g.Lq, q0l + 32, lane, qf[1]);
+  const int off = (int)g.off, kt = (int)g.kt, q0 = (int)q0l;
+  float nml[2];
+#pragma unroll
+  for (int gq = 0; gq < 2; ++gq) {
+    const int qi = q0 + 32 * gq + (lane & 31);
+    nml[gq] = qi < g.Lq ? g.nml[h * g.Lq + qi] : kNegInf;
+  }
+
+  // kept tokens the block can see: J is ascending, so count J < limit
+  const int32_t *Jh = g.J + h * g.kt_pad;
+  int64_t ncount = g.kt;
+  if (g.causal) {
+    const int64_t limit = qb * kRows + kRows - 1 + g.off;   // last visible token of the block
+    int64_t lo = 0, hi = g.kt;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) >> 1;
+      if ((int64_t)Jh[mid] <= limit) lo = mid + 1;
+      else hi = mid;
+    }
+    ncount = lo;
+  }
+  const int nt = (int)cdiv(ncount, kT);
+  const rsrc_t rk = mg::make_rsrc(g.KJ + h * g.kt_pad * KF, (uint64_t)g.kt_pad * KF * 2);
+  const rsrc_t rv = mg::make_rsrc(g.VJT + h * 128 * g.kt_pad, (uint64_t)128 * g.kt_pad * 2);
+  const rsrc_t rj = mg::make_rsrc(Jh, (uint64_t)g.kt_pad * 4);
+
+  auto issue = [&](int t, unsigned char *dst) {
+    const int64_t j0 = (int64_t)t * kT;
+    issue_tile<KF, kWaves2>(rk, j0, dst, wave, lane);
+#pragma unroll
+    for (int i = 0; i < VT_PER_WAVE; ++i) {
+      const int q = i * kWaves2 + wave;   // 16 blocks of 8 rows
+      const int row = q * 8 + lane / 8, slot = lane % 8;
+      const int logical = slot ^ ((row ^ (row >> 3)) & 7);
+      lds_load16(rv, dst + Tile<KF>::BYTES + q * 1024,
+                 (uint32_t)(((int64_t)row * g.kt_pad + j0 + logical * 8) * 2), 0);
+    }
+    if (wave == 0) lds_load4(rj, dst + Tile<KF>::BYTES + VT_BYTES, (uint32_t)((j0 + lane) * 4), 0);
+  };
+  constexpr int LPW = K_PER_WAVE + VT_PER_WAVE;
+
+  f32x16_t acc_o[2][4];
+#pragma unroll
+  for (int gq = 0; gq < 2; ++gq)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[gq][dt][r] = 0.f;
+
+  if (nt > 0) issue(0, smem);
+  for (int t = 0; t < nt; ++t) {
+    unsigned char *cur = smem + (t & 1) * STAGE;
+    if (t + 1 < nt) {
+      issue(t + 1, smem + ((t + 1) & 1) * STAGE);
+      if (wave == 0) __builtin_amdgcn_s_waitcnt(vm_imm(LPW + 1));
+      else __builtin_amdgcn_s_waitcnt(vm_imm(LPW));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vm_imm(0));
+    }
+    __syncthreads();
+    const int32_t *jt = reinterpret_cast<const int32_t *>(cur + Tile<KF>::BYTES + VT_BYTES);
+    const uint16_t *vt = reinterpret_cast<const uint16_t *>(cur + Tile<KF>::BYTES);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+#if RMM_ATTN_OUT2_KCACHE
+      bf16x8_t kfr[KF / 16];
+#pragma unroll
+      for (int ks = 0; ks < KF / 16; ++ks) kfr[ks] = lds_frag<KF>(cur, sub * 32 + (lane & 31), ks, lk);
+#endif
+      const int js0 = t * kT + sub * 32;
+      const int last_tok = jt[sub * 32 + 31];
+      bf16x8_t pf[2][2];
+#pragma unroll
+      for (int gq = 0; gq < 2; ++gq) {
+        f32x16_t acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KF / 16; ++ks) {
+#if RMM_ATTN_OUT2_KCACHE
+          const bf16x8_t kf8 = kfr[ks];
+#else
+          const bf16x8_t kf8 = lds_frag<KF>(cur, sub * 32 + (lane & 31), ks, lk);
+#endif
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf8, qf[gq][ks], acc, 0, 0, 0);
+        }
+        // Every query of the group sees every token of the slice unless the
+        // slice crosses the diagonal or the end of the kept list.
+        const int qg0 = q0 + 32 * gq;
+        const bool full = js0 + 31 < kt && (!g.causal || last_tok <= qg0 + off);
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = fexp2(fmaf(acc[r], g.c2, nml[gq]));
+        if (!full) {
+          const int qi = qg0 + (lane & 31);
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4) {
+            const int rr = sub * 32 + 8 * b4 + 4 * lk;   // tile row of register 4*b4
+            const int4 tv = *reinterpret_cast<const int4 *>(&jt[rr]);
+            const int32_t tok[4] = {tv.x, tv.y, tv.z, tv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int jpos = t * kT + rr + e;
+              const bool ok = jpos < kt && tok[e] >= 0 && (!g.causal || tok[e] <= qi + off);
+              p[4 * b4 + e] = ok ? p[4 * b4 + e] : 0.f;
+            }
+          }
+        }
+        // regroup into the A operand of two 16-token K-slices (see attn_out_kernel)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const uint32_t own_lo = pack_bf16x2(p[8 * kk + 0], p[8 * kk + 1]);
+          const uint32_t own_hi = pack_bf16x2(p[8 * kk + 2], p[8 * kk + 3]);
+          const uint32_t nxt_lo = pack_bf16x2(p[8 * kk + 4], p[8 * kk + 5]);
+          const uint32_t nxt_hi = pack_bf16x2(p[8 * kk + 6], p[8 * kk + 7]);
+          const uint32_t send_lo = lk ? own_lo : nxt_lo, send_hi = lk ? own_hi : nxt_hi;
+          const uint32_t got_lo = (uint32_t)__shfl_xor((int)send_lo, 32, 64);
+          const uint32_t got_hi = (uint32_t)__shfl_xor((int)send_hi, 32, 64);
+          const uint4 pa = lk ? make_uint4(got_lo, got_hi, nxt_lo, nxt_hi) : make_uint4(own_lo, own_hi, got_lo, got_hi);
+          pf[gq][kk] = __builtin_bit_cast(bf16x8_t, pa);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ksv = sub * 2 + kk;   // 16-token slice of the 64-token tile
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const bf16x8_t vfrag = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const uint4 *>(&vt[mg::swz(dt * 32 + (lane & 31), ksv * 2 + lk)]));
+          acc_o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[0][kk], vfrag, acc_o[0][dt], 0, 0, 0);
+          acc_o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[1][kk], vfrag, acc_o[1][dt], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  uint16_t *Oh = g.O + h * g.o_hs;
+#pragma unroll
+  for (int gq = 0; gq < 2; ++gq)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t q = q0 + 32 * gq + 8 * (r >> 2) + 4 * lk + (r & 3);
+        if (q < g.Lq) Oh[q * g.o_ts + dt * 32 + (lane & 31)] = f32_to_bf16(acc_o[gq][dt][r]);
+      }
+}
+
 // Rows of K_I gathered by the kept tokens: KJ[h][j] = KI[h][J[h][j]] (zero rows
 // for padding).  One thread per 16-byte chunk.
 template <int KF>
@@ -475,10 +646,8 @@ hipError_t launch_attn_passes(int pass, const AttnDesc &d, hipStream_t st) {
   g.KJ = static_cast<const uint16_t *>(d.KJ);
   g.VJT = static_cast<const uint16_t *>(d.VJT);
   g.J = d.J;
-  g.nm = d.nm;
-  g.il = d.il;
-  g.n2m = d.n2m;
-  g.il2 = d.il2;
+  g.nml = d.nml;
+  g.n2ml = d.n2ml;
   g.tok = d.tok;
   g.O = static_cast<uint16_t *>(d.O);
   g.o_ts = d.o_ts;
@@ -518,7 +687,11 @@ hipError_t launch_attn_passes(int pass, const AttnDesc &d, hipStream_t st) {
     KernelTimer timer("attn_out", st);
     dim3 grid((unsigned)(g.blocks_q * g.hq));
     if (kf128) hipLaunchKernelGGL(attn_out_kernel<128>, grid, dim3(kThreads), 0, st, g);
+#ifndef RMM_ATTN_OUT1
+    else hipLaunchKernelGGL(attn_out2_kernel<64>, grid, dim3(kThreads2), 0, st, g);
+#else
     else hipLaunchKernelGGL(attn_out_kernel<64>, grid, dim3(kThreads), 0, st, g);
+#endif
   }
   return hipGetLastError();
 }

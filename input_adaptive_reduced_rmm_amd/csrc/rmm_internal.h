@@ -122,8 +122,7 @@ struct AttnDesc {
   void *KJ;              // [hq][kt_pad][kf_pad] bf16 (written by pass 2)
   const void *VJT;       // [hq][dh][kt_pad] bf16
   const int32_t *J;      // [hq][kt_pad]
-  float *nm, *il;        // [hq][Lq] -(row max of c S), 1 / row sum
-  float *n2m, *il2;      // [hq][Lq] -2 max, 1 / sum^2
+  float *nml, *n2ml;     // [hq][Lq] -(row max of c S) - log2(row sum), and twice that
   float *tok;            // [hq][Lk]
   void *O;               // bf16, [Lq tokens of o_ts] x [hq of o_hs] x dh
   int64_t o_ts, o_hs;
