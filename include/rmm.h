@@ -170,6 +170,27 @@ rmm_status_t rmm_gemm_w8(const void *A, int64_t lda, const void *Bq, int64_t ldb
                          int64_t ldy, void *ws, size_t ws_bytes, rmm_stream_t stream);
 
 /*
+ * rmm_swiglu_scored - the gated MLP activation with its column scores in one
+ * pass: H = silu(G) * U elementwise (silu(x) = x / (1 + e^-x), float32
+ * arithmetic, bf16 result) and scores[j] = ||H[:, j]||_2 over the m rows of the
+ * bf16 values written, float32 accumulation in a fixed order.  Source:
+ * "Estrategia de Selección" (scores are column norms of the activation, a
+ * light vector operation): the producer of the down projection's input
+ * scores it, so rmm_topk can follow without a separate rmm_colnorm pass.
+ *   G, U (device, bf16) m x n gate and up projections, leading dimensions
+ *                ldg, ldu >= n (e.g. two halves of one fused GEMM output).
+ *   H (device, bf16) m x n output, leading dimension ldh >= n; may not alias G or U.
+ *   scores (device, float) [n].
+ *   Pointers and leading dimensions must give 16-byte aligned rows and n must
+ *   be a multiple of 8, else RMM_ERR_UNSUPPORTED.
+ *   ws: rmm_swiglu_scored_workspace_bytes(m, n) bytes (0: none), 256-byte aligned.
+ */
+size_t rmm_swiglu_scored_workspace_bytes(int64_t m, int64_t n);
+rmm_status_t rmm_swiglu_scored(const void *G, int64_t ldg, const void *U, int64_t ldu, int64_t m, int64_t n,
+                               void *H, int64_t ldh, float *scores, void *ws, size_t ws_bytes,
+                               rmm_stream_t stream);
+
+/*
  * rmm_qk - feature-reduced attention scores for every query head (bf16 in,
  * float32 out).  Source: "Alcance de Aplicación" (reduce the feature dimension
  * of Q K^T).  For query head h with kv head g = floor(h*Hkv/Hq):

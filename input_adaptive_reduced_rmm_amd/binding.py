@@ -16,10 +16,11 @@ import torch
 __all__ = [
     "RMMError", "load", "lib_path",
     "rmm_version", "rmm_k_from_rho", "rmm_k_pad",
-    "rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_gemm_w8", "rmm_qk", "rmm_pv", "rmm_attention",
+    "rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_gemm_w8", "rmm_swiglu_scored", "rmm_qk", "rmm_pv",
+    "rmm_attention",
     "rmm_colnorm_workspace_bytes", "rmm_topk_workspace_bytes", "rmm_gemm_workspace_bytes",
     "rmm_qk_workspace_bytes", "rmm_pv_workspace_bytes", "rmm_attention_workspace_bytes",
-    "rmm_gemm_w8_workspace_bytes",
+    "rmm_gemm_w8_workspace_bytes", "rmm_swiglu_scored_workspace_bytes",
     "rmm_linear", "timing",
 ]
 
@@ -68,6 +69,8 @@ _PROTOS = {
                               ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
     "rmm_attention_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
     "rmm_gemm_w8_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "rmm_swiglu_scored_workspace_bytes": (_sz, [_i64, _i64]),
+    "rmm_swiglu_scored": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp]),
     "rmm_gemm_w8": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _sz,
                                    _vp]),
     "rmm_attention": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _vp,
@@ -259,6 +262,30 @@ def rmm_gemm_w8(A: torch.Tensor, Bq: torch.Tensor, scale: torch.Tensor, idx: tor
     _check(lib.rmm_gemm_w8(_ptr(A), A.stride(0), _ptr(Bq), Bq.stride(0), _ptr(scale), _ptr(idx), m, d, n, int(k),
                            _ptr(out), out.stride(0), _ptr(ws), wsb, _stream(dev)))
     return out
+
+
+def rmm_swiglu_scored_workspace_bytes(m: int, n: int) -> int:
+    return int(load().rmm_swiglu_scored_workspace_bytes(m, n))
+
+
+def rmm_swiglu_scored(G: torch.Tensor, U: torch.Tensor, H: torch.Tensor | None = None,
+                      scores: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """H = silu(G) * U (bf16 [m, n]) and the column scores of H (float32 [n]) in one pass."""
+    lib = load()
+    dev = _dev(G, U)
+    if G.dtype != torch.bfloat16 or U.dtype != torch.bfloat16:
+        raise TypeError("rmm_swiglu_scored takes bfloat16 G and U")
+    if G.dim() != 2 or G.shape != U.shape or G.stride(1) != 1 or U.stride(1) != 1:
+        raise ValueError("G and U must be [m, n] with unit column stride")
+    m, n = G.shape
+    if H is None:
+        H = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    if scores is None:
+        scores = torch.empty(n, dtype=torch.float32, device=dev)
+    ws, wsb = _ws(rmm_swiglu_scored_workspace_bytes(m, n), dev, ws)
+    _check(lib.rmm_swiglu_scored(_ptr(G), G.stride(0), _ptr(U), U.stride(0), m, n, _ptr(H), H.stride(0),
+                                 _ptr(scores), _ptr(ws), wsb, _stream(dev)))
+    return H, scores
 
 
 def rmm_qk(Q: torch.Tensor, Kt: torch.Tensor, k: int, S: torch.Tensor | None = None,

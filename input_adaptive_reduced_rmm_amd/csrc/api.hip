@@ -330,6 +330,29 @@ RMM_API rmm_status_t rmm_gemm_w8(const void *A, int64_t lda, const void *Bq, int
   return hip_status(rmm::launch_gemm_bf16(g, rmm::OutType::BF16, st), "gemm_w8 launch");
 }
 
+// ------------------------------------------------------------------ producer-fused scores
+RMM_API size_t rmm_swiglu_scored_workspace_bytes(int64_t m, int64_t n) {
+  if (m < 1 || n < 1) return 0;
+  return align256(rmm::swiglu_part_bytes(m, n));
+}
+
+RMM_API rmm_status_t rmm_swiglu_scored(const void *G, int64_t ldg, const void *U, int64_t ldu, int64_t m, int64_t n,
+                                       void *H, int64_t ldh, float *scores, void *ws, size_t ws_bytes,
+                                       rmm_stream_t stream) {
+  if (!G || !U || !H || !scores) return fail(RMM_ERR_INVALID_ARG, "swiglu_scored: NULL pointer");
+  if (m < 1 || n < 1 || n >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "swiglu_scored: bad m or n");
+  if (ldg < n || ldu < n || ldh < n) return fail(RMM_ERR_INVALID_ARG, "swiglu_scored: leading dimension too small");
+  if (!aligned(scores, 4)) return fail(RMM_ERR_INVALID_ARG, "swiglu_scored: misaligned pointer");
+  if (!rmm::swiglu_ok(G, ldg, U, ldu, H, ldh, n))
+    return fail(RMM_ERR_UNSUPPORTED, "swiglu_scored: needs 16-byte aligned rows (pointers, leading dimensions and n multiples of 8 elements)");
+  const size_t need = rmm_swiglu_scored_workspace_bytes(m, n);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
+    return fail(RMM_ERR_WORKSPACE, "swiglu_scored: workspace needs %zu bytes (256-byte aligned)", need);
+  return hip_status(rmm::launch_swiglu_scored(G, ldg, U, ldu, m, n, H, ldh, scores, static_cast<float *>(ws),
+                                              (hipStream_t)stream),
+                    "swiglu_scored launch");
+}
+
 // ------------------------------------------------------------------ attention
 static size_t qk_layout(int64_t Lq, int64_t Hq, int64_t dh, int64_t k, size_t *o_scores,
                         size_t *o_part, size_t *o_pack, size_t *o_idx) {

@@ -236,6 +236,13 @@ hipError_t dispatch_tpr(int tpr, dim3 grid, const T *A, int64_t m, int64_t d, in
 
 }  // namespace
 
+hipError_t launch_colnorm_finish(const float *part, int64_t chunks, int64_t n, float *scores, hipStream_t st) {
+  KernelTimer timer("colnorm_finish", st);
+  hipLaunchKernelGGL(colnorm_finish, dim3((unsigned)ceil_div(n, kFinCols)), dim3(kFinCols * kFinGroups), 0, st, part,
+                     chunks, n, scores);
+  return hipGetLastError();
+}
+
 ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch, bool vec_ok, bool causal) {
   ColnormPlan p;
   const int esz = dt == RMM_BF16 ? 2 : 4;

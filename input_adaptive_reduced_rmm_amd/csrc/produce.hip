@@ -1,0 +1,137 @@
+// Producer-fused column scores: the kernel that writes an activation also
+// accumulates the sums of squares of its columns, so the next reduced product
+// can select its indices without reading the activation again ("Estrategia de
+// Selección": the score of index j is the norm of column j of A; the pages
+// call it a lightweight vector operation beside the product).
+//
+// swiglu_scored_kernel writes the gated MLP activation H = silu(G) * U (the
+// input of the down projection of a LLaMA-style layer), rounded to bf16, and
+// adds the squares of exactly those bf16 values per column.  A wave covers 512
+// contiguous columns of a row (16 bytes per lane); the four waves of a block
+// take interleaved rows of its row chunk, four rows in flight per lane, and
+// meet in LDS at the end; chunk partials are added in a fixed order by
+// colnorm_finish, so the scores are bitwise deterministic.
+#include "mfma_gemm.h"
+#include "rmm_internal.h"
+#include "timing.h"
+
+namespace rmm {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kCols = 64 * 8;   // columns per block (8 bf16 per lane)
+constexpr int kUnroll = 4;      // rows in flight per lane
+
+__device__ __forceinline__ float silu(float x) {
+  // x * sigmoid(x) = x / (1 + 2^(-x log2 e))
+  return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
+__global__ __launch_bounds__(64 * kWaves) void swiglu_scored_kernel(const uint16_t *__restrict__ G, int64_t ldg,
+                                                                    const uint16_t *__restrict__ U, int64_t ldu,
+                                                                    int64_t m, int64_t n, uint16_t *__restrict__ H,
+                                                                    int64_t ldh, int64_t rows_per_chunk,
+                                                                    float *__restrict__ out, int final_sqrt) {
+  __shared__ float red[kWaves][kCols];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * kCols + lane * 8;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
+  const int64_t r1 = r0 + rows_per_chunk < m ? r0 + rows_per_chunk : m;
+  const bool col_ok = c0 < n;   // n % 8 == 0: a chunk is all in or all out
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  if (col_ok) {
+    for (int64_t rb = r0 + wave; rb < r1; rb += kWaves * kUnroll) {
+      uint4 gv[kUnroll], uv[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t r = rb + (int64_t)u * kWaves;
+        if (r < r1) {
+          gv[u] = *reinterpret_cast<const uint4 *>(G + r * ldg + c0);
+          uv[u] = *reinterpret_cast<const uint4 *>(U + r * ldu + c0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t r = rb + (int64_t)u * kWaves;
+        if (r < r1) {
+          uint32_t hw[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t gw = mg::u4get(gv[u], q), uw = mg::u4get(uv[u], q);
+            const float h0 = silu(bf16_lo(gw)) * bf16_lo(uw);
+            const float h1 = silu(bf16_hi(gw)) * bf16_hi(uw);
+            hw[q] = pack_bf16x2(h0, h1);
+            // the scores are of the bf16 values the next product reads
+            const float b0 = bf16_lo(hw[q]), b1 = bf16_hi(hw[q]);
+            acc[2 * q] = fmaf(b0, b0, acc[2 * q]);
+            acc[2 * q + 1] = fmaf(b1, b1, acc[2 * q + 1]);
+          }
+          *reinterpret_cast<uint4 *>(H + r * ldh + c0) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[wave][lane * 8 + e] = acc[e];
+  __syncthreads();
+  // 256 threads finish 512 columns: two each, waves added in order
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = threadIdx.x + h * 64 * kWaves;
+    const int64_t col = (int64_t)blockIdx.x * kCols + c;
+    if (col < n) {
+      const float s = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
+      out[(int64_t)blockIdx.y * n * (1 - final_sqrt) + col] = final_sqrt ? __builtin_sqrtf(s) : s;
+    }
+  }
+}
+
+struct SwigluPlan {
+  int64_t col_tiles, rows_per_chunk, chunks;
+};
+
+SwigluPlan swiglu_plan(int64_t m, int64_t n) {
+  SwigluPlan p;
+  p.col_tiles = ceil_div(n, kCols);
+  // About 4096 blocks, each with at least 64 rows, at most 256 chunks.
+  int64_t chunks = ceil_div(4096, p.col_tiles);
+  const int64_t max_chunks = ceil_div(m, 64);
+  if (chunks > max_chunks) chunks = max_chunks;
+  if (chunks > 256) chunks = 256;
+  if (chunks < 1) chunks = 1;
+  const int64_t step = kWaves * kUnroll;
+  p.rows_per_chunk = ceil_div(ceil_div(m, chunks), step) * step;
+  p.chunks = ceil_div(m, p.rows_per_chunk);
+  return p;
+}
+
+}  // namespace
+
+bool swiglu_ok(const void *G, int64_t ldg, const void *U, int64_t ldu, const void *H, int64_t ldh, int64_t n) {
+  auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  return al(G) && al(U) && al(H) && ldg % 8 == 0 && ldu % 8 == 0 && ldh % 8 == 0 && n % 8 == 0;
+}
+
+size_t swiglu_part_bytes(int64_t m, int64_t n) {
+  const SwigluPlan p = swiglu_plan(m, n);
+  return p.chunks > 1 ? (size_t)p.chunks * (size_t)n * 4 : 0;
+}
+
+hipError_t launch_swiglu_scored(const void *G, int64_t ldg, const void *U, int64_t ldu, int64_t m, int64_t n,
+                                void *H, int64_t ldh, float *scores, float *part, hipStream_t st) {
+  const SwigluPlan p = swiglu_plan(m, n);
+  const bool single = p.chunks == 1;
+  {
+    KernelTimer timer("swiglu_scored", st);
+    hipLaunchKernelGGL(swiglu_scored_kernel, dim3((unsigned)p.col_tiles, (unsigned)p.chunks), dim3(64 * kWaves), 0,
+                       st, static_cast<const uint16_t *>(G), ldg, static_cast<const uint16_t *>(U), ldu, m, n,
+                       static_cast<uint16_t *>(H), ldh, p.rows_per_chunk, single ? scores : part, single ? 1 : 0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || single) return e;
+  }
+  return launch_colnorm_finish(part, p.chunks, n, scores, st);
+}
+
+}  // namespace rmm

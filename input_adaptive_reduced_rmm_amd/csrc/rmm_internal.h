@@ -46,6 +46,17 @@ hipError_t launch_colnorm(rmm_dtype_t dt, const void *A, int64_t m, int64_t d, i
                           const ColnormPlan &p, hipStream_t stream, bool causal = false,
                           int64_t coff = 0, bool stream_loads = false);
 
+// scores[j] = sqrt(sum over c < chunks of part[c][j]) for j < n, chunks added in a fixed order.
+hipError_t launch_colnorm_finish(const float *part, int64_t chunks, int64_t n, float *scores, hipStream_t stream);
+
+// ------------------------------------------------------------------ producer-fused scores
+// H = bf16(silu(G) * U) for bf16 G, U [m][n] and the column scores of H (its
+// bf16 values).  Rows 16-byte aligned, n % 8 == 0.  part: swiglu_part_bytes.
+bool swiglu_ok(const void *G, int64_t ldg, const void *U, int64_t ldu, const void *H, int64_t ldh, int64_t n);
+size_t swiglu_part_bytes(int64_t m, int64_t n);
+hipError_t launch_swiglu_scored(const void *G, int64_t ldg, const void *U, int64_t ldu, int64_t m, int64_t n,
+                                void *H, int64_t ldh, float *scores, float *part, hipStream_t stream);
+
 // ------------------------------------------------------------------ top-k
 hipError_t launch_topk(const float *scores, int64_t batch, int64_t d, int64_t k, int64_t k_pad,
                        int32_t *idx, hipStream_t stream);

@@ -61,6 +61,7 @@ __all__ = [
     "select_top",
     "reduced_product",
     "reduced_product_w8",
+    "swiglu",
     "rmm",
     "kv_head",
     "reduced_qk",
@@ -135,6 +136,19 @@ def reduced_product_w8(A, Bq, scale, I) -> np.ndarray:
     """
     B = np.asarray(Bq, dtype=np.float64) * np.asarray(scale, dtype=np.float64)[None, :]
     return reduced_product(A, B, I)
+
+
+def swiglu(G, U) -> np.ndarray:
+    """silu(G) * U elementwise in float64, silu(x) = x / (1 + e^-x).
+
+    The gated MLP activation of a LLaMA-style layer: the input of the down
+    projection, whose column scores ("Estrategia de Selección") the producer
+    can accumulate as it writes it.
+    """
+    G64 = np.asarray(G, dtype=np.float64)
+    U64 = np.asarray(U, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return G64 / (1.0 + np.exp(-G64)) * U64
 
 
 def rmm(A, B, rho: float):

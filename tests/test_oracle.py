@@ -420,3 +420,20 @@ def test_w8_product_scales_columns_and_drops_rows():
     # keeping every row and unit scales is the integer product
     Yf = O.reduced_product_w8(A, q, np.ones(n, dtype=np.float32), np.arange(d))
     np.testing.assert_allclose(Yf, A @ q.astype(np.int64), rtol=1e-13)
+
+
+def test_swiglu_closed_forms():
+    x = np.array([0.0, math.log(3.0), -math.log(3.0), 50.0, -800.0, 1e-3])
+    s = O.swiglu(x, np.ones_like(x))
+    assert s[0] == 0.0
+    assert s[1] == pytest.approx(0.75 * math.log(3.0), rel=1e-15)      # sigmoid(ln 3) = 3/4
+    assert s[2] == pytest.approx(-0.25 * math.log(3.0), rel=1e-15)     # sigmoid(-ln 3) = 1/4
+    assert s[3] == pytest.approx(50.0, rel=1e-15)
+    assert s[4] == 0.0                                                  # e^800 overflows: x / inf
+    assert s[5] == pytest.approx(1e-3 * 0.5 + 1e-6 / 4, rel=1e-9)      # x sigmoid(x) ~ x/2 + x^2/4
+    rng = np.random.default_rng(21)
+    g = rng.standard_normal(50) * 4
+    # silu(x) - silu(-x) = x, and the up factor multiplies elementwise
+    np.testing.assert_allclose(O.swiglu(g, np.ones(50)) - O.swiglu(-g, np.ones(50)), g, rtol=1e-13, atol=1e-14)
+    u = rng.standard_normal(50)
+    np.testing.assert_allclose(O.swiglu(g, u), O.swiglu(g, np.ones(50)) * u, rtol=1e-15)
