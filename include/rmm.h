@@ -265,6 +265,10 @@ rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, int64_t p
  *   the selections, written as by rmm_topk.
  *   tok_scores (device, float, optional) [Hq][Lk]: the token scores; NULL keeps
  *   them in the workspace.
+ *   o_scores (device, float, optional) [Hq][dh]: column scores of the bf16 O
+ *   over the Lq tokens, o_scores[h][j] = ||O[:, h, j]||_2 - the selection
+ *   scores of the projection that reads O as its [Lq][Hq*dh] input, formed
+ *   while O is written (producer-fused scoring); NULL skips them.
  * S and P are recomputed tile by tile in three passes (row max and sum,
  * column sums of squares, output over the kept tokens); the workspace holds
  * the packed Q[:, I], K[:, I] and the kept keys and values
@@ -277,8 +281,8 @@ rmm_status_t rmm_attention(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, in
                            int64_t kt_head_stride, int64_t ldkt, const void *V, int64_t v_tok_stride,
                            int64_t v_head_stride, int64_t k_feat, int64_t k_tok, int causal, void *O,
                            int64_t o_tok_stride, int64_t o_head_stride, int32_t *idx_feat,
-                           int32_t *idx_tok, float *tok_scores, void *ws, size_t ws_bytes,
-                           rmm_stream_t stream);
+                           int32_t *idx_tok, float *tok_scores, float *o_scores, void *ws,
+                           size_t ws_bytes, rmm_stream_t stream);
 
 /*
  * Per-kernel timing diagnostics (not part of the method; for measurement).

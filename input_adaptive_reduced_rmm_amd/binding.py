@@ -75,7 +75,7 @@ _PROTOS = {
                                    _vp]),
     "rmm_attention": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _vp,
                                      _i64, _i64, _i64, _i64, ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _vp,
-                                     _vp, _sz, _vp]),
+                                     _vp, _vp, _sz, _vp]),
 }
 
 
@@ -351,10 +351,11 @@ def rmm_attention_workspace_bytes(Lq: int, Lk: int, Hq: int, dh: int, k_feat: in
 def rmm_attention(Q: torch.Tensor, Kt: torch.Tensor, V: torch.Tensor, k_feat: int, k_tok: int,
                   O: torch.Tensor | None = None, idx_feat: torch.Tensor | None = None,
                   idx_tok: torch.Tensor | None = None, tok_scores: torch.Tensor | None = None,
-                  ws: torch.Tensor | None = None, causal: bool = True):
+                  ws: torch.Tensor | None = None, causal: bool = True, o_scores: torch.Tensor | None = None):
     """Fused reduced attention.  Q [Lq, Hq, dh], Kt [Hkv, dh, Lk], V [Lk, Hkv, dh] (bf16)
     -> (O bf16 [Lq, Hq, dh], idx_feat int32 [Hq, k_pad(k_feat)], idx_tok int32 [Hq, k_pad(k_tok)]).
-    tok_scores (optional float32 [Hq, Lk]) receives the token scores."""
+    tok_scores (optional float32 [Hq, Lk]) receives the token scores; o_scores (optional
+    float32 [Hq, dh]) the column scores of O for the projection that reads it."""
     lib = load()
     dev = _dev(Q, Kt, V)
     if Q.dtype != torch.bfloat16 or Kt.dtype != torch.bfloat16 or V.dtype != torch.bfloat16:
@@ -375,7 +376,7 @@ def rmm_attention(Q: torch.Tensor, Kt: torch.Tensor, V: torch.Tensor, k_feat: in
     _check(lib.rmm_attention(_ptr(Q), Lq, Hq, dh, Q.stride(0), Q.stride(1), _ptr(Kt), Lk, Hkv, Kt.stride(0),
                              Kt.stride(1), _ptr(V), V.stride(0), V.stride(1), int(k_feat), int(k_tok),
                              1 if causal else 0, _ptr(O), O.stride(0), O.stride(1), _ptr(idx_feat),
-                             _ptr(idx_tok), _ptr(tok_scores), _ptr(ws), wsb, _stream(dev)))
+                             _ptr(idx_tok), _ptr(tok_scores), _ptr(o_scores), _ptr(ws), wsb, _stream(dev)))
     return O, idx_feat, idx_tok
 
 

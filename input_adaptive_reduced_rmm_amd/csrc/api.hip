@@ -472,7 +472,7 @@ RMM_API rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, i
 
 // ------------------------------------------------------------------ fused attention
 struct AttnLayout {
-  size_t sc, part, qi, idxf, ki, stats, tok, kj, vjt, total;
+  size_t sc, part, qi, idxf, ki, stats, tok, kj, vjt, opart, total;
 };
 static AttnLayout attn_layout(int64_t Lq, int64_t Lk, int64_t Hq, int64_t dh, int64_t kf, int64_t kt) {
   const size_t kfp = (size_t)rmm_k_pad(kf), ktp = (size_t)rmm_k_pad(kt);
@@ -487,6 +487,7 @@ static AttnLayout attn_layout(int64_t Lq, int64_t Lk, int64_t Hq, int64_t dh, in
   L.tok = c.off;  c.take((size_t)Hq * Lk * 4);
   L.kj = c.off;   c.take((size_t)Hq * ktp * kfp * 2);
   L.vjt = c.off;  c.take((size_t)Hq * dh * ktp * 2);
+  L.opart = c.off; c.take((size_t)((Lq + 255) / 256) * Hq * dh * 4);
   L.total = c.off;
   return L;
 }
@@ -502,8 +503,8 @@ RMM_API rmm_status_t rmm_attention(const void *Q, int64_t Lq, int64_t Hq, int64_
                                    int64_t kt_head_stride, int64_t ldkt, const void *V, int64_t v_tok_stride,
                                    int64_t v_head_stride, int64_t k_feat, int64_t k_tok, int causal, void *O,
                                    int64_t o_tok_stride, int64_t o_head_stride, int32_t *idx_feat,
-                                   int32_t *idx_tok, float *tok_scores, void *ws, size_t ws_bytes,
-                                   rmm_stream_t stream) {
+                                   int32_t *idx_tok, float *tok_scores, float *o_scores, void *ws,
+                                   size_t ws_bytes, rmm_stream_t stream) {
   if (!Q || !Kt || !V || !O || !idx_feat || !idx_tok) return fail(RMM_ERR_INVALID_ARG, "attention: NULL pointer");
   if (Lq < 1 || Lk < 1 || dh < 1 || Lk >= kMaxDim || Lq >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "attention: bad Lq, Lk or dh");
   if (Hq < 1 || Hq > kMaxBatch || Hkv < 1 || Hkv > Hq || Hq % Hkv != 0)
@@ -515,7 +516,7 @@ RMM_API rmm_status_t rmm_attention(const void *Q, int64_t Lq, int64_t Hq, int64_
       kt_head_stride < 0 || v_head_stride < 0 || o_head_stride < 0)
     return fail(RMM_ERR_INVALID_ARG, "attention: bad stride");
   if (!aligned(Q, 2) || !aligned(Kt, 2) || !aligned(V, 2) || !aligned(O, 2) || !aligned(idx_feat, 4) ||
-      !aligned(idx_tok, 4) || (tok_scores && !aligned(tok_scores, 4)))
+      !aligned(idx_tok, 4) || (tok_scores && !aligned(tok_scores, 4)) || (o_scores && !aligned(o_scores, 4)))
     return fail(RMM_ERR_INVALID_ARG, "attention: misaligned pointer");
   const int64_t kfp = rmm_k_pad(k_feat), ktp = rmm_k_pad(k_tok);
   if (!rmm::attn_supported(dh, kfp)) return fail(RMM_ERR_UNSUPPORTED, "attention: needs dh == 128");
@@ -560,6 +561,7 @@ RMM_API rmm_status_t rmm_attention(const void *Q, int64_t Lq, int64_t Hq, int64_
     d.n2ml = st2 + Hq * Lq;
   }
   d.tok = tok;
+  d.opart = o_scores ? reinterpret_cast<float *>(w + L.opart) : nullptr;
   d.O = O;
   d.o_ts = o_tok_stride;
   d.o_hs = o_head_stride;
@@ -586,5 +588,8 @@ RMM_API rmm_status_t rmm_attention(const void *Q, int64_t Lq, int64_t Hq, int64_
                              dh * ktp, st);
     if (he != hipSuccess) return hip_status(he, "attention value pack launch");
   }
-  return hip_status(rmm::launch_attn_passes(3, d, st), "attention output launch");
+  he = rmm::launch_attn_passes(3, d, st);
+  if (he != hipSuccess || !o_scores) return hip_status(he, "attention output launch");
+  return hip_status(rmm::launch_colnorm_finish(d.opart, (Lq + 255) / 256, Hq * dh, o_scores, st),
+                    "attention output scores launch");
 }

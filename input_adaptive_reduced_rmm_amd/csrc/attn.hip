@@ -52,6 +52,7 @@ struct AttnArgs {
   float *nml;           // [hq][Lq] -(row max of c S) - log2(row sum): P = 2^(c S + nml)
   float *n2ml;          // [hq][Lq] 2 nml: P^2 = 2^(2 c S + n2ml)
   float *tok;           // [hq][Lk] token scores
+  float *opart;         // [blocks_q][hq][128] column sums of O^2 per row block, or null
   uint16_t *O;          // [Lq tokens of o_ts] x [hq of o_hs] x dh
   int64_t o_ts, o_hs;
   int64_t hq, Lq, Lk, kt, kt_pad;
@@ -121,6 +122,29 @@ __device__ __forceinline__ void load_row_frags(const uint16_t *base, int64_t nro
   for (int ks = 0; ks < KF / 16; ++ks)
     f[ks] = __builtin_bit_cast(bf16x8_t,
                                mg::bload16(r, (uint32_t)((row * KF + ks * 16 + (lane >> 5) * 8) * 2)));
+}
+
+// Column sums of squares of the bf16 output over this workgroup's queries
+// (producer-fused scores for the projection that reads O): lanes add the
+// squares of the values they store, the two lane halves and then the waves
+// are added in order, and one partial per (row block, head, column) is
+// written; colnorm_finish adds the row blocks.
+template <int NW>
+__device__ __forceinline__ void out_col_partials(float (&cs)[4], int wave, int lane, float *red, float *dst) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) cs[dt] += __shfl_xor(cs[dt], 32, 64);
+  if (lane < 32) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) red[wave * 128 + dt * 32 + lane] = cs[dt];
+  }
+  __syncthreads();
+  const int t = wave * 64 + lane;
+  if (t < 128) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s += red[w * 128 + t];
+    dst[t] = s;
+  }
 }
 
 // ---------------------------------------------------------------- pass A
@@ -432,13 +456,24 @@ __global__ __launch_bounds__(kThreads) void attn_out_kernel(AttnArgs g) {
   }
   // acc_o[dt]: lane holds column d = dt*32 + l%32 and queries q0 + 8*(r/4) + 4*(l/32) + r%4
   uint16_t *Oh = g.O + h * g.o_hs;
+  float cs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t q = q0 + 8 * (r >> 2) + 4 * lk + (r & 3);
-      if (q < g.Lq) Oh[q * g.o_ts + dt * 32 + (lane & 31)] = f32_to_bf16(acc_o[dt][r]);
+      if (q < g.Lq) {
+        const uint16_t b = f32_to_bf16(acc_o[dt][r]);
+        Oh[q * g.o_ts + dt * 32 + (lane & 31)] = b;
+        const float v = bf16_to_f32(b);
+        cs[dt] = fmaf(v, v, cs[dt]);
+      }
     }
+  if (g.opart) {
+    __syncthreads();   // the tile stages are free: reuse them for the wave sums
+    out_col_partials<kWaves>(cs, wave, lane, reinterpret_cast<float *>(smem),
+                             g.opart + (qb * g.hq + h) * 128);
+  }
 }
 
 // ---------------------------------------------------------------- pass D, 64 queries per wave
@@ -607,6 +642,7 @@ __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(RMM_A
     __syncthreads();
   }
   uint16_t *Oh = g.O + h * g.o_hs;
+  float cs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int gq = 0; gq < 2; ++gq)
 #pragma unroll
@@ -614,8 +650,18 @@ __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(RMM_A
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t q = q0 + 32 * gq + 8 * (r >> 2) + 4 * lk + (r & 3);
-        if (q < g.Lq) Oh[q * g.o_ts + dt * 32 + (lane & 31)] = f32_to_bf16(acc_o[gq][dt][r]);
+        if (q < g.Lq) {
+          const uint16_t b = f32_to_bf16(acc_o[gq][dt][r]);
+          Oh[q * g.o_ts + dt * 32 + (lane & 31)] = b;
+          const float v = bf16_to_f32(b);
+          cs[dt] = fmaf(v, v, cs[dt]);
+        }
       }
+  if (g.opart) {
+    __syncthreads();   // the tile stages are free: reuse them for the wave sums
+    out_col_partials<kWaves2>(cs, wave, lane, reinterpret_cast<float *>(smem),
+                              g.opart + (qb * g.hq + h) * 128);
+  }
 }
 
 // Rows of K_I gathered by the kept tokens: KJ[h][j] = KI[h][J[h][j]] (zero rows
@@ -649,6 +695,7 @@ hipError_t launch_attn_passes(int pass, const AttnDesc &d, hipStream_t st) {
   g.nml = d.nml;
   g.n2ml = d.n2ml;
   g.tok = d.tok;
+  g.opart = d.opart;
   g.O = static_cast<uint16_t *>(d.O);
   g.o_ts = d.o_ts;
   g.o_hs = d.o_hs;

@@ -135,6 +135,7 @@ struct AttnDesc {
   const int32_t *J;      // [hq][kt_pad]
   float *nml, *n2ml;     // [hq][Lq] -(row max of c S) - log2(row sum), and twice that
   float *tok;            // [hq][Lk]
+  float *opart;          // [ceil(Lq/256)][hq][128] column sums of O^2 per 256-query block, or null
   void *O;               // bf16, [Lq tokens of o_ts] x [hq of o_hs] x dh
   int64_t o_ts, o_hs;
   int64_t hq, Lq, Lk, dh, kf_pad, kt, kt_pad;

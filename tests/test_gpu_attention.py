@@ -13,7 +13,9 @@ P[:, J] V[J, :] without ever writing S or P.  Checks, per head:
   an absolute floor of 1e-6 of the largest score (float32 exponentials
   underflow where float64 ones do not);
 * O matches the oracle's P[:, J] V[J, :] (with the GPU's J) to the bf16
-  relative Frobenius bound 1e-2; P enters the product rounded to bf16.
+  relative Frobenius bound 1e-2; P enters the product rounded to bf16;
+* the column scores of O returned with it (for the projection that reads O)
+  match the oracle's column norms of the bf16 O to a relative 1e-5.
 """
 import math
 
@@ -43,12 +45,16 @@ def _run(Q, Kt, V, kf, kt, causal, ws_fill=None):
     Lk = Kt.shape[2]
     Qd, Ktd, Vd = (dev_tensor(x, torch.bfloat16) for x in (Q, Kt, V))
     ts = torch.full((Hq, Lk), float("nan"), dtype=torch.float32, device=DEV)
+    os_ = torch.full((Hq, dh), float("nan"), dtype=torch.float32, device=DEV)
     ws = torch.empty(R.rmm_attention_workspace_bytes(Lq, Lk, Hq, dh, kf, kt), dtype=torch.uint8, device=DEV)
     if ws_fill is not None:
         ws.fill_(ws_fill)
-    O, I, J = R.rmm_attention(Qd, Ktd, Vd, kf, kt, tok_scores=ts, ws=ws, causal=causal)
+    O, I, J = R.rmm_attention(Qd, Ktd, Vd, kf, kt, tok_scores=ts, ws=ws, causal=causal, o_scores=os_)
     fs = R.rmm_colnorm(Qd.permute(1, 0, 2))          # the feature scores the call selected on
     torch.cuda.synchronize()
+    # column scores of O for the projection that reads it, against the bf16 O written
+    On = O.float().cpu().numpy().astype(np.float64).reshape(Lq, Hq * dh)
+    np.testing.assert_allclose(os_.cpu().numpy().reshape(-1), oracle.column_scores(On), rtol=1e-5, atol=1e-30)
     return O, I, J, ts, fs
 
 
