@@ -492,10 +492,35 @@ static AttnLayout attn_layout(int64_t Lq, int64_t Lk, int64_t Hq, int64_t dh, in
   return L;
 }
 
+// Few queries (decode steps): the scores S of every key instead of packed
+// operands.  Both layouts start at offset 0; the query returns the larger.
+struct AttnDecLayout {
+  size_t sc, part, S, pstat, nml, tok, opart, total;
+};
+static AttnDecLayout attn_dec_layout(int64_t Lq, int64_t Lk, int64_t Hq, int64_t dh, int64_t kt) {
+  const rmm::AttnDecodeSizes z = rmm::attn_decode_sizes(Lq, Lk, Hq, kt);
+  AttnDecLayout L;
+  Carve c(nullptr);
+  L.sc = c.off;    c.take((size_t)Hq * dh * 4);
+  L.part = c.off;  c.take(colnorm_ws(RMM_BF16, Lq, dh, Hq));
+  L.S = c.off;     c.take(z.s_bytes);
+  L.pstat = c.off; c.take(z.pstat_bytes);
+  L.nml = c.off;   c.take(z.nml_bytes);
+  L.tok = c.off;   c.take((size_t)Hq * Lk * 4);
+  L.opart = c.off; c.take(z.opart_bytes);
+  L.total = c.off;
+  return L;
+}
+
 RMM_API size_t rmm_attention_workspace_bytes(int64_t Lq, int64_t Lk, int64_t Hq, int64_t dh, int64_t k_feat,
                                              int64_t k_tok) {
   if (Lq < 1 || Lk < 1 || Hq < 1 || dh < 1 || k_feat < 1 || k_tok < 1) return 0;
-  return attn_layout(Lq, Lk, Hq, dh, k_feat, k_tok).total;
+  size_t t = attn_layout(Lq, Lk, Hq, dh, k_feat, k_tok).total;
+  if (rmm::attn_decode_ok(Lq, dh)) {
+    const size_t td = attn_dec_layout(Lq, Lk, Hq, dh, k_tok).total;
+    if (td > t) t = td;
+  }
+  return t;
 }
 
 RMM_API rmm_status_t rmm_attention(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, int64_t q_tok_stride,
@@ -524,11 +549,62 @@ RMM_API rmm_status_t rmm_attention(const void *Q, int64_t Lq, int64_t Hq, int64_
       (uint64_t)((Lk - 1) * v_tok_stride + dh) * 2 >= rmm::mg::kMaxRecords ||
       (uint64_t)Lk * kfp * 2 >= rmm::mg::kMaxRecords)
     return fail(RMM_ERR_UNSUPPORTED, "attention: a key or value head spans 4 GiB or more");
-  const AttnLayout L = attn_layout(Lq, Lk, Hq, dh, k_feat, k_tok);
-  if (!ws || ws_bytes < L.total || !aligned(ws, 256))
-    return fail(RMM_ERR_WORKSPACE, "attention: workspace needs %zu bytes (256-byte aligned)", L.total);
+  const size_t need = rmm_attention_workspace_bytes(Lq, Lk, Hq, dh, k_feat, k_tok);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(RMM_ERR_WORKSPACE, "attention: workspace needs %zu bytes (256-byte aligned)", need);
   char *w = static_cast<char *>(ws);
   hipStream_t st = (hipStream_t)stream;
+  if (rmm::attn_decode_ok(Lq, dh) && aligned(V, 16) && v_tok_stride % 8 == 0 && v_head_stride % 8 == 0) {
+    // a few queries after a long context: passes split over keys
+    const AttnDecLayout D = attn_dec_layout(Lq, Lk, Hq, dh, k_tok);
+    float *tokd = tok_scores ? tok_scores : reinterpret_cast<float *>(w + D.tok);
+    const rmm::ColnormPlan p = plan_for(RMM_BF16, Q, Lq, dh, q_tok_stride, Hq, q_head_stride);
+    hipError_t he = rmm::launch_colnorm(RMM_BF16, Q, Lq, dh, q_tok_stride, Hq, q_head_stride,
+                                        reinterpret_cast<float *>(w + D.sc), w + D.part, p, st);
+    if (he != hipSuccess) return hip_status(he, "attention colnorm launch");
+    he = rmm::launch_topk(reinterpret_cast<float *>(w + D.sc), Hq, dh, k_feat, kfp, idx_feat, st);
+    if (he != hipSuccess) return hip_status(he, "attention topk launch");
+    rmm::AttnDecodeDesc dd{};
+    dd.Q = Q;
+    dd.q_ts = q_tok_stride;
+    dd.q_hs = q_head_stride;
+    dd.Kt = Kt;
+    dd.kt_hs = kt_head_stride;
+    dd.ldkt = ldkt;
+    dd.V = V;
+    dd.v_ts = v_tok_stride;
+    dd.v_hs = v_head_stride;
+    dd.I = idx_feat;
+    dd.J = idx_tok;
+    dd.S = reinterpret_cast<float *>(w + D.S);
+    dd.pstat = reinterpret_cast<float *>(w + D.pstat);
+    dd.nml = reinterpret_cast<float *>(w + D.nml);
+    dd.tok = tokd;
+    dd.opart = reinterpret_cast<float *>(w + D.opart);
+    dd.O = O;
+    dd.o_ts = o_tok_stride;
+    dd.o_hs = o_head_stride;
+    dd.o_scores = o_scores;
+    dd.hq = Hq;
+    dd.hkv = Hkv;
+    dd.Lq = Lq;
+    dd.Lk = Lk;
+    dd.kf = k_feat;
+    dd.kf_pad = kfp;
+    dd.kt = k_tok;
+    dd.kt_pad = ktp;
+    dd.causal = causal != 0;
+    he = rmm::launch_attn_decode(0, dd, st);
+    if (he != hipSuccess) return hip_status(he, "attention scores launch");
+    he = rmm::launch_attn_decode(1, dd, st);
+    if (he != hipSuccess) return hip_status(he, "attention token scores launch");
+    he = rmm::launch_topk(tokd, Hq, Lk, k_tok, ktp, idx_tok, st);
+    if (he != hipSuccess) return hip_status(he, "attention token topk launch");
+    he = rmm::launch_attn_decode(2, dd, st);
+    if (he != hipSuccess) return hip_status(he, "attention output launch");
+    return hip_status(rmm::launch_attn_decode(3, dd, st), "attention output merge launch");
+  }
+  const AttnLayout L = attn_layout(Lq, Lk, Hq, dh, k_feat, k_tok);
   float *tok = tok_scores ? tok_scores : reinterpret_cast<float *>(w + L.tok);
   int32_t *idx_clean = reinterpret_cast<int32_t *>(w + L.idxf);
 

@@ -1,0 +1,401 @@
+// Reduced attention for a few new tokens after a long context (decode steps,
+// Lq <= 16): the same computation as the fused path in attn.hip - features of
+// Q selected by column norm, S = Q[:, I] K[I, :], causal softmax, tokens
+// selected by the column norms of P, O = P[:, J] V[J, :] ("Alcance de
+// Aplicación", "Estrategia de Selección") - organised for Lq << Lk.
+//
+// With so few query rows the work is reading the kept feature rows of K and
+// the kept token rows of V once, so every pass is split over keys (or kept
+// tokens) across many workgroups per head instead of over query blocks:
+//   dec_scores  S[i][j] for all keys, straight from the feature-major K
+//               (each kept feature row of a 256-key block is 512 contiguous
+//               bytes), written to the workspace (Lq x Lk floats per head),
+//               with each block's per-query max and sum of 2^(c (S - max));
+//   dec_tok     merges those partial statistics and writes the token scores
+//               sqrt(sum_i P_ij^2), P_ij = 2^(c S_ij + nml_i);
+//   top-k       per head over the Lk token scores;
+//   dec_out     per block of 256 kept tokens: P_ij from S, the kept V rows
+//               (16-byte loads), partial O sums per (block, head);
+//   dec_merge   adds the partial O in block order, rounds to bf16 and (when
+//               asked) forms the column scores of O.
+// Everything is float32 except the bf16 inputs and O; all sums run in a fixed
+// order, so results are deterministic.
+#include "rmm_internal.h"
+#include "timing.h"
+
+namespace rmm {
+namespace {
+
+constexpr int kDB = 256;   // keys (or kept tokens) per workgroup pass, one per thread
+#ifndef RMM_DEC_TOKSUB
+#define RMM_DEC_TOKSUB 1
+#endif
+constexpr int kTokSub = RMM_DEC_TOKSUB;   // 256-token sub-tiles per output workgroup
+constexpr float kNegInfD = -__builtin_inff();
+
+__device__ __forceinline__ float dexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct DecArgs {
+  const uint16_t *Q;      // element (i, h, f) at Q + i*q_ts + h*q_hs + f
+  int64_t q_ts, q_hs;
+  const uint16_t *Kt;     // element (g, f, j) at Kt + g*kt_hs + f*ldkt + j
+  int64_t kt_hs, ldkt;
+  const uint16_t *V;      // element (j, g, d) at V + j*v_ts + g*v_hs + d
+  int64_t v_ts, v_hs;
+  const int32_t *I;       // [hq][kf_pad] kept features, ascending
+  const int32_t *J;       // [hq][kt_pad] kept tokens, ascending
+  float *S;               // [hq][Lq][Lk]
+  float2 *pstat;          // [hq][nblk][Lq] (block max of S, sum of 2^(c (S - max)))
+  float *nml;             // [hq][Lq]
+  float *tok;             // [hq][Lk]
+  float *opart;           // [nsplit][hq][Lq][128]
+  uint16_t *O;            // element (i, h, d) at O + i*o_ts + h*o_hs + d
+  int64_t o_ts, o_hs;
+  float *o_scores;        // [hq][128] or null
+  int64_t hq, hkv, Lq, Lk, kf, kf_pad, kt, kt_pad, off;
+  int causal, nblk, nsplit;
+  float c2;
+};
+
+// Block-wide reduction of LQ values per thread (max or sum); returns the result
+// to every thread.  red: LDS scratch of 4 * LQ floats.
+template <int LQ, bool MAX>
+__device__ __forceinline__ void block_reduce(float (&v)[LQ], float *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < LQ; ++i) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float w = __shfl_xor(v[i], o, 64);
+      v[i] = MAX ? fmaxf(v[i], w) : v[i] + w;
+    }
+  }
+  __syncthreads();
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < LQ; ++i) red[wave * LQ + i] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < LQ; ++i) {
+    const float a = red[i], b = red[LQ + i], c = red[2 * LQ + i], d = red[3 * LQ + i];
+    v[i] = MAX ? fmaxf(fmaxf(a, b), fmaxf(c, d)) : (a + b) + (c + d);
+  }
+}
+
+template <int LQ>
+__global__ __launch_bounds__(kDB) void dec_scores_kernel(DecArgs g) {
+  __shared__ int32_t sI[128];
+  __shared__ __attribute__((aligned(16))) float sq[LQ][128];
+  __shared__ float red[4 * LQ];
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x;
+  const int64_t h = blockIdx.y, grp = h * g.hkv / g.hq;
+  const int Lq = (int)g.Lq, kf = (int)g.kf;
+  if (tid < 128) sI[tid] = tid < kf ? g.I[h * g.kf_pad + tid] : 0;
+  __syncthreads();
+  for (int e = tid; e < LQ * 128; e += kDB) {
+    const int i = e / 128, f = e % 128;
+    sq[i][f] = (i < Lq && f < kf) ? bf16_to_f32(g.Q[i * g.q_ts + h * g.q_hs + sI[f]]) : 0.f;
+  }
+  __syncthreads();
+  const int64_t j = (int64_t)blk * kDB + tid;
+  float s[LQ];
+#pragma unroll
+  for (int i = 0; i < LQ; ++i) s[i] = 0.f;
+  if (j < g.Lk) {
+    const uint16_t *kb = g.Kt + grp * g.kt_hs + j;
+    int f = 0;
+    for (; f + 8 <= kf; f += 8) {
+      float kv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kv[u] = bf16_to_f32(kb[(int64_t)sI[f + u] * g.ldkt]);
+#pragma unroll
+      for (int i = 0; i < LQ; ++i) {
+        // two 16-byte LDS reads (broadcast) per query row and 8 features
+        const float4 qa = *reinterpret_cast<const float4 *>(&sq[i][f]);
+        const float4 qb = *reinterpret_cast<const float4 *>(&sq[i][f + 4]);
+        s[i] = fmaf(qa.x, kv[0], s[i]);
+        s[i] = fmaf(qa.y, kv[1], s[i]);
+        s[i] = fmaf(qa.z, kv[2], s[i]);
+        s[i] = fmaf(qa.w, kv[3], s[i]);
+        s[i] = fmaf(qb.x, kv[4], s[i]);
+        s[i] = fmaf(qb.y, kv[5], s[i]);
+        s[i] = fmaf(qb.z, kv[6], s[i]);
+        s[i] = fmaf(qb.w, kv[7], s[i]);
+      }
+    }
+    for (; f < kf; ++f) {
+      const float kv = bf16_to_f32(kb[(int64_t)sI[f] * g.ldkt]);
+#pragma unroll
+      for (int i = 0; i < LQ; ++i) s[i] = fmaf(sq[i][f], kv, s[i]);
+    }
+  }
+  // masked scores are -inf: they add nothing to any later sum
+#pragma unroll
+  for (int i = 0; i < LQ; ++i) {
+    const bool vis = j < g.Lk && i < Lq && (!g.causal || j <= i + g.off);
+    s[i] = vis ? s[i] : kNegInfD;
+    if (i < Lq && j < g.Lk) g.S[(h * g.Lq + i) * g.Lk + j] = s[i];
+  }
+  float m[LQ];
+#pragma unroll
+  for (int i = 0; i < LQ; ++i) m[i] = s[i];
+  block_reduce<LQ, true>(m, red);
+  float l[LQ];
+#pragma unroll
+  for (int i = 0; i < LQ; ++i) l[i] = m[i] == kNegInfD ? 0.f : dexp2((s[i] - m[i]) * g.c2);
+  block_reduce<LQ, false>(l, red);
+  if (tid < Lq) {
+    float mv = m[0], lv = l[0];
+#pragma unroll
+    for (int i = 1; i < LQ; ++i)
+      if (tid == i) { mv = m[i]; lv = l[i]; }
+    g.pstat[(h * g.nblk + blk) * g.Lq + tid] = make_float2(mv, lv);
+  }
+}
+
+// Merge the key blocks' statistics of head h: every thread takes the blocks
+// b = tid, tid + 256, ... (loads independent of each other), then block-wide
+// max and sum in a fixed order.  Returns nml_i = -c max_i - log2(sum_i).
+template <int LQ>
+__device__ __forceinline__ void merge_stats(const DecArgs &g, int64_t h, float (&nml)[LQ], float *red) {
+  const int tid = threadIdx.x, Lq = (int)g.Lq;
+  float M[LQ], L[LQ];
+#pragma unroll
+  for (int i = 0; i < LQ; ++i) M[i] = kNegInfD;
+  for (int b = tid; b < g.nblk; b += kDB)
+#pragma unroll
+    for (int i = 0; i < LQ; ++i)
+      if (i < Lq) M[i] = fmaxf(M[i], g.pstat[(h * g.nblk + b) * g.Lq + i].x);
+  block_reduce<LQ, true>(M, red);
+#pragma unroll
+  for (int i = 0; i < LQ; ++i) L[i] = 0.f;
+  for (int b = tid; b < g.nblk; b += kDB)
+#pragma unroll
+    for (int i = 0; i < LQ; ++i)
+      if (i < Lq) {
+        const float2 p = g.pstat[(h * g.nblk + b) * g.Lq + i];
+        if (p.x != kNegInfD) L[i] += p.y * dexp2((p.x - M[i]) * g.c2);
+      }
+  block_reduce<LQ, false>(L, red);
+#pragma unroll
+  for (int i = 0; i < LQ; ++i) nml[i] = (i < Lq && L[i] > 0.f) ? -M[i] * g.c2 - log2f(L[i]) : kNegInfD;
+}
+
+template <int LQ>
+__global__ __launch_bounds__(kDB) void dec_tok_kernel(DecArgs g) {
+  __shared__ float red[4 * LQ];
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x;
+  const int64_t h = blockIdx.y;
+  const int Lq = (int)g.Lq;
+  float snml[LQ];
+  merge_stats<LQ>(g, h, snml, red);
+  if (blk == 0 && tid < Lq) {
+    float v = snml[0];
+#pragma unroll
+    for (int i = 1; i < LQ; ++i)
+      if (tid == i) v = snml[i];
+    g.nml[h * g.Lq + tid] = v;
+  }
+  const int64_t j = (int64_t)blk * kDB + tid;
+  if (j >= g.Lk) return;
+  const float c4 = 2.f * g.c2;
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < LQ; ++i)
+    if (i < Lq) {
+      const float sv = g.S[(h * g.Lq + i) * g.Lk + j];
+      if (sv != kNegInfD) t += dexp2(fmaf(sv, c4, 2.f * snml[i]));
+    }
+  g.tok[h * g.Lk + j] = __builtin_sqrtf(t);
+}
+
+template <int LQ>
+__global__ __launch_bounds__(kDB) void dec_out_kernel(DecArgs g) {
+  __shared__ int32_t sj[kDB];
+  __shared__ float sp[kDB][LQ];
+  __shared__ float red[4][LQ * 128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = blockIdx.x;
+  const int64_t h = blockIdx.y, grp = h * g.hkv / g.hq;
+  const int Lq = (int)g.Lq;
+  float nmli[LQ];
+#pragma unroll
+  for (int i = 0; i < LQ; ++i) nmli[i] = i < Lq ? g.nml[h * g.Lq + i] : kNegInfD;
+  // thread: 8 output columns (dq) of 16 token lanes (tg); tokens tg, tg+16, ...
+  const int dq = tid & 15, tg = tid >> 4;
+  float acc[LQ][8];
+#pragma unroll
+  for (int i = 0; i < LQ; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+  for (int sub = 0; sub < kTokSub; ++sub) {
+    const int64_t t0 = ((int64_t)split * kTokSub + sub) * kDB;
+    if (t0 >= g.kt) break;
+    const int ntok = (int)(g.kt - t0 < kDB ? g.kt - t0 : kDB);
+    if (sub > 0) __syncthreads();   // the previous sub-tile's p and rows are consumed
+    {
+      const int32_t jt = tid < ntok ? g.J[h * g.kt_pad + t0 + tid] : -1;
+      sj[tid] = jt;
+#pragma unroll
+      for (int i = 0; i < LQ; ++i) {
+        float p = 0.f;
+        if (jt >= 0 && i < Lq) {
+          const float sv = g.S[(h * g.Lq + i) * g.Lk + jt];
+          if (sv != kNegInfD) p = dexp2(fmaf(sv, g.c2, nmli[i]));
+        }
+        sp[tid][i] = p;
+      }
+    }
+    __syncthreads();
+    for (int tt = tg; tt < ntok; tt += 16) {
+      const int32_t row = sj[tt];
+      if (row < 0) continue;
+      const uint4 v = *reinterpret_cast<const uint4 *>(g.V + (int64_t)row * g.v_ts + grp * g.v_hs + dq * 8);
+      const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                           bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+      for (int i = 0; i < LQ; ++i) {
+        const float p = sp[tt][i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(p, vf[e], acc[i][e]);
+      }
+    }
+  }
+  // add the four token lanes of a wave (lane bits 4 and 5), then the waves
+#pragma unroll
+  for (int i = 0; i < LQ; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[i][e] += __shfl_xor(acc[i][e], 16, 64);
+      acc[i][e] += __shfl_xor(acc[i][e], 32, 64);
+    }
+  if (lane < 16) {
+#pragma unroll
+    for (int i = 0; i < LQ; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[wave][i * 128 + dq * 8 + e] = acc[i][e];
+  }
+  __syncthreads();
+  float *dst = g.opart + ((int64_t)split * g.hq + h) * g.Lq * 128;
+  for (int e = tid; e < Lq * 128; e += kDB) dst[e] = (red[0][e] + red[1][e]) + (red[2][e] + red[3][e]);
+}
+
+// Block per (head, 32 columns): O = sum of the split partials in split order
+// (eight loads in flight), rounded to bf16; o_scores[h][d] = norm over the Lq
+// rows of that bf16 O, rows added in order.
+__global__ __launch_bounds__(256) void dec_merge_kernel(DecArgs g) {
+  __shared__ float sq[16][32];
+  const int64_t h = blockIdx.x;
+  const int d0 = blockIdx.y * 32;
+  const int Lq = (int)g.Lq;
+  for (int e = threadIdx.x; e < Lq * 32; e += 256) {
+    const int i = e / 32, d = d0 + e % 32;
+    const float *p = g.opart + (h * g.Lq + i) * 128 + d;
+    const int64_t stride = g.hq * g.Lq * 128;
+    float s = 0.f;
+    int sp = 0;
+    for (; sp + 8 <= g.nsplit; sp += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(sp + u) * stride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; sp < g.nsplit; ++sp) s += p[(int64_t)sp * stride];
+    const uint16_t b = f32_to_bf16(s);
+    g.O[i * g.o_ts + h * g.o_hs + d] = b;
+    const float v = bf16_to_f32(b);
+    sq[i][e % 32] = v * v;
+  }
+  if (!g.o_scores) return;
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    float cs = 0.f;
+    for (int i = 0; i < Lq; ++i) cs += sq[i][threadIdx.x];
+    g.o_scores[h * 128 + d0 + threadIdx.x] = __builtin_sqrtf(cs);
+  }
+}
+
+}  // namespace
+
+bool attn_decode_ok(int64_t Lq, int64_t dh) { return Lq >= 1 && Lq <= 16 && dh == 128; }
+
+AttnDecodeSizes attn_decode_sizes(int64_t Lq, int64_t Lk, int64_t Hq, int64_t kt) {
+  AttnDecodeSizes z;
+  z.nblk = (int)ceil_div(Lk, kDB);
+  z.nsplit = (int)ceil_div(kt, kDB * kTokSub);
+  z.s_bytes = (size_t)Hq * Lq * Lk * 4;
+  z.pstat_bytes = (size_t)Hq * z.nblk * Lq * 8;
+  z.nml_bytes = (size_t)Hq * Lq * 4;
+  z.opart_bytes = (size_t)z.nsplit * Hq * Lq * 128 * 4;
+  return z;
+}
+
+#define RMM_DEC_LAUNCH(KERNEL, LQV, GRID, ARGS, ST)                                                  \
+  do {                                                                                              \
+    switch (LQV) {                                                                                  \
+      case 1: hipLaunchKernelGGL(KERNEL<1>, GRID, dim3(kDB), 0, ST, ARGS); break;                   \
+      case 2: hipLaunchKernelGGL(KERNEL<2>, GRID, dim3(kDB), 0, ST, ARGS); break;                   \
+      case 4: hipLaunchKernelGGL(KERNEL<4>, GRID, dim3(kDB), 0, ST, ARGS); break;                   \
+      case 8: hipLaunchKernelGGL(KERNEL<8>, GRID, dim3(kDB), 0, ST, ARGS); break;                   \
+      default: hipLaunchKernelGGL(KERNEL<16>, GRID, dim3(kDB), 0, ST, ARGS); break;                 \
+    }                                                                                               \
+  } while (0)
+
+hipError_t launch_attn_decode(int pass, const AttnDecodeDesc &d, hipStream_t st) {
+  DecArgs g{};
+  g.Q = static_cast<const uint16_t *>(d.Q);
+  g.q_ts = d.q_ts;
+  g.q_hs = d.q_hs;
+  g.Kt = static_cast<const uint16_t *>(d.Kt);
+  g.kt_hs = d.kt_hs;
+  g.ldkt = d.ldkt;
+  g.V = static_cast<const uint16_t *>(d.V);
+  g.v_ts = d.v_ts;
+  g.v_hs = d.v_hs;
+  g.I = d.I;
+  g.J = d.J;
+  g.S = d.S;
+  g.pstat = reinterpret_cast<float2 *>(d.pstat);
+  g.nml = d.nml;
+  g.tok = d.tok;
+  g.opart = d.opart;
+  g.O = static_cast<uint16_t *>(d.O);
+  g.o_ts = d.o_ts;
+  g.o_hs = d.o_hs;
+  g.o_scores = d.o_scores;
+  g.hq = d.hq;
+  g.hkv = d.hkv;
+  g.Lq = d.Lq;
+  g.Lk = d.Lk;
+  g.kf = d.kf;
+  g.kf_pad = d.kf_pad;
+  g.kt = d.kt;
+  g.kt_pad = d.kt_pad;
+  g.off = d.Lk - d.Lq;
+  g.causal = d.causal ? 1 : 0;
+  const AttnDecodeSizes z = attn_decode_sizes(d.Lq, d.Lk, d.hq, d.kt);
+  g.nblk = z.nblk;
+  g.nsplit = z.nsplit;
+  g.c2 = (float)(1.4426950408889634 / __builtin_sqrt(128.0));
+  const int lq = d.Lq <= 1 ? 1 : d.Lq <= 2 ? 2 : d.Lq <= 4 ? 4 : d.Lq <= 8 ? 8 : 16;
+  if (pass == 0) {
+    KernelTimer timer("dec_scores", st);
+    RMM_DEC_LAUNCH(dec_scores_kernel, lq, dim3((unsigned)z.nblk, (unsigned)d.hq), g, st);
+  } else if (pass == 1) {
+    KernelTimer timer("dec_tok", st);
+    RMM_DEC_LAUNCH(dec_tok_kernel, lq, dim3((unsigned)z.nblk, (unsigned)d.hq), g, st);
+  } else if (pass == 2) {
+    KernelTimer timer("dec_out", st);
+    RMM_DEC_LAUNCH(dec_out_kernel, lq, dim3((unsigned)z.nsplit, (unsigned)d.hq), g, st);
+  } else {
+    KernelTimer timer("dec_merge", st);
+    hipLaunchKernelGGL(dec_merge_kernel, dim3((unsigned)d.hq, 4), dim3(256), 0, st, g);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rmm

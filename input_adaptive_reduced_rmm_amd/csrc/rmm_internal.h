@@ -145,4 +145,28 @@ bool attn_supported(int64_t dh, int64_t kf_pad);
 // pass 0: row statistics, 1: token scores, 2: gather of the kept K rows, 3: output
 hipError_t launch_attn_passes(int pass, const AttnDesc &d, hipStream_t stream);
 
+// ------------------------------------------------------------------ reduced attention, few queries
+// Lq <= 16 new tokens after a longer context (decode steps), dh == 128; V rows
+// 16-byte aligned.  Passes: 0 scores S (+ block statistics), 1 token scores,
+// 2 partial outputs over kept tokens, 3 merged output (+ column scores of O).
+struct AttnDecodeDesc {
+  const void *Q;  int64_t q_ts, q_hs;     // bf16
+  const void *Kt; int64_t kt_hs, ldkt;    // bf16, feature-major
+  const void *V;  int64_t v_ts, v_hs;     // bf16
+  const int32_t *I;                       // [hq][kf_pad] kept features
+  const int32_t *J;                       // [hq][kt_pad] kept tokens
+  float *S, *pstat, *nml, *tok, *opart;   // workspace (attn_decode_sizes), tok [hq][Lk]
+  void *O; int64_t o_ts, o_hs;            // bf16
+  float *o_scores;                        // [hq][128] or null
+  int64_t hq, hkv, Lq, Lk, kf, kf_pad, kt, kt_pad;
+  bool causal;
+};
+struct AttnDecodeSizes {
+  int nblk, nsplit;
+  size_t s_bytes, pstat_bytes, nml_bytes, opart_bytes;
+};
+bool attn_decode_ok(int64_t Lq, int64_t dh);
+AttnDecodeSizes attn_decode_sizes(int64_t Lq, int64_t Lk, int64_t Hq, int64_t kt);
+hipError_t launch_attn_decode(int pass, const AttnDecodeDesc &d, hipStream_t stream);
+
 }  // namespace rmm

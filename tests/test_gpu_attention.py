@@ -115,6 +115,53 @@ def test_fused_attention_small(case):
     print(f"  near ties: {near}")
 
 
+# A few new tokens after a longer context (decode steps: Lq <= 16 runs passes split
+# over keys): one token, a few, sixteen; grouped heads; with and without the mask.
+DECODE = [
+    (1, 300, 4, 2, 64, 150, True),
+    (3, 1025, 4, 1, 40, 500, True),
+    (16, 4096, 8, 2, 64, 2048, True),
+    (16, 16, 2, 2, 128, 16, True),
+    (7, 2000, 4, 4, 100, 1999, False),
+    (2, 513, 2, 1, 1, 1, True),
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: "Lq{}_Lk{}_h{}x{}_kf{}_kt{}_{}".format(
+    *c[:6], "causal" if c[6] else "full"))
+def test_fused_attention_decode(case):
+    Lq, Lk, Hq, Hkv, kf, kt, causal = case
+    Q, Kt, V = _operands(W4K, Lq, Lk, Hq, Hkv)
+    print(f"  near ties: {check_fused(Q, Kt, V, kf, kt, causal)}")
+
+
+def test_fused_attention_decode_unaligned_values_use_the_general_path():
+    """V rows that are not 16-byte aligned go through the general passes: same results."""
+    Lq, Lk, Hq, Hkv, kf, kt = 4, 700, 4, 2, 64, 350
+    Q, Kt, V = _operands(W4K, Lq, Lk, Hq, Hkv)
+    Vw = np.zeros((Lk, Hkv, 129), dtype=np.float32)
+    Vw[:, :, :128] = V
+    Qd, Ktd = dev_tensor(Q, torch.bfloat16), dev_tensor(Kt, torch.bfloat16)
+    Vd = dev_tensor(Vw, torch.bfloat16)[:, :, :128]            # head stride 129: unaligned rows
+    O, I, J = R.rmm_attention(Qd, Ktd, Vd, kf, kt, causal=True)
+    O2, I2, J2 = R.rmm_attention(Qd, Ktd, dev_tensor(V, torch.bfloat16), kf, kt, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(I, I2) and torch.equal(J, J2)
+    assert rel_fro(O.float().cpu().numpy(), O2.float().cpu().numpy()) < 1e-2
+
+
+@pytest.mark.parametrize("Lq", [1, 16])
+def test_fused_attention_decode_llama8b_16k_context(Lq):
+    """Decode steps after the 16k-token context of the LLaMA-3.1-8B layer, rho = 0.5."""
+    at = W8B.attention
+    Q, Kt, V = synth.attention_operands(W8B)
+    Q = np.ascontiguousarray(Q[at.L - Lq:])
+    kf = oracle.retained_count(at.rho, at.dh)
+    kt = oracle.retained_count(at.rho, at.L)
+    print(f"  near ties: {check_fused(Q, Kt, V, kf, kt, True, heads=[0, 13, 31])}")
+    torch.cuda.empty_cache()
+
+
 def test_fused_attention_full_retention_is_attention():
     """k_feat = dh and k_tok = Lk: the result is ordinary causal attention."""
     L, Hq, Hkv = 384, 4, 2
