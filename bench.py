@@ -357,7 +357,38 @@ def fused_attention(R, layer, steps, warmup, dense=True):
         torch.cuda.empty_cache()
     if "rho1" in res:
         res["speedup_vs_rho1"] = round(res["rho1"]["ms"] / res["rho"]["ms"], 3)
+    res["decode"] = decode_attention(R, layer, steps, warmup, dense)
     return res
+
+
+def decode_attention(R, layer, steps, warmup, dense=True):
+    """One new token after the layer's full context (a decode step): rmm_attention
+    with Lq = 1 on the last query row and every key, replayed from a HIP graph
+    (the call is a handful of short launches)."""
+    import torch
+
+    at = layer["attention"]
+    L, Hq, dh = at["L"], at["Hq"], at["dh"]
+    Q1 = at["Q"][L - 1:]
+    out = {"Lq": 1, "context": L, "launch": "hip graph replay"}
+    ratios = [("rho", R.rmm_k_from_rho(at["rho"], dh), R.rmm_k_from_rho(at["rho"], L))]
+    if dense:
+        ratios.append(("rho1", dh, L))
+    for name, kf, kt in ratios:
+        dev = Q1.device
+        O = torch.empty((1, Hq, dh), dtype=torch.bfloat16, device=dev)
+        If = torch.empty((Hq, R.rmm_k_pad(kf)), dtype=torch.int32, device=dev)
+        It = torch.empty((Hq, R.rmm_k_pad(kt)), dtype=torch.int32, device=dev)
+        ws = torch.empty(R.rmm_attention_workspace_bytes(1, L, Hq, dh, kf, kt), dtype=torch.uint8, device=dev)
+
+        class _One:
+            def step(self, tagged=False):
+                R.rmm_attention(Q1, at["Kt"], at["V"], kf, kt, O=O, idx_feat=If, idx_tok=It, ws=ws, causal=True)
+
+        ms, _ = time_steps(GraphStep(_One()), max(steps, 20), warmup)
+        out[name + "_us"] = round(ms * 1e3, 1)
+        del O, If, It, ws
+    return out
 
 
 def csrc_sha256():
@@ -398,7 +429,7 @@ def cpu_baseline(wl, layer_meta):
     except Exception:
         cores = os.cpu_count()
     lins = layer_meta["linears"]
-    m_s = min(4096, min(l.m for l in lins)) if lins else 0
+    m_s = min(8192, min(l.m for l in lins)) if lins else 0
     parts = []
     flops = 0.0
     t_total = 0.0
