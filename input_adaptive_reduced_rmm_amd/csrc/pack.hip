@@ -11,8 +11,17 @@
 // block so that no lane idles.  Stores are full 16-byte, fully coalesced.  The blocks of the first
 // row block also write the cleaned index list (-1 for padding and for indices
 // outside [0, d)) that the GEMM reads with 16-byte loads.
+//
+// Wide bf16 rows (the projections: d >= 512, one matrix) go through
+// pack_rows_kernel instead: at the ratios the method uses nearly every
+// 128-byte line of a source row holds a kept column, so the whole row is read
+// with 16-byte direct-to-LDS loads (one load instruction per 16 bytes rather
+// than per 2-byte element) and the kept columns are gathered from LDS.
+#include "mfma_gemm.h"
 #include "rmm_internal.h"
 #include "timing.h"
+
+#define LDS_AS __attribute__((address_space(3)))
 
 namespace rmm {
 namespace {
@@ -121,12 +130,94 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const T *__restrict__ A,
   }
 }
 
+// One block walks `rows_per_block` rows: the whole source row into LDS
+// (each wave moves 1 KiB per load instruction), then every thread writes up
+// to MAXC 16-byte chunks of the packed row (8 kept columns each, gathered
+// from LDS; padding slots are zero).  Several blocks per CU overlap one
+// block's loads with another's gathers.
+__device__ __forceinline__ void lds_row_load16(mg::rsrc_t r, void *lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void *)lds, 16, voff, 0, 0, 0);
+}
+
+template <int MAXC>
+__global__ __launch_bounds__(kThreads) void pack_rows_kernel(const uint16_t *__restrict__ A, int64_t lda,
+                                                             const int32_t *__restrict__ idx, int64_t m,
+                                                             int64_t d, int64_t k, int64_t k_pad,
+                                                             int64_t rows_per_block, uint16_t *__restrict__ out,
+                                                             int32_t *__restrict__ idx_clean) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char row_lds[];
+  const uint16_t *row16 = reinterpret_cast<const uint16_t *>(row_lds);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nchunk = k_pad / 8;
+  int32_t col[MAXC][8];
+#pragma unroll
+  for (int u = 0; u < MAXC; ++u) {
+    const int64_t c = tid + (int64_t)kThreads * u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t t = c * 8 + e;
+      int32_t v = -1;
+      if (c < nchunk && t < k) {
+        const int32_t x = idx[t];
+        v = (x >= 0 && x < d) ? x : -1;
+      }
+      col[u][e] = v;
+    }
+    if (idx_clean && blockIdx.x == 0 && c < nchunk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) idx_clean[c * 8 + e] = col[u][e];
+    }
+  }
+  const mg::rsrc_t ra = mg::make_rsrc(A, (uint64_t)((m - 1) * lda + d) * 2);
+  const int nblk1k = (int)((d * 2 + 1023) / 1024);   // 1 KiB pieces of a row
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
+  const int64_t r1 = r0 + rows_per_block < m ? r0 + rows_per_block : m;
+  for (int64_t r = r0; r < r1; ++r) {
+    for (int q = wave; q < nblk1k; q += kThreads / 64)
+      lds_row_load16(ra, row_lds + q * 1024, (uint32_t)(r * lda * 2 + q * 1024 + lane * 16));
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    uint16_t *orow = out + r * k_pad;
+#pragma unroll
+    for (int u = 0; u < MAXC; ++u) {
+      const int64_t c = tid + (int64_t)kThreads * u;
+      if (c < nchunk) {
+        uint16_t v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = col[u][e] >= 0 ? row16[col[u][e]] : (uint16_t)0;
+        store16(orow + c * 8, v);
+      }
+    }
+    __syncthreads();   // the row buffer is refilled next
+  }
+}
+
 }  // namespace
 
 hipError_t launch_pack(rmm_dtype_t dt, const void *A, int64_t lda, int64_t a_bs,
                        const int32_t *idx, int64_t idx_bs, int64_t batch, int64_t m, int64_t d,
                        int64_t k, int64_t k_pad, void *out, int32_t *idx_clean, hipStream_t st) {
   const int N = dt == RMM_BF16 ? 8 : 4;
+  const int64_t row_bytes = ceil_div(d * 2, 1024) * 1024;
+  if (dt == RMM_BF16 && batch == 1 && d >= 512 && row_bytes <= 64 * 1024 && k_pad <= 8 * 8 * kThreads &&
+      reinterpret_cast<uintptr_t>(A) % 16 == 0 && lda % 8 == 0 && (uint64_t)((m - 1) * lda + d) * 2 < mg::kMaxRecords) {
+    const int64_t nchunk = k_pad / 8;
+    const int64_t per_thread = ceil_div(nchunk, (int64_t)kThreads);
+    // about 2048 blocks of at least one row
+    int64_t rpb = ceil_div(m, 2048);
+    const int64_t blocks = ceil_div(m, rpb);
+    KernelTimer timer("pack", st);
+#define RMM_PACK_ROWS(C)                                                                                     \
+  hipLaunchKernelGGL(pack_rows_kernel<C>, dim3((unsigned)blocks), dim3(kThreads), (unsigned)row_bytes, st,     \
+                     static_cast<const uint16_t *>(A), lda, idx, m, d, k, k_pad, rpb, static_cast<uint16_t *>(out), \
+                     idx_clean)
+    if (per_thread <= 1) RMM_PACK_ROWS(1);
+    else if (per_thread <= 2) RMM_PACK_ROWS(2);
+    else if (per_thread <= 4) RMM_PACK_ROWS(4);
+    else RMM_PACK_ROWS(8);
+#undef RMM_PACK_ROWS
+    return hipGetLastError();
+  }
   const int64_t cpr = k_pad / N;                    // 16-byte chunks per packed row
   const int cpb = (int)(cpr < kThreads ? cpr : kThreads);
   const int rpi = kThreads / cpb;                   // rows side by side in a block
