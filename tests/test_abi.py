@@ -143,3 +143,61 @@ def test_qk_pv_reject(lib):
     need = lib.rmm_pv_workspace_bytes(4, 64, 64, 32)
     assert need > 0
     assert p(FAKE, 4, 64, 64, 4096, 64, FAKE, 2, 128, 256, 128, 32, 0, FAKE, 512, 128, FAKE, FAKE, need - 1, None) == 3
+
+
+def test_gemm_w8_rejects(lib):
+    f = lib.rmm_gemm_w8
+    args = dict(A=FAKE, lda=64, Bq=FAKE, ldb=32, scale=FAKE, idx=FAKE, m=16, d=64, n=32, k=8, Y=FAKE, ldy=32)
+    def call(ws=FAKE, wsb=1 << 30, **kw):
+        a = {**args, **kw}
+        return f(a["A"], a["lda"], a["Bq"], a["ldb"], a["scale"], a["idx"], a["m"], a["d"], a["n"], a["k"], a["Y"],
+                 a["ldy"], ws, wsb, None)
+    assert call(scale=None) == 1
+    assert call(k=0) == 1
+    assert call(k=65) == 1
+    assert call(ldb=31) == 1
+    assert call(lda=63) == 1
+    assert call(ldb=40) == 2                     # decode rows must be 16-byte aligned
+    assert call(Bq=ctypes.c_void_p(0x10008)) == 2
+    need = lib.rmm_gemm_w8_workspace_bytes(16, 32, 8)
+    assert need >= 16 * 64 * 2 + 256
+    assert call(wsb=need - 1) == 3
+    # more rows: the dequantized kept rows are part of the workspace
+    assert lib.rmm_gemm_w8_workspace_bytes(2048, 1024, 300) >= 2048 * 320 * 2 + 320 * 1024 * 2
+    assert lib.rmm_gemm_w8_workspace_bytes(0, 32, 8) == 0
+
+
+def test_swiglu_scored_rejects(lib):
+    f = lib.rmm_swiglu_scored
+    def call(G=FAKE, ldg=64, U=FAKE, ldu=64, m=100, n=64, H=FAKE, ldh=64, s=FAKE, ws=FAKE, wsb=1 << 30):
+        return f(G, ldg, U, ldu, m, n, H, ldh, s, ws, wsb, None)
+    assert call(s=None) == 1
+    assert call(m=0) == 1
+    assert call(ldg=63) == 1
+    assert call(n=60, ldg=64, ldu=64, ldh=64) == 2          # n % 8 != 0
+    assert call(ldu=68) == 2                                 # unaligned rows
+    assert call(G=ctypes.c_void_p(0x10002)) == 2
+    need = lib.rmm_swiglu_scored_workspace_bytes(100000, 4096)
+    assert need > 0
+    assert call(m=100000, n=4096, ldg=4096, ldu=4096, ldh=4096, wsb=need - 1) == 3
+    assert lib.rmm_swiglu_scored_workspace_bytes(1, 0) == 0
+
+
+def test_attention_rejects(lib):
+    f = lib.rmm_attention
+    def call(Lq=64, Hq=4, dh=128, qts=512, qhs=128, Lk=64, Hkv=2, kths=8192, ldkt=64, vts=256, vhs=128,
+             kf=32, kt=32, causal=1, ots=512, ohs=128, ws=FAKE, wsb=1 << 30, O=FAKE):
+        return f(FAKE, Lq, Hq, dh, qts, qhs, FAKE, Lk, Hkv, kths, ldkt, FAKE, vts, vhs, kf, kt, causal, O, ots, ohs,
+                 FAKE, FAKE, None, None, ws, wsb, None)
+    assert call(O=None) == 1
+    assert call(Hq=6, Hkv=4) == 1                 # Hq % Hkv != 0
+    assert call(kf=129) == 1                      # more features than dh
+    assert call(kt=65) == 1                       # more tokens than Lk
+    assert call(Lq=65) == 1                       # causal queries beyond the keys
+    assert call(ldkt=63) == 1
+    assert call(dh=64, qts=256, qhs=64, vts=128, vhs=64, ots=256, ohs=64) == 2   # head size not served
+    for Lq in (1, 16, 64):
+        need = lib.rmm_attention_workspace_bytes(Lq, 64, 4, 128, 32, 32)
+        assert need > 0
+        assert call(Lq=Lq, wsb=need - 1) == 3
+    assert lib.rmm_attention_workspace_bytes(0, 64, 4, 128, 32, 32) == 0
