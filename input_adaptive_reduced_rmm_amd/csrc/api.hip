@@ -181,13 +181,22 @@ RMM_API rmm_status_t rmm_topk(const float *scores, int64_t batch, int64_t d, int
 
 // ------------------------------------------------------------------ gemm
 // Many-row bf16 products also keep a transposed copy of the kept weight rows.
-static bool gemm_uses_nt(rmm_dtype_t dt, int64_t m) { return dt == RMM_BF16 && m >= 1024; }
+// The persistent 256 x 256 NT kernel needs enough output tiles to occupy the
+// chip; smaller outputs (e.g. 2048 x 2048) run on the 128 x 128 row-gather core.
+#ifndef RMM_NT_MIN_TILES
+#define RMM_NT_MIN_TILES 192
+#endif
+static bool gemm_uses_nt(rmm_dtype_t dt, int64_t m, int64_t n = -1) {
+  if (dt != RMM_BF16 || m < 1024) return false;
+  if (n < 0) return true;
+  return ((m + 255) / 256) * ((n + 255) / 256) >= RMM_NT_MIN_TILES;
+}
 
 RMM_API size_t rmm_gemm_workspace_bytes(rmm_dtype_t dt, int64_t m, int64_t n, int64_t k) {
   if (!dtype_ok(dt) || m < 1 || k < 1 || n < 1) return 0;
   const int64_t k_pad = rmm_k_pad(k);
   size_t b = align256((size_t)m * (size_t)k_pad * esize(dt)) + align256((size_t)k_pad * 4);
-  if (gemm_uses_nt(dt, m)) b += rmm::gemm_nt_bt_bytes(n, k_pad);
+  if (gemm_uses_nt(dt, m, n)) b += rmm::gemm_nt_bt_bytes(n, k_pad);
   if (dt == RMM_BF16 && m <= 32) b += align256(rmm::skinny_part_bytes(false, m, n, k_pad));
   return b;
 }
@@ -211,7 +220,7 @@ RMM_API rmm_status_t rmm_gemm(rmm_dtype_t dt, const void *A, int64_t lda, const 
   int32_t *idx_clean = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + align256((size_t)m * k_pad * e));
   hipError_t he = rmm::launch_pack(dt, A, lda, 0, idx, 0, 1, m, d, k, k_pad, ws, idx_clean, st);
   if (he != hipSuccess) return hip_status(he, "gemm pack launch");
-  if (gemm_uses_nt(dt, m) && rmm::gemm_nt_ok(m, n, d, ldb, k_pad)) {
+  if (gemm_uses_nt(dt, m, n) && rmm::gemm_nt_ok(m, n, d, ldb, k_pad)) {
     void *bt = static_cast<char *>(ws) + align256((size_t)m * k_pad * e) + align256((size_t)k_pad * 4);
     return hip_status(rmm::launch_gemm_nt(ws, idx_clean, B, ldb, d, bt, Y, ldy, m, n, k_pad, st),
                       "gemm launch");
@@ -262,7 +271,7 @@ static W8Layout w8_layout(int64_t m, int64_t n, int64_t k) {
   } else {
     L.bd = c.off;   c.take((size_t)k_pad * n * 2);
     L.iota = c.off; c.take((size_t)k_pad * 4);
-    if (gemm_uses_nt(RMM_BF16, m)) {
+    if (gemm_uses_nt(RMM_BF16, m, n)) {
       L.bt = c.off;
       c.take(rmm::gemm_nt_bt_bytes(n, k_pad));
     }
@@ -308,7 +317,7 @@ RMM_API rmm_status_t rmm_gemm_w8(const void *A, int64_t lda, const void *Bq, int
   int32_t *iota = reinterpret_cast<int32_t *>(w + L.iota);
   he = rmm::launch_topk(nullptr, 1, k, k, k_pad, iota, st);   // k == d: 0..k-1, then -1
   if (he != hipSuccess) return hip_status(he, "gemm_w8 index launch");
-  if (gemm_uses_nt(RMM_BF16, m) && rmm::gemm_nt_ok(m, n, k_pad, n, k_pad))
+  if (gemm_uses_nt(RMM_BF16, m, n) && rmm::gemm_nt_ok(m, n, k_pad, n, k_pad))
     return hip_status(rmm::launch_gemm_nt(w + L.a, iota, w + L.bd, n, k_pad, w + L.bt, Y, ldy, m, n, k_pad, st),
                       "gemm_w8 launch");
   rmm::GemmArgs g{};
