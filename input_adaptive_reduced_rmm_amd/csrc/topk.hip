@@ -1,8 +1,9 @@
 // Top-k selection of column scores ("Estrategia de Selección": keep the k
 // indices with the highest scores), ties to the lower index, output ascending.
 //
-// One 1024-thread workgroup per batch row.  Scores are mapped to order-
-// preserving unsigned keys and (for d up to kLdsKeys) parked in LDS.  The exact
+// One workgroup per batch row (1024 threads; 256 for rows of at most 4096).
+// Scores are mapped to order-preserving unsigned keys and (for d up to
+// kLdsKeys) parked in LDS.  The exact
 // k-th largest key T is found by MSD radix select: the bits every key shares
 // are skipped (found with a block OR/AND reduction), then <= 8-bit digits are
 // histogrammed in LDS and a single wave locates the digit that holds the k-th
@@ -15,8 +16,7 @@
 namespace rmm {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
+constexpr int kMaxThreads = 1024;
 constexpr int kLdsKeys = 32768;  // 128 KiB of keys; beyond that, keys are re-read from global
 
 __device__ __forceinline__ uint32_t score_key(float f) {
@@ -30,12 +30,15 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-template <bool IN_LDS>
-__global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict__ scores, int64_t d,
+// NT threads per workgroup: 1024 for long rows, 256 for short ones (fewer
+// waves meet at each of the select's barriers).
+template <bool IN_LDS, int NT>
+__global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scores, int64_t d,
                                                         int64_t k, int64_t k_pad,
                                                         int32_t *__restrict__ idx) {
-  __shared__ uint32_t keys[IN_LDS ? kLdsKeys : 1];
+  __shared__ uint32_t keys[IN_LDS ? (NT == 256 ? 4096 : kLdsKeys) : 1];
   __shared__ uint32_t hist[256];
+  constexpr int kThreads = NT, kWaves = NT / 64;
   __shared__ uint32_t red_or[kWaves], red_and[kWaves];
   __shared__ uint32_t sel_digit, sel_above;
 
@@ -239,11 +242,13 @@ hipError_t launch_topk(const float *scores, int64_t batch, int64_t d, int64_t k,
     hipLaunchKernelGGL(iota_kernel, dim3(gx, (unsigned)batch), dim3(256), 0, st, d, k_pad, idx);
     return hipGetLastError();
   }
-  if (d <= kLdsKeys)
-    hipLaunchKernelGGL(topk_kernel<true>, dim3((unsigned)batch), dim3(kThreads), 0, st, scores, d,
-                       k, k_pad, idx);
+  if (d <= 4096)
+    hipLaunchKernelGGL((topk_kernel<true, 256>), dim3((unsigned)batch), dim3(256), 0, st, scores, d, k, k_pad, idx);
+  else if (d <= kLdsKeys)
+    hipLaunchKernelGGL((topk_kernel<true, kMaxThreads>), dim3((unsigned)batch), dim3(kMaxThreads), 0, st, scores,
+                       d, k, k_pad, idx);
   else
-    hipLaunchKernelGGL(topk_kernel<false>, dim3((unsigned)batch), dim3(kThreads), 0, st, scores,
+    hipLaunchKernelGGL((topk_kernel<false, kMaxThreads>), dim3((unsigned)batch), dim3(kMaxThreads), 0, st, scores,
                        d, k, k_pad, idx);
   return hipGetLastError();
 }
