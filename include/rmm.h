@@ -191,6 +191,32 @@ rmm_status_t rmm_swiglu_scored(const void *G, int64_t ldg, const void *U, int64_
                                rmm_stream_t stream);
 
 /*
+ * rmm_rmsnorm_scored - RMS normalisation of each row with the column scores of
+ * the result in one pass: Y[i][j] = X[i][j] * w[j] / sqrt(mean_j'(X[i][j']^2)
+ * + eps) in float32 arithmetic, rounded to bf16, and scores[j] =
+ * ||Y[:, j]||_2 over the m rows of the bf16 values written (float32
+ * accumulation in a fixed order).  Source: "Estrategia de Selección" (the
+ * score of an index is the norm of that column of A, computed beside the
+ * product): in a LLaMA-style layer the normalised hidden state is the A of
+ * the q, k, v, gate and up projections, so its producer scores it and
+ * rmm_topk follows with no rmm_colnorm pass.
+ *   X (device, bf16) m x d, leading dimension ldx >= d.
+ *   w (device, bf16) [d] per-column gain.
+ *   eps: finite, >= 0, added to the mean square (eps = 0 and an all-zero row
+ *        give non-finite values in that row, as the formula does).
+ *   Y (device, bf16) m x d output, leading dimension ldy >= d; may not alias X.
+ *   scores (device, float) [d].
+ *   d must be a multiple of 512 no larger than 8192 and X, w, Y rows 16-byte
+ *   aligned (pointers and leading dimensions multiples of 8 elements), else
+ *   RMM_ERR_UNSUPPORTED.
+ *   ws: rmm_rmsnorm_scored_workspace_bytes(m, d) bytes (0: none), 256-byte aligned.
+ */
+size_t rmm_rmsnorm_scored_workspace_bytes(int64_t m, int64_t d);
+rmm_status_t rmm_rmsnorm_scored(const void *X, int64_t ldx, const void *w, float eps, int64_t m, int64_t d,
+                                void *Y, int64_t ldy, float *scores, void *ws, size_t ws_bytes,
+                                rmm_stream_t stream);
+
+/*
  * rmm_qk - feature-reduced attention scores for every query head (bf16 in,
  * float32 out).  Source: "Alcance de Aplicación" (reduce the feature dimension
  * of Q K^T).  For query head h with kv head g = floor(h*Hkv/Hq):

@@ -16,11 +16,11 @@ import torch
 __all__ = [
     "RMMError", "load", "lib_path",
     "rmm_version", "rmm_k_from_rho", "rmm_k_pad",
-    "rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_gemm_w8", "rmm_swiglu_scored", "rmm_qk", "rmm_pv",
+    "rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_gemm_w8", "rmm_swiglu_scored", "rmm_rmsnorm_scored", "rmm_qk", "rmm_pv",
     "rmm_attention",
     "rmm_colnorm_workspace_bytes", "rmm_topk_workspace_bytes", "rmm_gemm_workspace_bytes",
     "rmm_qk_workspace_bytes", "rmm_pv_workspace_bytes", "rmm_attention_workspace_bytes",
-    "rmm_gemm_w8_workspace_bytes", "rmm_swiglu_scored_workspace_bytes",
+    "rmm_gemm_w8_workspace_bytes", "rmm_swiglu_scored_workspace_bytes", "rmm_rmsnorm_scored_workspace_bytes",
     "rmm_linear", "timing",
 ]
 
@@ -71,6 +71,9 @@ _PROTOS = {
     "rmm_gemm_w8_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "rmm_swiglu_scored_workspace_bytes": (_sz, [_i64, _i64]),
     "rmm_swiglu_scored": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "rmm_rmsnorm_scored_workspace_bytes": (_sz, [_i64, _i64]),
+    "rmm_rmsnorm_scored": (ctypes.c_int, [_vp, _i64, _vp, ctypes.c_float, _i64, _i64, _vp, _i64, _vp, _vp, _sz,
+                                          _vp]),
     "rmm_gemm_w8": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _sz,
                                    _vp]),
     "rmm_attention": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _vp,
@@ -286,6 +289,30 @@ def rmm_swiglu_scored(G: torch.Tensor, U: torch.Tensor, H: torch.Tensor | None =
     _check(lib.rmm_swiglu_scored(_ptr(G), G.stride(0), _ptr(U), U.stride(0), m, n, _ptr(H), H.stride(0),
                                  _ptr(scores), _ptr(ws), wsb, _stream(dev)))
     return H, scores
+
+
+def rmm_rmsnorm_scored_workspace_bytes(m: int, d: int) -> int:
+    return int(load().rmm_rmsnorm_scored_workspace_bytes(m, d))
+
+
+def rmm_rmsnorm_scored(X: torch.Tensor, w: torch.Tensor, eps: float = 1e-5, Y: torch.Tensor | None = None,
+                       scores: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """Y = X * w / sqrt(mean(X^2, row) + eps) (bf16 [m, d]) and the column scores of Y (float32 [d])."""
+    lib = load()
+    dev = _dev(X, w)
+    if X.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise TypeError("rmm_rmsnorm_scored takes bfloat16 X and w")
+    if X.dim() != 2 or X.stride(1) != 1 or w.dim() != 1 or w.shape[0] != X.shape[1] or w.stride(0) != 1:
+        raise ValueError("X must be [m, d] with unit column stride and w contiguous [d]")
+    m, d = X.shape
+    if Y is None:
+        Y = torch.empty((m, d), dtype=torch.bfloat16, device=dev)
+    if scores is None:
+        scores = torch.empty(d, dtype=torch.float32, device=dev)
+    ws, wsb = _ws(rmm_rmsnorm_scored_workspace_bytes(m, d), dev, ws)
+    _check(lib.rmm_rmsnorm_scored(_ptr(X), X.stride(0), _ptr(w), float(eps), m, d, _ptr(Y), Y.stride(0),
+                                  _ptr(scores), _ptr(ws), wsb, _stream(dev)))
+    return Y, scores
 
 
 def rmm_qk(Q: torch.Tensor, Kt: torch.Tensor, k: int, S: torch.Tensor | None = None,

@@ -362,6 +362,30 @@ RMM_API rmm_status_t rmm_swiglu_scored(const void *G, int64_t ldg, const void *U
                     "swiglu_scored launch");
 }
 
+RMM_API size_t rmm_rmsnorm_scored_workspace_bytes(int64_t m, int64_t d) {
+  if (m < 1 || d < 1) return 0;
+  return align256(rmm::rmsnorm_part_bytes(m, d));
+}
+
+RMM_API rmm_status_t rmm_rmsnorm_scored(const void *X, int64_t ldx, const void *w, float eps, int64_t m, int64_t d,
+                                        void *Y, int64_t ldy, float *scores, void *ws, size_t ws_bytes,
+                                        rmm_stream_t stream) {
+  if (!X || !w || !Y || !scores) return fail(RMM_ERR_INVALID_ARG, "rmsnorm_scored: NULL pointer");
+  if (m < 1 || d < 1 || d >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "rmsnorm_scored: bad m or d");
+  if (!(eps >= 0.f) || eps > 3.0e38f) return fail(RMM_ERR_INVALID_ARG, "rmsnorm_scored: eps must be finite and >= 0");
+  if (ldx < d || ldy < d) return fail(RMM_ERR_INVALID_ARG, "rmsnorm_scored: leading dimension too small");
+  if (!aligned(scores, 4)) return fail(RMM_ERR_INVALID_ARG, "rmsnorm_scored: misaligned pointer");
+  if (!rmm::rmsnorm_ok(X, ldx, w, Y, ldy, d))
+    return fail(RMM_ERR_UNSUPPORTED,
+                "rmsnorm_scored: needs d a multiple of 512 up to 8192 and 16-byte aligned rows and weight");
+  const size_t need = rmm_rmsnorm_scored_workspace_bytes(m, d);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
+    return fail(RMM_ERR_WORKSPACE, "rmsnorm_scored: workspace needs %zu bytes (256-byte aligned)", need);
+  return hip_status(rmm::launch_rmsnorm_scored(X, ldx, w, eps, m, d, Y, ldy, scores, static_cast<float *>(ws),
+                                               (hipStream_t)stream),
+                    "rmsnorm_scored launch");
+}
+
 // ------------------------------------------------------------------ attention
 static size_t qk_layout(int64_t Lq, int64_t Hq, int64_t dh, int64_t k, size_t *o_scores,
                         size_t *o_part, size_t *o_pack, size_t *o_idx) {

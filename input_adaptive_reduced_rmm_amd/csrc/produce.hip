@@ -88,6 +88,94 @@ __global__ __launch_bounds__(64 * kWaves) void swiglu_scored_kernel(const uint16
   }
 }
 
+// rmsnorm_scored_kernel writes Y = bf16(x * w / sqrt(mean(x^2) + eps)) per
+// row (the normalised input of the q, k, v and up, gate projections of a
+// LLaMA-style layer) and adds the squares of the bf16 Y per column.  A
+// workgroup has one thread per 8 columns (d / 8 threads, 1 to 16 waves), so
+// each column belongs to one thread and its sum needs no reduction across
+// threads.  kRmsRows rows are in flight per thread; their sums of squares meet
+// through a double-buffered LDS array (one barrier per kRmsRows rows, the
+// waves' parts added in wave order).
+#ifndef RMM_RMS_ROWS
+#define RMM_RMS_ROWS 4
+#endif
+constexpr int kRmsRows = RMM_RMS_ROWS;
+
+__global__ __launch_bounds__(1024) void rmsnorm_scored_kernel(const uint16_t *__restrict__ X, int64_t ldx,
+                                                               const uint16_t *__restrict__ w, float eps, int64_t m,
+                                                               int64_t d, uint16_t *__restrict__ Y, int64_t ldy,
+                                                               int64_t rows_per_chunk, float *__restrict__ out,
+                                                               int final_sqrt) {
+  __shared__ float red[2][kRmsRows][16];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
+  const int64_t col = (int64_t)t * 8;
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_chunk;
+  const int64_t r1 = r0 + rows_per_chunk < m ? r0 + rows_per_chunk : m;
+  const float inv_d = 1.f / (float)d;
+  const uint4 wv = *reinterpret_cast<const uint4 *>(w + col);
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  int buf = 0;
+  for (int64_t rb = r0; rb < r1; rb += kRmsRows) {
+    uint4 xv[kRmsRows];
+#pragma unroll
+    for (int u = 0; u < kRmsRows; ++u)
+      xv[u] = rb + u < r1 ? *reinterpret_cast<const uint4 *>(X + (rb + u) * ldx + col) : make_uint4(0, 0, 0, 0);
+    float ss[kRmsRows];
+#pragma unroll
+    for (int u = 0; u < kRmsRows; ++u) {
+      ss[u] = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t xw = mg::u4get(xv[u], q);
+        const float a = bf16_lo(xw), b = bf16_hi(xw);
+        ss[u] = fmaf(a, a, ss[u]);
+        ss[u] = fmaf(b, b, ss[u]);
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) ss[u] += __shfl_xor(ss[u], o, 64);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int u = 0; u < kRmsRows; ++u) red[buf][u][wave] = ss[u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kRmsRows; ++u) {
+      const int64_t r = rb + u;
+      if (r < r1) {
+        float tot = 0.f;
+        for (int v = 0; v < nw; ++v) tot += red[buf][u][v];
+        const float inv = 1.f / __builtin_sqrtf(tot * inv_d + eps);
+        uint32_t yw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t xw = mg::u4get(xv[u], q), ww = mg::u4get(wv, q);
+          yw[q] = pack_bf16x2(bf16_lo(xw) * inv * bf16_lo(ww), bf16_hi(xw) * inv * bf16_hi(ww));
+          const float y0 = bf16_lo(yw[q]), y1 = bf16_hi(yw[q]);
+          acc[2 * q] = fmaf(y0, y0, acc[2 * q]);
+          acc[2 * q + 1] = fmaf(y1, y1, acc[2 * q + 1]);
+        }
+        *reinterpret_cast<uint4 *>(Y + r * ldy + col) = make_uint4(yw[0], yw[1], yw[2], yw[3]);
+      }
+    }
+    buf ^= 1;
+  }
+  float *o = out + (int64_t)blockIdx.x * d * (1 - final_sqrt) + col;
+  if (final_sqrt) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = __builtin_sqrtf(acc[e]);
+  }
+  if ((reinterpret_cast<uintptr_t>(out) & 15) == 0) {   // partials always; scores when 16-byte aligned
+    *reinterpret_cast<float4 *>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4 *>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = acc[e];
+  }
+}
+
 struct SwigluPlan {
   int64_t col_tiles, rows_per_chunk, chunks;
 };
@@ -107,7 +195,41 @@ SwigluPlan swiglu_plan(int64_t m, int64_t n) {
   return p;
 }
 
+#ifndef RMM_RMS_BLOCKS
+#define RMM_RMS_BLOCKS 512
+#endif
+// About RMM_RMS_BLOCKS workgroups, each a whole number of row groups.
+int64_t rmsnorm_rows_per_chunk(int64_t m) { return ceil_div(ceil_div(m, RMM_RMS_BLOCKS), kRmsRows) * kRmsRows; }
+
 }  // namespace
+
+bool rmsnorm_ok(const void *X, int64_t ldx, const void *w, const void *Y, int64_t ldy, int64_t d) {
+  auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  return al(X) && al(w) && al(Y) && ldx % 8 == 0 && ldy % 8 == 0 && d % kCols == 0 && d / kCols >= 1 &&
+         d / kCols <= 16;
+}
+
+size_t rmsnorm_part_bytes(int64_t m, int64_t d) {
+  const int64_t chunks = ceil_div(m, rmsnorm_rows_per_chunk(m));
+  return chunks > 1 ? (size_t)chunks * (size_t)d * 4 : 0;
+}
+
+hipError_t launch_rmsnorm_scored(const void *X, int64_t ldx, const void *w, float eps, int64_t m, int64_t d, void *Y,
+                                 int64_t ldy, float *scores, float *part, hipStream_t st) {
+  const int64_t rpc = rmsnorm_rows_per_chunk(m), chunks = ceil_div(m, rpc);
+  const bool single = chunks == 1;
+  {
+    KernelTimer timer("rmsnorm_scored", st);
+    const uint16_t *x = static_cast<const uint16_t *>(X), *wp = static_cast<const uint16_t *>(w);
+    uint16_t *y = static_cast<uint16_t *>(Y);
+    float *o = single ? scores : part;
+    const dim3 grid((unsigned)chunks), blk((unsigned)(d / 8));
+    hipLaunchKernelGGL(rmsnorm_scored_kernel, grid, blk, 0, st, x, ldx, wp, eps, m, d, y, ldy, rpc, o, single);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || single) return e;
+  }
+  return launch_colnorm_finish(part, chunks, d, scores, st);
+}
 
 bool swiglu_ok(const void *G, int64_t ldg, const void *U, int64_t ldu, const void *H, int64_t ldh, int64_t n) {
   auto al = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };

@@ -57,6 +57,13 @@ size_t swiglu_part_bytes(int64_t m, int64_t n);
 hipError_t launch_swiglu_scored(const void *G, int64_t ldg, const void *U, int64_t ldu, int64_t m, int64_t n,
                                 void *H, int64_t ldh, float *scores, float *part, hipStream_t stream);
 
+// Y = bf16(X * w / sqrt(mean(X^2 over the row) + eps)) for bf16 X [m][d], w [d],
+// and the column scores of Y.  d = 512 c, c = 1 .. 16; rows 16-byte aligned.
+bool rmsnorm_ok(const void *X, int64_t ldx, const void *w, const void *Y, int64_t ldy, int64_t d);
+size_t rmsnorm_part_bytes(int64_t m, int64_t d);
+hipError_t launch_rmsnorm_scored(const void *X, int64_t ldx, const void *w, float eps, int64_t m, int64_t d, void *Y,
+                                 int64_t ldy, float *scores, float *part, hipStream_t stream);
+
 // ------------------------------------------------------------------ top-k
 hipError_t launch_topk(const float *scores, int64_t batch, int64_t d, int64_t k, int64_t k_pad,
                        int32_t *idx, hipStream_t stream);

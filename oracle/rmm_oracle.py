@@ -62,6 +62,7 @@ __all__ = [
     "reduced_product",
     "reduced_product_w8",
     "swiglu",
+    "rmsnorm",
     "rmm",
     "kv_head",
     "reduced_qk",
@@ -149,6 +150,20 @@ def swiglu(G, U) -> np.ndarray:
     U64 = np.asarray(U, dtype=np.float64)
     with np.errstate(over="ignore"):
         return G64 / (1.0 + np.exp(-G64)) * U64
+
+
+def rmsnorm(X, w, eps: float) -> np.ndarray:
+    """RMS normalisation of each row in float64: x * w / sqrt(mean(x^2) + eps).
+
+    The normalisation that produces the A of the q, k, v, gate and up
+    projections of a LLaMA-style layer; its column scores ("Estrategia de
+    Selección") can be accumulated by the producer as it writes A.
+    """
+    X64 = np.asarray(X, dtype=np.float64)
+    w64 = np.asarray(w, dtype=np.float64)
+    ms = np.mean(X64 * X64, axis=1, keepdims=True)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return X64 / np.sqrt(ms + float(eps)) * w64[None, :]
 
 
 def rmm(A, B, rho: float):

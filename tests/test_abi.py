@@ -183,6 +183,26 @@ def test_swiglu_scored_rejects(lib):
     assert lib.rmm_swiglu_scored_workspace_bytes(1, 0) == 0
 
 
+def test_rmsnorm_scored_rejects(lib):
+    f = lib.rmm_rmsnorm_scored
+    def call(X=FAKE, ldx=1024, w=FAKE, eps=1e-5, m=100, d=1024, Y=FAKE, ldy=1024, s=FAKE, ws=FAKE, wsb=1 << 30):
+        return f(X, ldx, w, eps, m, d, Y, ldy, s, ws, wsb, None)
+    assert call(w=None) == 1
+    assert call(m=0) == 1
+    assert call(eps=-1e-6) == 1
+    assert call(eps=float("nan")) == 1
+    assert call(eps=float("inf")) == 1
+    assert call(ldy=1000) == 1
+    assert call(d=1000, ldx=1000, ldy=1000) == 2             # d % 512 != 0
+    assert call(d=512 * 17, ldx=512 * 17, ldy=512 * 17) == 2  # wider than 8192
+    assert call(ldx=1028) == 2                                 # unaligned rows
+    assert call(w=ctypes.c_void_p(0x10008)) == 2
+    need = lib.rmm_rmsnorm_scored_workspace_bytes(100000, 4096)
+    assert need > 0
+    assert call(m=100000, d=4096, ldx=4096, ldy=4096, wsb=need - 1) == 3
+    assert lib.rmm_rmsnorm_scored_workspace_bytes(0, 4096) == 0
+
+
 def test_attention_rejects(lib):
     f = lib.rmm_attention
     def call(Lq=64, Hq=4, dh=128, qts=512, qhs=128, Lk=64, Hkv=2, kths=8192, ldkt=64, vts=256, vhs=128,

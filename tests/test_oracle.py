@@ -437,3 +437,33 @@ def test_swiglu_closed_forms():
     np.testing.assert_allclose(O.swiglu(g, np.ones(50)) - O.swiglu(-g, np.ones(50)), g, rtol=1e-13, atol=1e-14)
     u = rng.standard_normal(50)
     np.testing.assert_allclose(O.swiglu(g, u), O.swiglu(g, np.ones(50)) * u, rtol=1e-15)
+
+
+def test_rmsnorm_worked_examples():
+    # [3, 4]: mean square 12.5, so y = x / sqrt(12.5) = [0.84852..., 1.13137...]
+    y = O.rmsnorm(np.array([[3.0, 4.0]]), np.ones(2), 0.0)
+    np.testing.assert_allclose(y, [[3 / np.sqrt(12.5), 4 / np.sqrt(12.5)]], rtol=1e-15)
+    np.testing.assert_allclose(y, [[0.848528137423857, 1.131370849898476]], rtol=1e-14)
+    # ones with eps = 3: sqrt(1 + 3) = 2, gain w applied per column
+    y = O.rmsnorm(np.ones((2, 4)), np.array([1.0, 2.0, -1.0, 0.5]), 3.0)
+    np.testing.assert_allclose(y, [[0.5, 1.0, -0.5, 0.25]] * 2, rtol=1e-15)
+
+
+def test_rmsnorm_invariants():
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((7, 96)) * rng.uniform(0.1, 10.0, size=(7, 1))
+    w = rng.uniform(0.5, 2.0, size=96)
+    # unit gain, eps = 0: every row has mean square exactly 1
+    y1 = O.rmsnorm(X, np.ones(96), 0.0)
+    np.testing.assert_allclose(np.mean(y1 * y1, axis=1), 1.0, rtol=1e-13)
+    # scale invariance per row with eps = 0; sign follows x
+    sc = rng.uniform(0.01, 100.0, size=(7, 1))
+    np.testing.assert_allclose(O.rmsnorm(X * sc, w, 0.0), O.rmsnorm(X, w, 0.0), rtol=1e-12)
+    np.testing.assert_array_equal(np.sign(O.rmsnorm(X, w, 1e-5)), np.sign(X))
+    # the gain multiplies columns; the normaliser is one number per row
+    np.testing.assert_allclose(O.rmsnorm(X, w, 1e-5), O.rmsnorm(X, np.ones(96), 1e-5) * w, rtol=1e-15)
+    r = X[:, :1] / O.rmsnorm(X, np.ones(96), 1e-5)[:, :1]
+    np.testing.assert_allclose(r[:, 0], np.sqrt(np.mean(X * X, axis=1) + 1e-5), rtol=1e-13)
+    # a constant row c normalises to sign(c) * w when eps = 0
+    np.testing.assert_allclose(O.rmsnorm(np.full((1, 5), -2.5), np.arange(1.0, 6.0), 0.0), [[-1, -2, -3, -4, -5]],
+                               rtol=1e-15)
