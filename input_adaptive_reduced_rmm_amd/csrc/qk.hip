@@ -51,6 +51,7 @@ __host__ __device__ __forceinline__ int64_t tiles_before(int64_t x, int64_t c0, 
 }
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kPitch = 68;                                  // staging row pitch (floats)
 constexpr int kOperandBytes = 2 * kT * mg::kBK * 2;        // A and B tiles
 constexpr int kStageBytes = 4 * 32 * kPitch * 4;           // 4 waves x 32 rows
@@ -61,12 +62,20 @@ constexpr int kSmemBytes = kOperandBytes > kStageBytes ? kOperandBytes : kStageB
 #define RMM_QK_BPC 2
 #endif
 
-template <bool BVEC>
+// BSTORE: S is written with buffer stores whose resource drops rows past Lq
+// and whose offsets drop columns past Lk, so every tile issues the same number
+// of stores on every path (no branch around them).  The next tile's loads go
+// out before them, and the wait for those loads then leaves this tile's stores
+// in flight (one counter tracks loads and stores in issue order) instead of
+// draining them before the next tile's product.  Needs 32 rows of S within one
+// resource (4 GiB), 16-byte aligned rows and Lk % 4 == 0.
+template <bool BVEC, bool BSTORE>
 __global__ __launch_bounds__(256) void qk_persistent(QkArgs g) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
   uint16_t *As = reinterpret_cast<uint16_t *>(smem);
   uint16_t *Bs = As + kT * mg::kBK;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: store resources stay scalar
   const int wm = wave >> 1, wn = wave & 1;
   const int lrow = lane & 31, lk = lane >> 5;
   const int akc = tid & 7;
@@ -123,7 +132,17 @@ __global__ __launch_bounds__(256) void qk_persistent(QkArgs g) {
   int64_t t = blockIdx.x;
   if (gridDim.x % 8 == 0) t = (int64_t)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
   Tile cur = tile_at(t < t_end ? t : 0);
-  if (t < t_end) issue(cur, 0);
+  if (t < t_end) {
+    issue(cur, 0);
+    if constexpr (BSTORE) {
+      // Dropped stores (empty resource): the loop is entered with the same
+      // count of stores behind the first loads as every later tile, so the
+      // wait at its top is for the loads only.
+      const rsrc_t none = mg::make_rsrc(g.S, 0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) __builtin_amdgcn_raw_buffer_store_b32(0, none, (int)mg::kOOB - 64 * q, 0, 0);
+    }
+  }
   for (; t < t_end; t += t_step) {
     f32x16_t acc[2][2];
 #pragma unroll
@@ -191,6 +210,8 @@ __global__ __launch_bounds__(256) void qk_persistent(QkArgs g) {
     float *stage = reinterpret_cast<float *>(smem) + wave * (32 * kPitch);
     const bool full_cols = ti.n0 + kT <= g.Lk && (g.lds % 4 == 0) &&
                            (reinterpret_cast<uintptr_t>(Sh) % 16 == 0);
+    // lane part of a store offset: row lane/16 of a 4-row group, 4 columns
+    const uint32_t vo = (uint32_t)(((lane >> 4) * g.lds + (lane & 15) * 4) * 4);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -202,6 +223,25 @@ __global__ __launch_bounds__(256) void qk_persistent(QkArgs g) {
       __builtin_amdgcn_wave_barrier();
       const int64_t rbase = ti.m0 + wm * 64 + i * 32;
       const int64_t cbase = ti.n0 + wn * 64;
+      if constexpr (BSTORE) {
+        // Resource over this wave's 32 x 64 block: rows past Lq and, in the
+        // last row, columns past Lk fall outside it; a 4-column group past Lk
+        // in other rows gets an offset outside it (Lk % 4 == 0 here).
+        const int64_t rows = g.Lq - rbase < 32 ? g.Lq - rbase : 32;
+        const int64_t ncols = g.Lk - cbase < 64 ? g.Lk - cbase : 64;
+        const rsrc_t rs = mg::make_rsrc(Sh + rbase * g.lds + cbase,
+                                        rows > 0 && ncols > 0 ? ((uint64_t)(rows - 1) * g.lds + ncols) * 4 : 0);
+        const bool col_ok = (lane & 15) * 4 < ncols;
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const f32x4_t v = *reinterpret_cast<const f32x4_t *>(&stage[(it * 4 + (lane >> 4)) * kPitch +
+                                                                       (lane & 15) * 4]);
+          const uint32_t off = col_ok ? vo + (uint32_t)(it * 4 * g.lds * 4) : mg::kOOB;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, v), rs, (int)off, 0, 2 /* nt */);
+        }
+        __builtin_amdgcn_wave_barrier();
+        continue;
+      }
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
         const int rr = it * 4 + (lane >> 4);
@@ -273,13 +313,20 @@ hipError_t launch_qk(const void *Apacked, const int32_t *idx_clean, const void *
   g.total = g.per_head * hq;
   if (g.total == 0) return hipSuccess;
   const bool bvec = reinterpret_cast<uintptr_t>(Kt) % 16 == 0 && ldkt % 8 == 0 && kt_hs % 8 == 0;
+  // Stores left in flight pay off when a tile has two K tiles (k_pad = 128:
+  // 4.10 -> 3.80 ms for 32 heads x 16384^2 causal); with one K tile, letting
+  // them drain at the next tile's first wait measured faster (3.02 against
+  // 3.29 ms at k_pad = 64).
+  const bool bstore = k_pad > mg::kBK && reinterpret_cast<uintptr_t>(S) % 16 == 0 && lds % 4 == 0 &&
+                      s_hs % 4 == 0 && Lk % 4 == 0 && (uint64_t)32 * lds * 4 < mg::kMaxRecords;
   int64_t grid = 256 * RMM_QK_BPC;
   if (grid > g.total) grid = g.total;
   KernelTimer timer("qk_gemm", st);
-  if (bvec)
-    hipLaunchKernelGGL(qk_persistent<true>, dim3((unsigned)grid), dim3(256), 0, st, g);
-  else
-    hipLaunchKernelGGL(qk_persistent<false>, dim3((unsigned)grid), dim3(256), 0, st, g);
+  const dim3 gr((unsigned)grid), blk(256);
+  if (bvec && bstore) hipLaunchKernelGGL((qk_persistent<true, true>), gr, blk, 0, st, g);
+  else if (bvec) hipLaunchKernelGGL((qk_persistent<true, false>), gr, blk, 0, st, g);
+  else if (bstore) hipLaunchKernelGGL((qk_persistent<false, true>), gr, blk, 0, st, g);
+  else hipLaunchKernelGGL((qk_persistent<false, false>), gr, blk, 0, st, g);
   return hipGetLastError();
 }
 

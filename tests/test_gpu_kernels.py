@@ -222,6 +222,32 @@ def test_qk_causal_skips_only_upper_tiles(Lq, Lk, Hq, Hkv, k):
         assert rel_fro(got[allowed], want[allowed]) < TOL_BF16
 
 
+@pytest.mark.parametrize("k", [40, 100])   # one and two K tiles (the two store paths)
+@pytest.mark.parametrize("Lq,Lk,causal", [(300, 300, True), (300, 300, False), (200, 332, True), (77, 36, False),
+                                           (77, 36, True), (129, 129, False), (64, 128, True)])
+def test_qk_strided_output_writes_only_its_block(Lq, Lk, causal, k):
+    """S is a view into a larger NaN-filled buffer: every element outside the view
+    (padding columns before and after each row, rows past Lq, other heads) stays
+    NaN, and the view holds the reduced product where the mask allows."""
+    Hq, Hkv = 3, 1
+    Q, _, _ = synth.attention_qkv(11, 77, Lq, Hq, Hkv, 128)
+    _, Kt, _ = synth.attention_qkv(12, 77, Lk, Hq, Hkv, 128)
+    full = torch.full((Hq + 1, Lq + 5, Lk + 12), float("nan"), device=DEV)
+    view = full[:Hq, :Lq, 4:4 + Lk]
+    S, idx = R.rmm_qk(dev_tensor(Q, BF), dev_tensor(Kt, BF), k, S=view, causal=causal)
+    F = full.cpu().numpy()
+    outside = np.ones(F.shape, dtype=bool)
+    outside[:Hq, :Lq, 4:4 + Lk] = False
+    assert np.isnan(F[outside]).all(), "a store landed outside S"
+    idx = idx.cpu().numpy()
+    allowed = np.arange(Lk)[None, :] <= np.arange(Lq)[:, None] + (Lk - Lq) if causal else np.ones((Lq, Lk), bool)
+    for h in range(Hq):
+        want = oracle.reduced_product(Q[:, h, :], Kt[oracle.kv_head(h, Hq, Hkv)], idx[h][:k])
+        got = F[h, :Lq, 4:4 + Lk]
+        assert not np.isnan(got[allowed]).any()
+        assert rel_fro(got[allowed], want[allowed]) < TOL_BF16
+
+
 @pytest.mark.parametrize("Lq,Lk,Hq,Hkv,k", [(300, 300, 4, 2, 150), (200, 330, 2, 1, 165), (1000, 1000, 2, 2, 333),
                                             (700, 700, 2, 1, 1), (640, 640, 2, 2, 640)])
 def test_pv_causal_never_uses_upper_triangle(Lq, Lk, Hq, Hkv, k):
