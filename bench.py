@@ -54,6 +54,8 @@ def parse():
                     help="replay the step from a captured HIP graph (launch-bound shapes such as decode batches)")
     ap.add_argument("--no-fused-attention", action="store_true",
                     help="skip the separate timing of the fused reduced attention (rmm_attention)")
+    ap.add_argument("--no-producers", action="store_true",
+                    help="skip the separate timing of the producer-fused scoring kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -391,6 +393,67 @@ def decode_attention(R, layer, steps, warmup, dense=True):
     return out
 
 
+def producer_fused(R, wl, args, steps, warmup, dev):
+    """Time the producers that write a projection's A together with its column
+    scores, on the layer's shapes: rmm_rmsnorm_scored (the q/k/v/gate/up input,
+    m x hidden) and rmm_swiglu_scored (the down input, m x mlp), each beside the
+    separate rmm_colnorm pass over the same output that it makes unnecessary.
+    Bytes are the algorithmic ones (rmsnorm: read X, write Y; swiglu: read G
+    and U, write H); inputs are seeded normal draws resident in HBM."""
+    import torch
+
+    sel = _selected(wl, args)
+    q = next((l for l in sel if l.name == "q"), None)
+    dn = next((l for l in sel if l.name == "down"), None)
+    if wl.dtype != "bf16" or (q is None and dn is None):
+        return None
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    bf = torch.bfloat16
+    res = {}
+
+    def timed(fn):
+        class _S:
+            def step(self, tagged=False):
+                fn()
+        return time_steps(_S(), steps, warmup)[0]
+
+    def entry(shape, ms, nbytes, ms_colnorm):
+        rate = nbytes / (ms * 1e-3) / 1e9
+        return {"shape": list(shape), "ms": round(ms, 4), "gbs": round(rate, 1),
+                "frac": round(rate / PEAK_HBM_GBS, 4), "colnorm_ms": round(ms_colnorm, 4)}
+
+    if q is not None and q.d % 512 == 0 and q.d <= 8192:
+        m, d = q.m, q.d
+        X = torch.randn((m, d), generator=g, device=dev).mul_(
+            torch.rand((m, 1), generator=g, device=dev).mul_(20.0).add_(0.05)).to(bf)
+        w = torch.rand(d, generator=g, device=dev).mul_(1.3).add_(0.2).to(bf)
+        Y = torch.empty((m, d), dtype=bf, device=dev)
+        s = torch.empty(d, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(R.rmm_rmsnorm_scored_workspace_bytes(m, d), 256), dtype=torch.uint8, device=dev)
+        wsc = torch.empty(max(R.rmm_colnorm_workspace_bytes(torch.bfloat16, m, d, 1), 256), dtype=torch.uint8,
+                          device=dev)
+        ms = timed(lambda: R.rmm_rmsnorm_scored(X, w, 1e-5, Y=Y, scores=s, ws=ws))
+        ms_c = timed(lambda: R.rmm_colnorm(Y, out=s, ws=wsc))
+        res["rmsnorm_scored"] = entry((m, d), ms, 2 * m * d * 2, ms_c)
+        del X, w, Y, s, ws, wsc
+    if dn is not None and dn.d % 8 == 0:
+        m, n = dn.m, dn.d
+        G = torch.randn((m, n), generator=g, device=dev).to(bf)
+        U = torch.randn((m, n), generator=g, device=dev).to(bf)
+        H = torch.empty((m, n), dtype=bf, device=dev)
+        s = torch.empty(n, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(R.rmm_swiglu_scored_workspace_bytes(m, n), 256), dtype=torch.uint8, device=dev)
+        wsc = torch.empty(max(R.rmm_colnorm_workspace_bytes(torch.bfloat16, m, n, 1), 256), dtype=torch.uint8,
+                          device=dev)
+        ms = timed(lambda: R.rmm_swiglu_scored(G, U, H=H, scores=s, ws=ws))
+        ms_c = timed(lambda: R.rmm_colnorm(H, out=s, ws=wsc))
+        res["swiglu_scored"] = entry((m, n), ms, 3 * m * n * 2, ms_c)
+        del G, U, H, s, ws, wsc
+    torch.cuda.empty_cache()
+    return res
+
+
 def csrc_sha256():
     import glob
     import hashlib
@@ -545,6 +608,10 @@ def main():
         fused["step_qk_pv_ms"] = round(qkpv_ms, 4)
         print(f"[bench] fused attention {fused['rho']['ms']:.3f} ms", file=sys.stderr, flush=True)
 
+    producers = None
+    if not args.no_producers:
+        producers = producer_fused(R, wl, args, args.steps, args.warmup, dev)
+
     speedup = dense_ms = None
     if not args.no_dense:
         run1 = Runner(R, layer, dev, rho_scale_one=True)
@@ -575,6 +642,7 @@ def main():
         "rho1_ms_per_step": round(dense_ms, 4) if dense_ms else None,
         "gemm_kept_mfma_frac": round(mfma_frac, 4) if mfma_frac is not None else None,
         "roofline": roof, "cpu_baseline": cpu, "kernels": detail, "fused_attention": fused,
+        "producer_fused": producers,
     }
     print(json.dumps(out), flush=True)
 
