@@ -242,6 +242,46 @@ def time_steps(runner, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
+def step_distribution(runner, steps, flush_buf=None):
+    """Per-step times (HIP events around each step): median, p10 and p90 in ms.
+    With `flush_buf` (>= 1 GiB), the buffer is overwritten before every step,
+    outside the timed span, so the 256 MB Infinity Cache holds none of the
+    step's operands when it starts (cold cache)."""
+    import numpy as np
+    import torch
+
+    ts = []
+    for _ in range(steps):
+        if flush_buf is not None:
+            flush_buf.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        runner.step()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    a = np.asarray(ts)
+    return {"median_ms": round(float(np.median(a)), 4), "p10_ms": round(float(np.percentile(a, 10)), 4),
+            "p90_ms": round(float(np.percentile(a, 90)), 4), "steps": steps}
+
+
+def torch_matmul_context(layer, steps, warmup):
+    """Context only: the step's projections as dense torch.matmul (hipBLASLt) on
+    the same A and B, with no selection (ms per step)."""
+    import torch
+
+    outs = [torch.empty((l["m"], l["n"]), dtype=layer["dtype"], device=l["A"].device) for l in layer["linears"]]
+
+    class _D:
+        def step(self, tagged=False):
+            for l, o in zip(layer["linears"], outs):
+                torch.matmul(l["A"], l["B"], out=o)
+
+    ms, _ = time_steps(_D(), steps, warmup)
+    del outs
+    return round(ms, 4)
+
+
 def kernel_breakdown(runner, steps):
     """Per tag/kernel average launch durations (HIP events recorded by the library)."""
     import torch
@@ -554,6 +594,11 @@ def main():
     run = Runner(R, layer, dev)
     ms, wall = time_steps(GraphStep(run) if args.graph else run, args.steps, args.warmup)
     print(f"[bench] rho step {ms:.3f} ms (wall {wall:.3f})", file=sys.stderr, flush=True)
+    stepper = GraphStep(run) if args.graph else run
+    hot = step_distribution(stepper, max(args.steps, 20))
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = step_distribution(stepper, max(args.steps, 20), flush)
+    del flush, stepper
     kern = kernel_breakdown(run, max(2, min(args.steps, 5)))
     flops = dense_flops(layer)
     # Dominant kernel and its roofline.
@@ -598,6 +643,9 @@ def main():
     mfma_frac = (g_fl / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS) if g_ms > 0 else None
     # the step's own Q K^T and P V (P an input), for comparison with the fused call
     qkpv_ms = sum(v["avg_ms"] * v["launches_per_step"] for k, v in kern.items() if k.split("/")[0] in ("qk", "pv"))
+    proj_ms = sum(v["avg_ms"] * v["launches_per_step"] for k, v in kern.items()
+                  if k.split("/")[0] not in ("qk", "pv"))
+    torch_proj_ms = torch_matmul_context(layer, args.steps, args.warmup) if layer["linears"] else None
     run.free()
     del run
     torch.cuda.empty_cache()
@@ -643,6 +691,8 @@ def main():
         "gemm_kept_mfma_frac": round(mfma_frac, 4) if mfma_frac is not None else None,
         "roofline": roof, "cpu_baseline": cpu, "kernels": detail, "fused_attention": fused,
         "producer_fused": producers,
+        "step_times": {"hot": hot, "cold_cache": cold},
+        "context": {"rmm_projections_ms": round(proj_ms, 4), "torch_matmul_projections_ms": torch_proj_ms},
     }
     print(json.dumps(out), flush=True)
 
