@@ -430,6 +430,51 @@ def decode_attention(R, layer, steps, warmup, dense=True):
         ms, _ = time_steps(GraphStep(_One()), max(steps, 20), warmup)
         out[name + "_us"] = round(ms * 1e3, 1)
         del O, If, It, ws
+    out["batch"] = decode_batch(R, layer, steps, warmup, dense)
+    return out
+
+
+def decode_batch(R, layer, steps, warmup, dense=True, nseq=16):
+    """One decode step of `nseq` sequences with their own caches (rmm_attention_decode_batch):
+    context lengths drawn uniformly from [L/4, L] (seeded), the layer's heads and ratio, caches
+    of seeded normal draws; HIP graph replay."""
+    import numpy as np
+    import torch
+
+    at = layer["attention"]
+    L, Hq, Hkv, dh = at["L"], at["Hq"], at["Hkv"], at["dh"]
+    dev = at["Q"].device
+    rng = np.random.default_rng([0, 91, nseq])
+    lens = np.sort(rng.integers(L // 4, L + 1, size=nseq)).astype(np.int32)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    Q = torch.randn((nseq, Hq, dh), generator=g, device=dev).to(torch.bfloat16)
+    Kt = torch.randn((nseq, Hkv, dh, L), generator=g, device=dev).to(torch.bfloat16)
+    V = torch.randn((nseq, L, Hkv, dh), generator=g, device=dev).to(torch.bfloat16)
+    ld = torch.from_numpy(lens).to(dev)
+    out = {"sequences": nseq, "context_min": int(lens.min()), "context_max": int(lens.max()),
+           "launch": "hip graph replay"}
+    ratios = [("rho", R.rmm_k_from_rho(at["rho"], dh), [R.rmm_k_from_rho(at["rho"], int(x)) for x in lens])]
+    if dense:
+        ratios.append(("rho1", dh, [int(x) for x in lens]))
+    for name, kf, kts in ratios:
+        kd = torch.tensor(kts, dtype=torch.int32, device=dev)
+        ktm = max(kts)
+        O = torch.empty((nseq, Hq, dh), dtype=torch.bfloat16, device=dev)
+        If = torch.empty((nseq * Hq, R.rmm_k_pad(kf)), dtype=torch.int32, device=dev)
+        It = torch.empty((nseq * Hq, R.rmm_k_pad(ktm)), dtype=torch.int32, device=dev)
+        ws = torch.empty(R.rmm_attention_decode_batch_workspace_bytes(nseq, Hq, dh, L, ktm), dtype=torch.uint8,
+                         device=dev)
+
+        class _B:
+            def step(self, tagged=False):
+                R.rmm_attention_decode_batch(Q, Kt, V, ld, kd, kf, ktm, O=O, idx_feat=If, idx_tok=It, ws=ws)
+
+        ms, _ = time_steps(GraphStep(_B()), max(steps, 20), warmup)
+        out[name + "_us"] = round(ms * 1e3, 1)
+        del O, If, It, ws
+    del Q, Kt, V
+    torch.cuda.empty_cache()
     return out
 
 

@@ -311,6 +311,55 @@ rmm_status_t rmm_attention(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, in
                            size_t ws_bytes, rmm_stream_t stream);
 
 /*
+ * rmm_attention_decode_batch - one decode step of nseq sequences, each with
+ * its own KV cache: for every (sequence b, query head h) the reduced attention
+ * of the sequence's one new token over its lens[b] cached tokens, as
+ * rmm_attention computes it with Lq = 1 (causal: the new token is the last
+ * position, so it sees the whole context).  Sources: "Alcance de Aplicación"
+ * (feature reduction of Q K^T, token reduction of P V) and "Estrategia de
+ * Selección" (column-norm scores, top-k); the pages state that the method
+ * holds up in autoregressive generation.  With one row, the feature scores
+ * are |q_f| and the token scores are the probabilities p_j.
+ *   Q (device, bf16): element (b, h, f) at Q + b*q_seq_stride + h*q_head_stride + f.
+ *   Kt (device, bf16): feature-major caches, element (b, g, f, j) at
+ *        Kt + b*kt_seq_stride + g*kt_head_stride + f*ldkt + j, ldkt >= Lmax.
+ *   V (device, bf16): element (b, j, g, d) at V + b*v_seq_stride + j*v_tok_stride
+ *        + g*v_head_stride + d; 16-byte aligned rows (V and the three strides
+ *        multiples of 8 elements), else RMM_ERR_UNSUPPORTED.
+ *        Query head h reads kv head floor(h*Hkv/Hq).
+ *   lens (device, int32) [nseq]: context length of each sequence (including
+ *        the new token), clamped to [1, Lmax]; cache positions past it are
+ *        never read for scores and never selected.
+ *   k_tok (device, int32) [nseq]: tokens kept per sequence (the caller's
+ *        ceil(rho * lens[b]), see rmm_k_from_rho), clamped to [1, min(lens[b], kt_max)].
+ *   Lmax: longest context (cache capacity read); kt_max: the largest k_tok
+ *        (1 <= kt_max <= Lmax), which sizes idx_tok rows.
+ *   k_feat: features kept per (sequence, head), 1 <= k_feat <= dh; dh must be 128.
+ *   O (device, bf16): element (b, h, d) at O + b*o_seq_stride + h*o_head_stride + d.
+ *   idx_feat (device, int32) [nseq*Hq][rmm_k_pad(k_feat)], row b*Hq + h: kept
+ *        features ascending, then -1.
+ *   idx_tok (device, int32) [nseq*Hq][rmm_k_pad(kt_max)]: kept tokens of
+ *        each row ascending, then -1 (ties to the lower index).
+ *   tok_scores (device, float, optional) [nseq*Hq][Lmax]: token scores
+ *        (-inf past lens[b]).
+ *   ws: rmm_attention_decode_batch_workspace_bytes(nseq, Hq, dh, Lmax, kt_max)
+ *        bytes, 256-byte aligned.
+ * nseq * Hq must not exceed 65535.  Nothing is allocated; the call is
+ * asynchronous on `stream` and can be captured in a HIP graph.
+ */
+size_t rmm_attention_decode_batch_workspace_bytes(int64_t nseq, int64_t Hq, int64_t dh, int64_t Lmax,
+                                                  int64_t kt_max);
+rmm_status_t rmm_attention_decode_batch(const void *Q, int64_t q_seq_stride, int64_t q_head_stride,
+                                        const void *Kt, int64_t kt_seq_stride, int64_t kt_head_stride,
+                                        int64_t ldkt, const void *V, int64_t v_seq_stride,
+                                        int64_t v_tok_stride, int64_t v_head_stride, const int32_t *lens,
+                                        const int32_t *k_tok, int64_t nseq, int64_t Hq, int64_t Hkv,
+                                        int64_t dh, int64_t Lmax, int64_t k_feat, int64_t kt_max, void *O,
+                                        int64_t o_seq_stride, int64_t o_head_stride, int32_t *idx_feat,
+                                        int32_t *idx_tok, float *tok_scores, void *ws, size_t ws_bytes,
+                                        rmm_stream_t stream);
+
+/*
  * Per-kernel timing diagnostics (not part of the method; for measurement).
  * When enabled, each kernel the library enqueues is bracketed by two HIP
  * events recorded on its launch stream and filed under "<tag>/<kernel>"

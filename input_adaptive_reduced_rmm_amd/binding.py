@@ -16,11 +16,12 @@ import torch
 __all__ = [
     "RMMError", "load", "lib_path",
     "rmm_version", "rmm_k_from_rho", "rmm_k_pad",
-    "rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_gemm_w8", "rmm_swiglu_scored", "rmm_rmsnorm_scored", "rmm_qk", "rmm_pv",
+    "rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_gemm_w8", "rmm_swiglu_scored", "rmm_rmsnorm_scored", "rmm_attention_decode_batch", "rmm_qk", "rmm_pv",
     "rmm_attention",
     "rmm_colnorm_workspace_bytes", "rmm_topk_workspace_bytes", "rmm_gemm_workspace_bytes",
     "rmm_qk_workspace_bytes", "rmm_pv_workspace_bytes", "rmm_attention_workspace_bytes",
     "rmm_gemm_w8_workspace_bytes", "rmm_swiglu_scored_workspace_bytes", "rmm_rmsnorm_scored_workspace_bytes",
+    "rmm_attention_decode_batch_workspace_bytes",
     "rmm_linear", "timing",
 ]
 
@@ -72,6 +73,10 @@ _PROTOS = {
     "rmm_swiglu_scored_workspace_bytes": (_sz, [_i64, _i64]),
     "rmm_swiglu_scored": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp]),
     "rmm_rmsnorm_scored_workspace_bytes": (_sz, [_i64, _i64]),
+    "rmm_attention_decode_batch_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+    "rmm_attention_decode_batch": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
+                                                  _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _i64,
+                                                  _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "rmm_rmsnorm_scored": (ctypes.c_int, [_vp, _i64, _vp, ctypes.c_float, _i64, _i64, _vp, _i64, _vp, _vp, _sz,
                                           _vp]),
     "rmm_gemm_w8": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _sz,
@@ -404,6 +409,47 @@ def rmm_attention(Q: torch.Tensor, Kt: torch.Tensor, V: torch.Tensor, k_feat: in
                              Kt.stride(1), _ptr(V), V.stride(0), V.stride(1), int(k_feat), int(k_tok),
                              1 if causal else 0, _ptr(O), O.stride(0), O.stride(1), _ptr(idx_feat),
                              _ptr(idx_tok), _ptr(tok_scores), _ptr(o_scores), _ptr(ws), wsb, _stream(dev)))
+    return O, idx_feat, idx_tok
+
+
+def rmm_attention_decode_batch_workspace_bytes(nseq: int, Hq: int, dh: int, Lmax: int, kt_max: int) -> int:
+    return int(load().rmm_attention_decode_batch_workspace_bytes(nseq, Hq, dh, Lmax, kt_max))
+
+
+def rmm_attention_decode_batch(Q: torch.Tensor, Kt: torch.Tensor, V: torch.Tensor, lens: torch.Tensor,
+                               k_tok: torch.Tensor, k_feat: int, kt_max: int | None = None,
+                               O: torch.Tensor | None = None, idx_feat: torch.Tensor | None = None,
+                               idx_tok: torch.Tensor | None = None, tok_scores: torch.Tensor | None = None,
+                               ws: torch.Tensor | None = None):
+    """One decode step of B sequences.  Q [B, Hq, dh] (one new token each), Kt [B, Hkv, dh, Lmax],
+    V [B, Lmax, Hkv, dh] (bf16), lens and k_tok int32 [B] on the device ->
+    (O bf16 [B, Hq, dh], idx_feat int32 [B*Hq, k_pad(k_feat)], idx_tok int32 [B*Hq, k_pad(kt_max)])."""
+    lib = load()
+    dev = _dev(Q, Kt, V, lens, k_tok)
+    if Q.dtype != torch.bfloat16 or Kt.dtype != torch.bfloat16 or V.dtype != torch.bfloat16:
+        raise TypeError("rmm_attention_decode_batch takes bfloat16 Q, Kt and V")
+    if lens.dtype != torch.int32 or k_tok.dtype != torch.int32 or not lens.is_contiguous() or not k_tok.is_contiguous():
+        raise TypeError("lens and k_tok must be contiguous int32 device tensors")
+    if Q.dim() != 3 or Kt.dim() != 4 or V.dim() != 4 or Q.stride(2) != 1 or Kt.stride(3) != 1 or V.stride(3) != 1:
+        raise ValueError("Q [B, Hq, dh], Kt [B, Hkv, dh, Lmax], V [B, Lmax, Hkv, dh] with unit innermost stride")
+    B, Hq, dh = Q.shape
+    Hkv, Lmax = Kt.shape[1], Kt.shape[3]
+    if Kt.shape[0] != B or Kt.shape[2] != dh or V.shape[0] != B or V.shape[1] != Lmax or V.shape[2] != Hkv \
+            or V.shape[3] != dh or lens.numel() != B or k_tok.numel() != B:
+        raise ValueError("inconsistent shapes")
+    kt_max = Lmax if kt_max is None else int(kt_max)
+    if O is None:
+        O = torch.empty((B, Hq, dh), dtype=torch.bfloat16, device=dev)
+    if idx_feat is None:
+        idx_feat = torch.empty((B * Hq, rmm_k_pad(k_feat)), dtype=torch.int32, device=dev)
+    if idx_tok is None:
+        idx_tok = torch.empty((B * Hq, rmm_k_pad(kt_max)), dtype=torch.int32, device=dev)
+    ws, wsb = _ws(rmm_attention_decode_batch_workspace_bytes(B, Hq, dh, Lmax, kt_max), dev, ws)
+    _check(lib.rmm_attention_decode_batch(
+        _ptr(Q), Q.stride(0), Q.stride(1), _ptr(Kt), Kt.stride(0), Kt.stride(1), Kt.stride(2),
+        _ptr(V), V.stride(0), V.stride(1), V.stride(2), _ptr(lens), _ptr(k_tok), B, Hq, Hkv, dh, Lmax,
+        int(k_feat), kt_max, _ptr(O), O.stride(0), O.stride(1), _ptr(idx_feat), _ptr(idx_tok),
+        _ptr(tok_scores) if tok_scores is not None else None, _ptr(ws), wsb, _stream(dev)))
     return O, idx_feat, idx_tok
 
 

@@ -702,3 +702,115 @@ RMM_API rmm_status_t rmm_attention(const void *Q, int64_t Lq, int64_t Hq, int64_
   return hip_status(rmm::launch_colnorm_finish(d.opart, (Lq + 255) / 256, Hq * dh, o_scores, st),
                     "attention output scores launch");
 }
+
+// ------------------------------------------------------------------ batched decode attention
+// One new token for each of nseq sequences, each over its own cache: the rows
+// of the decode passes are the (sequence, head) pairs.
+struct AttnBatchLayout {
+  size_t sc, S, pstat, nml, tok, opart, total;
+};
+static AttnBatchLayout attn_batch_layout(int64_t nseq, int64_t Hq, int64_t Lmax, int64_t kt_max) {
+  const int64_t rows = nseq * Hq;
+  const rmm::AttnDecodeSizes z = rmm::attn_decode_sizes(1, Lmax, rows, kt_max);
+  AttnBatchLayout L;
+  Carve c(nullptr);
+  L.sc = c.off;    c.take((size_t)rows * 128 * 4);
+  L.S = c.off;     c.take(z.s_bytes);
+  L.pstat = c.off; c.take(z.pstat_bytes);
+  L.nml = c.off;   c.take(z.nml_bytes);
+  L.tok = c.off;   c.take((size_t)rows * Lmax * 4);
+  L.opart = c.off; c.take(z.opart_bytes);
+  L.total = c.off;
+  return L;
+}
+
+RMM_API size_t rmm_attention_decode_batch_workspace_bytes(int64_t nseq, int64_t Hq, int64_t dh, int64_t Lmax,
+                                                          int64_t kt_max) {
+  if (nseq < 1 || Hq < 1 || dh != 128 || Lmax < 1 || kt_max < 1) return 0;
+  return attn_batch_layout(nseq, Hq, Lmax, kt_max).total;
+}
+
+RMM_API rmm_status_t rmm_attention_decode_batch(
+    const void *Q, int64_t q_seq_stride, int64_t q_head_stride, const void *Kt, int64_t kt_seq_stride,
+    int64_t kt_head_stride, int64_t ldkt, const void *V, int64_t v_seq_stride, int64_t v_tok_stride,
+    int64_t v_head_stride, const int32_t *lens, const int32_t *k_tok, int64_t nseq, int64_t Hq, int64_t Hkv,
+    int64_t dh, int64_t Lmax, int64_t k_feat, int64_t kt_max, void *O, int64_t o_seq_stride,
+    int64_t o_head_stride, int32_t *idx_feat, int32_t *idx_tok, float *tok_scores, void *ws, size_t ws_bytes,
+    rmm_stream_t stream) {
+  if (!Q || !Kt || !V || !lens || !k_tok || !O || !idx_feat || !idx_tok)
+    return fail(RMM_ERR_INVALID_ARG, "attention_decode_batch: NULL pointer");
+  if (nseq < 1 || Lmax < 1 || Lmax >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "attention_decode_batch: bad nseq or Lmax");
+  if (Hq < 1 || Hkv < 1 || Hkv > Hq || Hq % Hkv != 0 || nseq * Hq > kMaxBatch)
+    return fail(RMM_ERR_INVALID_ARG,
+                "attention_decode_batch: need 1 <= Hkv <= Hq, Hq %% Hkv == 0 and nseq * Hq <= 65535");
+  if (dh != 128) return fail(RMM_ERR_UNSUPPORTED, "attention_decode_batch: needs dh == 128");
+  if (k_feat < 1 || k_feat > dh) return fail(RMM_ERR_INVALID_ARG, "attention_decode_batch: need 1 <= k_feat <= dh");
+  if (kt_max < 1 || kt_max > Lmax) return fail(RMM_ERR_INVALID_ARG, "attention_decode_batch: need 1 <= kt_max <= Lmax");
+  if (q_head_stride < 0 || q_seq_stride < 0 || kt_head_stride < 0 || kt_seq_stride < 0 || ldkt < Lmax ||
+      v_tok_stride < dh || v_head_stride < 0 || v_seq_stride < 0 || o_head_stride < 0 || o_seq_stride < 0)
+    return fail(RMM_ERR_INVALID_ARG, "attention_decode_batch: bad stride");
+  if (!aligned(Q, 2) || !aligned(Kt, 2) || !aligned(O, 2) || !aligned(lens, 4) || !aligned(k_tok, 4) ||
+      !aligned(idx_feat, 4) || !aligned(idx_tok, 4) || (tok_scores && !aligned(tok_scores, 4)))
+    return fail(RMM_ERR_INVALID_ARG, "attention_decode_batch: misaligned pointer");
+  if (!aligned(V, 16) || v_tok_stride % 8 != 0 || v_head_stride % 8 != 0 || v_seq_stride % 8 != 0)
+    return fail(RMM_ERR_UNSUPPORTED, "attention_decode_batch: value rows must be 16-byte aligned");
+  const size_t need = rmm_attention_decode_batch_workspace_bytes(nseq, Hq, dh, Lmax, kt_max);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(RMM_ERR_WORKSPACE, "attention_decode_batch: workspace needs %zu bytes (256-byte aligned)", need);
+  char *w = static_cast<char *>(ws);
+  hipStream_t st = (hipStream_t)stream;
+  const AttnBatchLayout D = attn_batch_layout(nseq, Hq, Lmax, kt_max);
+  const int64_t kfp = rmm_k_pad(k_feat), ktp = rmm_k_pad(kt_max), rows = nseq * Hq;
+  float *sc = reinterpret_cast<float *>(w + D.sc);
+  float *tokd = tok_scores ? tok_scores : reinterpret_cast<float *>(w + D.tok);
+  hipError_t he = rmm::launch_dec_qabs(Q, q_seq_stride, q_head_stride, nseq, Hq, sc, st);
+  if (he != hipSuccess) return hip_status(he, "attention_decode_batch feature scores launch");
+  he = rmm::launch_topk(sc, rows, dh, k_feat, kfp, idx_feat, st);
+  if (he != hipSuccess) return hip_status(he, "attention_decode_batch feature topk launch");
+  rmm::AttnDecodeDesc dd{};
+  dd.Q = Q;
+  dd.q_ts = dh;
+  dd.q_hs = q_head_stride;
+  dd.Kt = Kt;
+  dd.kt_hs = kt_head_stride;
+  dd.ldkt = ldkt;
+  dd.V = V;
+  dd.v_ts = v_tok_stride;
+  dd.v_hs = v_head_stride;
+  dd.I = idx_feat;
+  dd.J = idx_tok;
+  dd.S = reinterpret_cast<float *>(w + D.S);
+  dd.pstat = reinterpret_cast<float *>(w + D.pstat);
+  dd.nml = reinterpret_cast<float *>(w + D.nml);
+  dd.tok = tokd;
+  dd.opart = reinterpret_cast<float *>(w + D.opart);
+  dd.O = O;
+  dd.o_ts = dh;
+  dd.o_hs = o_head_stride;
+  dd.o_scores = nullptr;
+  dd.hq = Hq;
+  dd.hkv = Hkv;
+  dd.Lq = 1;
+  dd.Lk = Lmax;
+  dd.kf = k_feat;
+  dd.kf_pad = kfp;
+  dd.kt = kt_max;
+  dd.kt_pad = ktp;
+  dd.causal = true;   // the new token is the last position of its sequence
+  dd.nseq = nseq;
+  dd.q_ss = q_seq_stride;
+  dd.kt_ss = kt_seq_stride;
+  dd.v_ss = v_seq_stride;
+  dd.o_ss = o_seq_stride;
+  dd.lens = lens;
+  dd.kts = k_tok;
+  he = rmm::launch_attn_decode(0, dd, st);
+  if (he != hipSuccess) return hip_status(he, "attention_decode_batch scores launch");
+  he = rmm::launch_attn_decode(1, dd, st);
+  if (he != hipSuccess) return hip_status(he, "attention_decode_batch token scores launch");
+  he = rmm::launch_topk(tokd, rows, Lmax, kt_max, ktp, idx_tok, st, k_tok, (int)Hq);
+  if (he != hipSuccess) return hip_status(he, "attention_decode_batch token topk launch");
+  he = rmm::launch_attn_decode(2, dd, st);
+  if (he != hipSuccess) return hip_status(he, "attention_decode_batch output launch");
+  return hip_status(rmm::launch_attn_decode(3, dd, st), "attention_decode_batch output merge launch");
+}

@@ -20,6 +20,12 @@
 //               asked) forms the column scores of O.
 // Everything is float32 except the bf16 inputs and O; all sums run in a fixed
 // order, so results are deterministic.
+//
+// A batch of sequences (a decode step over several caches) runs through the
+// same passes with the (sequence, head) pairs as the rows: each pair reads
+// its own sequence's Q, K and V at the sequence strides, its context length
+// and kept-token count come from device arrays, and keys past a sequence's
+// length score -inf (never selected, weight zero).
 #include "rmm_internal.h"
 #include "timing.h"
 
@@ -55,7 +61,35 @@ struct DecArgs {
   int64_t hq, hkv, Lq, Lk, kf, kf_pad, kt, kt_pad, off;
   int causal, nblk, nsplit;
   float c2;
+  // batch of sequences: row r = b * hq + h; Lk is the longest context
+  int64_t q_ss, kt_ss, v_ss, o_ss;
+  const int32_t *lens;    // [nseq] context lengths (null: Lk for all)
+  const int32_t *kts;     // [nseq] kept tokens (null: kt for all)
+  int64_t nrows;          // nseq * hq: rows of I, J, S, pstat, nml, tok and opart
 };
+
+// The sequence of row r, its context length, its causal offset and its
+// kept-token count.
+struct SeqRow {
+  int64_t b, h, Lk, off, kt;
+};
+__device__ __forceinline__ SeqRow seq_row(const DecArgs &g, int64_t r) {
+  SeqRow q;
+  q.b = r / g.hq;
+  q.h = r - q.b * g.hq;
+  q.Lk = g.Lk;
+  if (g.lens) {
+    const int64_t L = g.lens[q.b];
+    q.Lk = L < 1 ? 1 : (L > g.Lk ? g.Lk : L);
+  }
+  q.off = q.Lk - g.Lq;
+  q.kt = g.kt;
+  if (g.kts) {   // clamped to [1, min(Lk of the row, kt)] as the top-k clamps it
+    const int64_t k = g.kts[q.b], kmax = q.Lk < g.kt ? q.Lk : g.kt;
+    q.kt = k < 1 ? 1 : (k > kmax ? kmax : k);
+  }
+  return q;
+}
 
 // Block-wide reduction of LQ values per thread (max or sum); returns the result
 // to every thread.  red: LDS scratch of 4 * LQ floats.
@@ -90,21 +124,23 @@ __global__ __launch_bounds__(kDB) void dec_scores_kernel(DecArgs g) {
   __shared__ float red[4 * LQ];
   const int tid = threadIdx.x;
   const int blk = blockIdx.x;
-  const int64_t h = blockIdx.y, grp = h * g.hkv / g.hq;
+  const int64_t h = blockIdx.y;   // row: sequence * hq + head
+  const SeqRow sr = seq_row(g, h);
+  const int64_t grp = sr.h * g.hkv / g.hq;
   const int Lq = (int)g.Lq, kf = (int)g.kf;
   if (tid < 128) sI[tid] = tid < kf ? g.I[h * g.kf_pad + tid] : 0;
   __syncthreads();
   for (int e = tid; e < LQ * 128; e += kDB) {
     const int i = e / 128, f = e % 128;
-    sq[i][f] = (i < Lq && f < kf) ? bf16_to_f32(g.Q[i * g.q_ts + h * g.q_hs + sI[f]]) : 0.f;
+    sq[i][f] = (i < Lq && f < kf) ? bf16_to_f32(g.Q[sr.b * g.q_ss + i * g.q_ts + sr.h * g.q_hs + sI[f]]) : 0.f;
   }
   __syncthreads();
   const int64_t j = (int64_t)blk * kDB + tid;
   float s[LQ];
 #pragma unroll
   for (int i = 0; i < LQ; ++i) s[i] = 0.f;
-  if (j < g.Lk) {
-    const uint16_t *kb = g.Kt + grp * g.kt_hs + j;
+  if (j < sr.Lk) {
+    const uint16_t *kb = g.Kt + sr.b * g.kt_ss + grp * g.kt_hs + j;
     int f = 0;
     for (; f + 8 <= kf; f += 8) {
       float kv[8];
@@ -134,7 +170,7 @@ __global__ __launch_bounds__(kDB) void dec_scores_kernel(DecArgs g) {
   // masked scores are -inf: they add nothing to any later sum
 #pragma unroll
   for (int i = 0; i < LQ; ++i) {
-    const bool vis = j < g.Lk && i < Lq && (!g.causal || j <= i + g.off);
+    const bool vis = j < sr.Lk && i < Lq && (!g.causal || j <= i + sr.off);
     s[i] = vis ? s[i] : kNegInfD;
     if (i < Lq && j < g.Lk) g.S[(h * g.Lq + i) * g.Lk + j] = s[i];
   }
@@ -201,6 +237,10 @@ __global__ __launch_bounds__(kDB) void dec_tok_kernel(DecArgs g) {
   }
   const int64_t j = (int64_t)blk * kDB + tid;
   if (j >= g.Lk) return;
+  if (g.lens && j >= seq_row(g, h).Lk) {   // past this sequence's context: never kept
+    g.tok[h * g.Lk + j] = kNegInfD;
+    return;
+  }
   const float c4 = 2.f * g.c2;
   float t = 0.f;
 #pragma unroll
@@ -219,7 +259,10 @@ __global__ __launch_bounds__(kDB) void dec_out_kernel(DecArgs g) {
   __shared__ float red[4][LQ * 128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x;
-  const int64_t h = blockIdx.y, grp = h * g.hkv / g.hq;
+  const int64_t h = blockIdx.y;   // row: sequence * hq + head
+  const SeqRow sr = seq_row(g, h);
+  const int64_t grp = sr.h * g.hkv / g.hq;
+  const uint16_t *Vs = g.V + sr.b * g.v_ss;
   const int Lq = (int)g.Lq;
   float nmli[LQ];
 #pragma unroll
@@ -233,8 +276,8 @@ __global__ __launch_bounds__(kDB) void dec_out_kernel(DecArgs g) {
     for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
   for (int sub = 0; sub < kTokSub; ++sub) {
     const int64_t t0 = ((int64_t)split * kTokSub + sub) * kDB;
-    if (t0 >= g.kt) break;
-    const int ntok = (int)(g.kt - t0 < kDB ? g.kt - t0 : kDB);
+    if (t0 >= sr.kt) break;   // splits past this row's kept tokens write zero partials
+    const int ntok = (int)(sr.kt - t0 < kDB ? sr.kt - t0 : kDB);
     if (sub > 0) __syncthreads();   // the previous sub-tile's p and rows are consumed
     {
       const int32_t jt = tid < ntok ? g.J[h * g.kt_pad + t0 + tid] : -1;
@@ -253,7 +296,7 @@ __global__ __launch_bounds__(kDB) void dec_out_kernel(DecArgs g) {
     for (int tt = tg; tt < ntok; tt += 16) {
       const int32_t row = sj[tt];
       if (row < 0) continue;
-      const uint4 v = *reinterpret_cast<const uint4 *>(g.V + (int64_t)row * g.v_ts + grp * g.v_hs + dq * 8);
+      const uint4 v = *reinterpret_cast<const uint4 *>(Vs + (int64_t)row * g.v_ts + grp * g.v_hs + dq * 8);
       const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                            bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
 #pragma unroll
@@ -279,7 +322,7 @@ __global__ __launch_bounds__(kDB) void dec_out_kernel(DecArgs g) {
       for (int e = 0; e < 8; ++e) red[wave][i * 128 + dq * 8 + e] = acc[i][e];
   }
   __syncthreads();
-  float *dst = g.opart + ((int64_t)split * g.hq + h) * g.Lq * 128;
+  float *dst = g.opart + ((int64_t)split * g.nrows + h) * g.Lq * 128;
   for (int e = tid; e < Lq * 128; e += kDB) dst[e] = (red[0][e] + red[1][e]) + (red[2][e] + red[3][e]);
 }
 
@@ -294,7 +337,7 @@ __global__ __launch_bounds__(256) void dec_merge_kernel(DecArgs g) {
   for (int e = threadIdx.x; e < Lq * 32; e += 256) {
     const int i = e / 32, d = d0 + e % 32;
     const float *p = g.opart + (h * g.Lq + i) * 128 + d;
-    const int64_t stride = g.hq * g.Lq * 128;
+    const int64_t stride = g.nrows * g.Lq * 128;
     float s = 0.f;
     int sp = 0;
     for (; sp + 8 <= g.nsplit; sp += 8) {
@@ -306,7 +349,8 @@ __global__ __launch_bounds__(256) void dec_merge_kernel(DecArgs g) {
     }
     for (; sp < g.nsplit; ++sp) s += p[(int64_t)sp * stride];
     const uint16_t b = f32_to_bf16(s);
-    g.O[i * g.o_ts + h * g.o_hs + d] = b;
+    const int64_t sb = h / g.hq, sh = h - sb * g.hq;
+    g.O[sb * g.o_ss + i * g.o_ts + sh * g.o_hs + d] = b;
     const float v = bf16_to_f32(b);
     sq[i][e % 32] = v * v;
   }
@@ -319,7 +363,24 @@ __global__ __launch_bounds__(256) void dec_merge_kernel(DecArgs g) {
   }
 }
 
+// Feature scores of one new token per (sequence, head) row: the column norm
+// over a single row is |q_f| (sqrt of an exact square).
+__global__ __launch_bounds__(128) void dec_qabs_kernel(const uint16_t *__restrict__ Q, int64_t q_ss, int64_t q_hs,
+                                                       int64_t hq, float *__restrict__ sc) {
+  const int64_t r = blockIdx.x, b = r / hq, h = r - b * hq;
+  const float q = bf16_to_f32(Q[b * q_ss + h * q_hs + threadIdx.x]);
+  sc[r * 128 + threadIdx.x] = __builtin_sqrtf(q * q);
+}
+
 }  // namespace
+
+hipError_t launch_dec_qabs(const void *Q, int64_t q_ss, int64_t q_hs, int64_t nseq, int64_t hq, float *scores,
+                           hipStream_t st) {
+  KernelTimer timer("colnorm", st);
+  hipLaunchKernelGGL(dec_qabs_kernel, dim3((unsigned)(nseq * hq)), dim3(128), 0, st,
+                     static_cast<const uint16_t *>(Q), q_ss, q_hs, hq, scores);
+  return hipGetLastError();
+}
 
 bool attn_decode_ok(int64_t Lq, int64_t dh) { return Lq >= 1 && Lq <= 16 && dh == 128; }
 
@@ -377,23 +438,32 @@ hipError_t launch_attn_decode(int pass, const AttnDecodeDesc &d, hipStream_t st)
   g.kt_pad = d.kt_pad;
   g.off = d.Lk - d.Lq;
   g.causal = d.causal ? 1 : 0;
-  const AttnDecodeSizes z = attn_decode_sizes(d.Lq, d.Lk, d.hq, d.kt);
+  const int64_t nseq = d.nseq < 1 ? 1 : d.nseq;
+  g.q_ss = d.q_ss;
+  g.kt_ss = d.kt_ss;
+  g.v_ss = d.v_ss;
+  g.o_ss = d.o_ss;
+  g.lens = d.lens;
+  g.kts = d.kts;
+  g.nrows = nseq * d.hq;
+  if (g.nrows > 65535) return hipErrorInvalidValue;
+  const AttnDecodeSizes z = attn_decode_sizes(d.Lq, d.Lk, g.nrows, d.kt);
   g.nblk = z.nblk;
   g.nsplit = z.nsplit;
   g.c2 = (float)(1.4426950408889634 / __builtin_sqrt(128.0));
   const int lq = d.Lq <= 1 ? 1 : d.Lq <= 2 ? 2 : d.Lq <= 4 ? 4 : d.Lq <= 8 ? 8 : 16;
   if (pass == 0) {
     KernelTimer timer("dec_scores", st);
-    RMM_DEC_LAUNCH(dec_scores_kernel, lq, dim3((unsigned)z.nblk, (unsigned)d.hq), g, st);
+    RMM_DEC_LAUNCH(dec_scores_kernel, lq, dim3((unsigned)z.nblk, (unsigned)g.nrows), g, st);
   } else if (pass == 1) {
     KernelTimer timer("dec_tok", st);
-    RMM_DEC_LAUNCH(dec_tok_kernel, lq, dim3((unsigned)z.nblk, (unsigned)d.hq), g, st);
+    RMM_DEC_LAUNCH(dec_tok_kernel, lq, dim3((unsigned)z.nblk, (unsigned)g.nrows), g, st);
   } else if (pass == 2) {
     KernelTimer timer("dec_out", st);
-    RMM_DEC_LAUNCH(dec_out_kernel, lq, dim3((unsigned)z.nsplit, (unsigned)d.hq), g, st);
+    RMM_DEC_LAUNCH(dec_out_kernel, lq, dim3((unsigned)z.nsplit, (unsigned)g.nrows), g, st);
   } else {
     KernelTimer timer("dec_merge", st);
-    hipLaunchKernelGGL(dec_merge_kernel, dim3((unsigned)d.hq, 4), dim3(256), 0, st, g);
+    hipLaunchKernelGGL(dec_merge_kernel, dim3((unsigned)g.nrows, 4), dim3(256), 0, st, g);
   }
   return hipGetLastError();
 }

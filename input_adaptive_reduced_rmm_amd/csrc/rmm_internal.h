@@ -66,7 +66,7 @@ hipError_t launch_rmsnorm_scored(const void *X, int64_t ldx, const void *w, floa
 
 // ------------------------------------------------------------------ top-k
 hipError_t launch_topk(const float *scores, int64_t batch, int64_t d, int64_t k, int64_t k_pad,
-                       int32_t *idx, hipStream_t stream);
+                       int32_t *idx, hipStream_t stream, const int32_t *k_rows = nullptr, int k_div = 1);
 
 // ------------------------------------------------------------------ pack
 // out[b][i][t] = A[b][i][idx[b][t]] for t < k (0 when idx is out of [0,d)), 0 for k <= t < k_pad.
@@ -167,6 +167,12 @@ struct AttnDecodeDesc {
   float *o_scores;                        // [hq][128] or null
   int64_t hq, hkv, Lq, Lk, kf, kf_pad, kt, kt_pad;
   bool causal;
+  // batch of sequences (rows of I, J and the workspace arrays: nseq * hq);
+  // Lk and kt are then the largest context and kept-token count
+  int64_t nseq = 1;
+  int64_t q_ss = 0, kt_ss = 0, v_ss = 0, o_ss = 0;   // sequence strides (elements)
+  const int32_t *lens = nullptr;                     // [nseq] context lengths
+  const int32_t *kts = nullptr;                      // [nseq] kept tokens
 };
 struct AttnDecodeSizes {
   int nblk, nsplit;
@@ -175,5 +181,8 @@ struct AttnDecodeSizes {
 bool attn_decode_ok(int64_t Lq, int64_t dh);
 AttnDecodeSizes attn_decode_sizes(int64_t Lq, int64_t Lk, int64_t Hq, int64_t kt);
 hipError_t launch_attn_decode(int pass, const AttnDecodeDesc &d, hipStream_t stream);
+// scores[r][f] = |Q[b][h][f]| for row r = b * hq + h (one new token per sequence; dh == 128)
+hipError_t launch_dec_qabs(const void *Q, int64_t q_ss, int64_t q_hs, int64_t nseq, int64_t hq, float *scores,
+                           hipStream_t stream);
 
 }  // namespace rmm

@@ -32,10 +32,14 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 
 // NT threads per workgroup: 1024 for long rows, 256 for short ones (fewer
 // waves meet at each of the select's barriers).
+// k_rows (optional): row b keeps k_rows[b / k_div] indices instead of k,
+// clamped to [1, min(k, d)] (ragged batches: one count per sequence, shared
+// by its heads; k is then the largest count, which sizes the output rows).
 template <bool IN_LDS, int NT>
 __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scores, int64_t d,
                                                         int64_t k, int64_t k_pad,
-                                                        int32_t *__restrict__ idx) {
+                                                        int32_t *__restrict__ idx,
+                                                        const int32_t *__restrict__ k_rows, int k_div) {
   __shared__ uint32_t keys[IN_LDS ? (NT == 256 ? 4096 : kLdsKeys) : 1];
   __shared__ uint32_t hist[256];
   constexpr int kThreads = NT, kWaves = NT / 64;
@@ -43,6 +47,10 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
   __shared__ uint32_t sel_digit, sel_above;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (k_rows) {
+    const int64_t kr = k_rows[blockIdx.x / k_div], kmax = k < d ? k : d;
+    k = kr < 1 ? 1 : (kr > kmax ? kmax : kr);
+  }
   const float *s = scores + (int64_t)blockIdx.x * d;
   int32_t *out = idx + (int64_t)blockIdx.x * k_pad;
   auto key_at = [&](int64_t j) -> uint32_t {
@@ -234,22 +242,24 @@ __global__ __launch_bounds__(256) void iota_kernel(int64_t d, int64_t k_pad, int
 }  // namespace
 
 hipError_t launch_topk(const float *scores, int64_t batch, int64_t d, int64_t k, int64_t k_pad,
-                       int32_t *idx, hipStream_t st) {
+                       int32_t *idx, hipStream_t st, const int32_t *k_rows, int k_div) {
   KernelTimer timer("topk", st);
-  if (k == d) {
+  if (k == d && !k_rows) {
     unsigned gx = (unsigned)ceil_div(k_pad, 256);
     if (gx > 1024) gx = 1024;
     hipLaunchKernelGGL(iota_kernel, dim3(gx, (unsigned)batch), dim3(256), 0, st, d, k_pad, idx);
     return hipGetLastError();
   }
+  if (k_div < 1) k_div = 1;
   if (d <= 4096)
-    hipLaunchKernelGGL((topk_kernel<true, 256>), dim3((unsigned)batch), dim3(256), 0, st, scores, d, k, k_pad, idx);
+    hipLaunchKernelGGL((topk_kernel<true, 256>), dim3((unsigned)batch), dim3(256), 0, st, scores, d, k, k_pad, idx,
+                       k_rows, k_div);
   else if (d <= kLdsKeys)
     hipLaunchKernelGGL((topk_kernel<true, kMaxThreads>), dim3((unsigned)batch), dim3(kMaxThreads), 0, st, scores,
-                       d, k, k_pad, idx);
+                       d, k, k_pad, idx, k_rows, k_div);
   else
     hipLaunchKernelGGL((topk_kernel<false, kMaxThreads>), dim3((unsigned)batch), dim3(kMaxThreads), 0, st, scores,
-                       d, k, k_pad, idx);
+                       d, k, k_pad, idx, k_rows, k_div);
   return hipGetLastError();
 }
 

@@ -203,6 +203,28 @@ def test_rmsnorm_scored_rejects(lib):
     assert lib.rmm_rmsnorm_scored_workspace_bytes(0, 4096) == 0
 
 
+def test_attention_decode_batch_rejects(lib):
+    f = lib.rmm_attention_decode_batch
+    def call(Q=FAKE, Kt=FAKE, V=FAKE, lens=FAKE, ktok=FAKE, nseq=4, Hq=8, Hkv=2, dh=128, Lmax=1000, kf=64,
+             ktm=500, vts=256, ws=FAKE, wsb=1 << 30, O=FAKE):
+        return f(Q, 8 * 128, 128, Kt, 2 * 128 * 1000, 128 * 1000, 1000, V, 1000 * 256, vts, 128,
+                 lens, ktok, nseq, Hq, Hkv, dh, Lmax, kf, ktm, O, 8 * 128, 128, FAKE, FAKE, None, ws, wsb, None)
+    assert call(lens=None) == 1
+    assert call(O=None) == 1
+    assert call(nseq=0) == 1
+    assert call(Hkv=3) == 1                   # Hq % Hkv != 0
+    assert call(nseq=9000) == 1               # nseq * Hq > 65535
+    assert call(kf=0) == 1
+    assert call(ktm=1001) == 1                # kt_max > Lmax
+    assert call(dh=64) == 2
+    assert call(vts=252) == 2                 # value rows not 16-byte aligned
+    assert call(V=ctypes.c_void_p(0x10008)) == 2
+    need = lib.rmm_attention_decode_batch_workspace_bytes(4, 8, 128, 1000, 500)
+    assert need > 0
+    assert call(wsb=need - 1) == 3
+    assert lib.rmm_attention_decode_batch_workspace_bytes(4, 8, 64, 1000, 500) == 0
+
+
 def test_attention_rejects(lib):
     f = lib.rmm_attention
     def call(Lq=64, Hq=4, dh=128, qts=512, qhs=128, Lk=64, Hkv=2, kths=8192, ldkt=64, vts=256, vhs=128,
