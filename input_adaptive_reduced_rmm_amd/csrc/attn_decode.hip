@@ -66,6 +66,8 @@ struct DecArgs {
   const int32_t *lens;    // [nseq] context lengths (null: Lk for all)
   const int32_t *kts;     // [nseq] kept tokens (null: kt for all)
   int64_t nrows;          // nseq * hq: rows of I, J, S, pstat, nml, tok and opart
+  int sblk_keys;          // keys per score block (one pstat entry)
+  int kvec;               // K rows 16-byte aligned (pointer and strides multiples of 8 elements)
 };
 
 // The sequence of row r, its context length, its causal offset and its
@@ -191,23 +193,107 @@ __global__ __launch_bounds__(kDB) void dec_scores_kernel(DecArgs g) {
   }
 }
 
+// One query row (a single new token): each thread takes 8 consecutive keys,
+// so a kept feature row of K is read as one 16-byte load per thread (a block
+// covers 2048 keys).  Blocks wholly past a sequence's context exit at once;
+// the statistics merge reads only the blocks a row has.
+constexpr int kKPT = 8, kSB1 = kDB * kKPT;
+__global__ __launch_bounds__(kDB) void dec_scores1_kernel(DecArgs g) {
+  __shared__ int32_t sI[128];
+  __shared__ float sq[128];
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x;
+  const int64_t h = blockIdx.y;   // row: sequence * hq + head
+  const SeqRow sr = seq_row(g, h);
+  const int64_t jb = (int64_t)blk * kSB1;
+  if (jb >= sr.Lk) return;
+  const int64_t grp = sr.h * g.hkv / g.hq;
+  const int kf = (int)g.kf;
+  if (tid < 128) {
+    const int f = tid < kf ? g.I[h * g.kf_pad + tid] : 0;
+    sI[tid] = f;
+    sq[tid] = tid < kf ? bf16_to_f32(g.Q[sr.b * g.q_ss + sr.h * g.q_hs + f]) : 0.f;
+  }
+  __syncthreads();
+  const int64_t j0 = jb + (int64_t)tid * kKPT;
+  float s[kKPT];
+#pragma unroll
+  for (int e = 0; e < kKPT; ++e) s[e] = 0.f;
+  const uint16_t *kb = g.Kt + sr.b * g.kt_ss + grp * g.kt_hs + j0;
+  if (g.kvec && j0 + kKPT <= sr.Lk) {
+    int f = 0;
+    for (; f + 4 <= kf; f += 4) {
+      uint4 kv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kv[u] = *reinterpret_cast<const uint4 *>(kb + (int64_t)sI[f + u] * g.ldkt);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float q = sq[f + u];
+        const float kx[8] = {bf16_lo(kv[u].x), bf16_hi(kv[u].x), bf16_lo(kv[u].y), bf16_hi(kv[u].y),
+                             bf16_lo(kv[u].z), bf16_hi(kv[u].z), bf16_lo(kv[u].w), bf16_hi(kv[u].w)};
+#pragma unroll
+        for (int e = 0; e < kKPT; ++e) s[e] = fmaf(q, kx[e], s[e]);
+      }
+    }
+    for (; f < kf; ++f) {
+      const uint4 kv = *reinterpret_cast<const uint4 *>(kb + (int64_t)sI[f] * g.ldkt);
+      const float q = sq[f];
+      const float kx[8] = {bf16_lo(kv.x), bf16_hi(kv.x), bf16_lo(kv.y), bf16_hi(kv.y),
+                           bf16_lo(kv.z), bf16_hi(kv.z), bf16_lo(kv.w), bf16_hi(kv.w)};
+#pragma unroll
+      for (int e = 0; e < kKPT; ++e) s[e] = fmaf(q, kx[e], s[e]);
+    }
+  } else if (j0 < sr.Lk) {
+    for (int f = 0; f < kf; ++f) {
+      const float q = sq[f];
+      const uint16_t *kr = kb + (int64_t)sI[f] * g.ldkt;
+#pragma unroll
+      for (int e = 0; e < kKPT; ++e)
+        if (j0 + e < sr.Lk) s[e] = fmaf(q, bf16_to_f32(kr[e]), s[e]);
+    }
+  }
+  // masked scores are -inf: they add nothing to any later sum
+  float m = kNegInfD;
+#pragma unroll
+  for (int e = 0; e < kKPT; ++e) {
+    const int64_t j = j0 + e;
+    const bool vis = j < sr.Lk && (!g.causal || j <= sr.off);
+    s[e] = vis ? s[e] : kNegInfD;
+    m = fmaxf(m, s[e]);
+    if (j < g.Lk) g.S[h * g.Lk + j] = s[e];
+  }
+  float mv[1] = {m};
+  block_reduce<1, true>(mv, red);
+  float l = 0.f;
+  if (mv[0] != kNegInfD) {
+#pragma unroll
+    for (int e = 0; e < kKPT; ++e) l += dexp2((s[e] - mv[0]) * g.c2);
+  }
+  float lv[1] = {l};
+  block_reduce<1, false>(lv, red);
+  if (tid == 0) g.pstat[h * g.nblk + blk] = make_float2(mv[0], lv[0]);
+}
+
 // Merge the key blocks' statistics of head h: every thread takes the blocks
 // b = tid, tid + 256, ... (loads independent of each other), then block-wide
 // max and sum in a fixed order.  Returns nml_i = -c max_i - log2(sum_i).
 template <int LQ>
 __device__ __forceinline__ void merge_stats(const DecArgs &g, int64_t h, float (&nml)[LQ], float *red) {
   const int tid = threadIdx.x, Lq = (int)g.Lq;
+  // blocks this row has (a shorter sequence has fewer)
+  const int nb = g.lens ? (int)((seq_row(g, h).Lk + g.sblk_keys - 1) / g.sblk_keys) : g.nblk;
   float M[LQ], L[LQ];
 #pragma unroll
   for (int i = 0; i < LQ; ++i) M[i] = kNegInfD;
-  for (int b = tid; b < g.nblk; b += kDB)
+  for (int b = tid; b < nb; b += kDB)
 #pragma unroll
     for (int i = 0; i < LQ; ++i)
       if (i < Lq) M[i] = fmaxf(M[i], g.pstat[(h * g.nblk + b) * g.Lq + i].x);
   block_reduce<LQ, true>(M, red);
 #pragma unroll
   for (int i = 0; i < LQ; ++i) L[i] = 0.f;
-  for (int b = tid; b < g.nblk; b += kDB)
+  for (int b = tid; b < nb; b += kDB)
 #pragma unroll
     for (int i = 0; i < LQ; ++i)
       if (i < Lq) {
@@ -226,6 +312,11 @@ __global__ __launch_bounds__(kDB) void dec_tok_kernel(DecArgs g) {
   const int blk = blockIdx.x;
   const int64_t h = blockIdx.y;
   const int Lq = (int)g.Lq;
+  if (g.lens && (int64_t)blk * kDB >= seq_row(g, h).Lk) {   // wholly past this sequence's context
+    const int64_t j = (int64_t)blk * kDB + tid;
+    if (j < g.Lk) g.tok[h * g.Lk + j] = kNegInfD;
+    return;
+  }
   float snml[LQ];
   merge_stats<LQ>(g, h, snml, red);
   if (blk == 0 && tid < Lq) {
@@ -386,7 +477,8 @@ bool attn_decode_ok(int64_t Lq, int64_t dh) { return Lq >= 1 && Lq <= 16 && dh =
 
 AttnDecodeSizes attn_decode_sizes(int64_t Lq, int64_t Lk, int64_t Hq, int64_t kt) {
   AttnDecodeSizes z;
-  z.nblk = (int)ceil_div(Lk, kDB);
+  z.nblk = (int)ceil_div(Lk, Lq == 1 ? kSB1 : kDB);   // score blocks (one statistics entry each)
+  z.ntokblk = (int)ceil_div(Lk, kDB);
   z.nsplit = (int)ceil_div(kt, kDB * kTokSub);
   z.s_bytes = (size_t)Hq * Lq * Lk * 4;
   z.pstat_bytes = (size_t)Hq * z.nblk * Lq * 8;
@@ -450,14 +542,19 @@ hipError_t launch_attn_decode(int pass, const AttnDecodeDesc &d, hipStream_t st)
   const AttnDecodeSizes z = attn_decode_sizes(d.Lq, d.Lk, g.nrows, d.kt);
   g.nblk = z.nblk;
   g.nsplit = z.nsplit;
+  g.sblk_keys = d.Lq == 1 ? kSB1 : kDB;
+  g.kvec = reinterpret_cast<uintptr_t>(d.Kt) % 16 == 0 && d.ldkt % 8 == 0 && d.kt_hs % 8 == 0 && d.kt_ss % 8 == 0;
   g.c2 = (float)(1.4426950408889634 / __builtin_sqrt(128.0));
   const int lq = d.Lq <= 1 ? 1 : d.Lq <= 2 ? 2 : d.Lq <= 4 ? 4 : d.Lq <= 8 ? 8 : 16;
   if (pass == 0) {
     KernelTimer timer("dec_scores", st);
-    RMM_DEC_LAUNCH(dec_scores_kernel, lq, dim3((unsigned)z.nblk, (unsigned)g.nrows), g, st);
+    if (d.Lq == 1)
+      hipLaunchKernelGGL(dec_scores1_kernel, dim3((unsigned)z.nblk, (unsigned)g.nrows), dim3(kDB), 0, st, g);
+    else
+      RMM_DEC_LAUNCH(dec_scores_kernel, lq, dim3((unsigned)z.nblk, (unsigned)g.nrows), g, st);
   } else if (pass == 1) {
     KernelTimer timer("dec_tok", st);
-    RMM_DEC_LAUNCH(dec_tok_kernel, lq, dim3((unsigned)z.nblk, (unsigned)g.nrows), g, st);
+    RMM_DEC_LAUNCH(dec_tok_kernel, lq, dim3((unsigned)z.ntokblk, (unsigned)g.nrows), g, st);
   } else if (pass == 2) {
     KernelTimer timer("dec_out", st);
     RMM_DEC_LAUNCH(dec_out_kernel, lq, dim3((unsigned)z.nsplit, (unsigned)g.nrows), g, st);

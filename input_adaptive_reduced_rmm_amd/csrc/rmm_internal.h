@@ -175,7 +175,7 @@ struct AttnDecodeDesc {
   const int32_t *kts = nullptr;                      // [nseq] kept tokens
 };
 struct AttnDecodeSizes {
-  int nblk, nsplit;
+  int nblk, ntokblk, nsplit;   // score blocks, token-score blocks, output splits
   size_t s_bytes, pstat_bytes, nml_bytes, opart_bytes;
 };
 bool attn_decode_ok(int64_t Lq, int64_t dh);
