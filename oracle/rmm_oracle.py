@@ -22,7 +22,7 @@ What it is
     written out, with library primitives (an elementwise square, a sum, a
     sort, a matmul) as steps and no blocking, fusion or reordering.
 
-Readings where the pages are silent (each one is also listed in the design notes)
+Readings where the pages are silent
     R1  k = ceil(rho*d) with rho taken as the decimal number the caller wrote
         (the shortest decimal string that round-trips the float), computed in
         exact rational arithmetic; rho must lie in (0, 1].
