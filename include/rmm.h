@@ -56,7 +56,7 @@ extern "C" {
 typedef enum {
   RMM_OK = 0,
   RMM_ERR_INVALID_ARG = 1, /* bad size, stride, pointer or ratio            */
-  RMM_ERR_UNSUPPORTED = 2, /* valid request this build does not serve       */
+  RMM_ERR_UNSUPPORTED = 2, /* valid request the library does not serve     */
   RMM_ERR_WORKSPACE = 3,   /* ws_bytes below the size the query returns     */
   RMM_ERR_HIP = 4          /* the HIP runtime rejected a launch             */
 } rmm_status_t;
