@@ -47,18 +47,29 @@ KernelTimer::KernelTimer(const char *kernel, hipStream_t s) : stream_(s) {
   std::lock_guard<std::mutex> lk(g_mu);
   a_ = take_event();
   b_ = take_event();
-  if (!a_ || !b_) {
+  if (!a_ || !b_) {   // out of events: give back the one that was taken, time nothing
+    if (a_) g_pool.push_back(static_cast<hipEvent_t>(a_));
+    if (b_) g_pool.push_back(static_cast<hipEvent_t>(b_));
     a_ = b_ = nullptr;
     return;
   }
   key_ = g_tag.empty() ? std::string(kernel) : g_tag + "/" + kernel;
-  hipEventRecord(static_cast<hipEvent_t>(a_), s);
+  if (hipEventRecord(static_cast<hipEvent_t>(a_), s) != hipSuccess) {   // e.g. a stream under capture
+    g_pool.push_back(static_cast<hipEvent_t>(a_));
+    g_pool.push_back(static_cast<hipEvent_t>(b_));
+    a_ = b_ = nullptr;
+  }
 }
 
 KernelTimer::~KernelTimer() {
   if (!a_) return;
-  hipEventRecord(static_cast<hipEvent_t>(b_), stream_);
+  const bool ok = hipEventRecord(static_cast<hipEvent_t>(b_), stream_) == hipSuccess;
   std::lock_guard<std::mutex> lk(g_mu);
+  if (!ok) {   // this launch goes untimed; the events return to the pool
+    g_pool.push_back(static_cast<hipEvent_t>(a_));
+    g_pool.push_back(static_cast<hipEvent_t>(b_));
+    return;
+  }
   g_pending.push_back({key_, static_cast<hipEvent_t>(a_), static_cast<hipEvent_t>(b_)});
 }
 
