@@ -539,6 +539,97 @@ def producer_fused(R, wl, args, steps, warmup, dev):
     return res
 
 
+def fused_layer(R, layer, steps, warmup, dense=True):
+    """A LLaMA-style layer built from the fused entry points: RMS norm with its
+    column scores -> top-k -> q|k|v reduced GEMM -> fused reduced attention
+    (with the column scores of O) -> top-k -> o reduced GEMM -> residual ->
+    RMS norm with scores -> top-k -> up|gate reduced GEMM -> SiLU gate with
+    scores -> top-k -> down reduced GEMM -> residual.  No separate column-norm
+    pass and no S or P in memory.  Glue that a model would fuse elsewhere
+    runs in torch inside the timed step: the transposed copy of K that the
+    attention reads (feature-major) and the two residual adds.  RoPE is left
+    out.  Timed at the layer's ratios and with every index kept (k = d)."""
+    import torch
+
+    at = layer["attention"]
+    lin = {l["name"].split("@")[0]: l for l in layer["linears"]}
+    need = ("q+k+v", "o", "up+gate", "down")
+    if at is None or any(n not in lin for n in need):
+        return None
+    m, hid = lin["q+k+v"]["m"], lin["q+k+v"]["d"]
+    mlp = lin["down"]["d"]
+    Hq, Hkv, dh, L = at["Hq"], at["Hkv"], at["dh"], at["L"]
+    if m != L or lin["q+k+v"]["n"] != (Hq + 2 * Hkv) * dh:
+        return None
+    dev = lin["o"]["A"].device
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    X = torch.randn((m, hid), generator=g, device=dev).to(bf)
+    w1 = (torch.rand(hid, generator=g, device=dev) * 1.3 + 0.2).to(bf)
+    w2 = (torch.rand(hid, generator=g, device=dev) * 1.3 + 0.2).to(bf)
+    Wqkv, Wo, Wug, Wd = lin["q+k+v"]["B"], lin["o"]["B"], lin["up+gate"]["B"], lin["down"]["B"]
+    nq, nkv = Hq * dh, Hkv * dh
+    buf = {
+        "Xn": torch.empty((m, hid), dtype=bf, device=dev), "s": torch.empty(mlp, dtype=torch.float32, device=dev),
+        "QKV": torch.empty((m, nq + 2 * nkv), dtype=bf, device=dev), "Kt": torch.empty((Hkv, dh, m), dtype=bf, device=dev),
+        "O": torch.empty((m, Hq, dh), dtype=bf, device=dev), "os": torch.empty(nq, dtype=torch.float32, device=dev),
+        "Yo": torch.empty((m, hid), dtype=bf, device=dev), "X2": torch.empty((m, hid), dtype=bf, device=dev),
+        "UG": torch.empty((m, Wug.shape[1]), dtype=bf, device=dev), "H": torch.empty((m, mlp), dtype=bf, device=dev),
+        "Yd": torch.empty((m, hid), dtype=bf, device=dev), "X3": torch.empty((m, hid), dtype=bf, device=dev),
+    }
+    ws_n = torch.empty(max(R.rmm_rmsnorm_scored_workspace_bytes(m, hid), 256), dtype=torch.uint8, device=dev)
+    ws_h = torch.empty(max(R.rmm_swiglu_scored_workspace_bytes(m, mlp), 256), dtype=torch.uint8, device=dev)
+    out = {"model": "llama3.1-8b layer", "tokens": m,
+           "glue": "torch: K transposed for the attention, residual adds; RoPE left out"}
+    for name, scale_one in [("rho", False)] + ([("rho1", True)] if dense else []):
+        def kk(l, d):
+            return d if scale_one else R.rmm_k_from_rho(l["rho"], d)
+        k1, ko, k2, kd = kk(lin["q+k+v"], hid), kk(lin["o"], nq), kk(lin["up+gate"], hid), kk(lin["down"], mlp)
+        kf = dh if scale_one else R.rmm_k_from_rho(at["rho"], dh)
+        kt = L if scale_one else R.rmm_k_from_rho(at["rho"], L)
+        ix = {n: torch.empty(R.rmm_k_pad(k), dtype=torch.int32, device=dev)
+              for n, k in (("qkv", k1), ("o", ko), ("ug", k2), ("d", kd))}
+        If = torch.empty((Hq, R.rmm_k_pad(kf)), dtype=torch.int32, device=dev)
+        It = torch.empty((Hq, R.rmm_k_pad(kt)), dtype=torch.int32, device=dev)
+        wsg = torch.empty(max(R.rmm_gemm_workspace_bytes(bf, m, n, k) for n, k in
+                              ((nq + 2 * nkv, k1), (hid, ko), (Wug.shape[1], k2), (hid, kd))), dtype=torch.uint8,
+                          device=dev)
+        wsa = torch.empty(R.rmm_attention_workspace_bytes(m, m, Hq, dh, kf, kt), dtype=torch.uint8, device=dev)
+        b = buf
+        half = Wug.shape[1] // 2
+
+        class _Layer:
+            def step(self, tagged=False):
+                s1 = b["s"][:hid]
+                R.rmm_rmsnorm_scored(X, w1, 1e-5, Y=b["Xn"], scores=s1, ws=ws_n)
+                R.rmm_topk(s1, k1, out=ix["qkv"])
+                R.rmm_gemm(b["Xn"], Wqkv, ix["qkv"], k1, out=b["QKV"], ws=wsg)
+                Q = b["QKV"][:, :nq].view(m, Hq, dh)
+                b["Kt"].copy_(b["QKV"][:, nq:nq + nkv].view(m, Hkv, dh).permute(1, 2, 0))
+                V = b["QKV"][:, nq + nkv:].view(m, Hkv, dh)
+                R.rmm_attention(Q, b["Kt"], V, kf, kt, O=b["O"], idx_feat=If, idx_tok=It, ws=wsa, causal=True,
+                                o_scores=b["os"])
+                R.rmm_topk(b["os"], ko, out=ix["o"])
+                R.rmm_gemm(b["O"].view(m, nq), Wo, ix["o"], ko, out=b["Yo"], ws=wsg)
+                torch.add(X, b["Yo"], out=b["X2"])
+                R.rmm_rmsnorm_scored(b["X2"], w2, 1e-5, Y=b["Xn"], scores=s1, ws=ws_n)
+                R.rmm_topk(s1, k2, out=ix["ug"])
+                R.rmm_gemm(b["Xn"], Wug, ix["ug"], k2, out=b["UG"], ws=wsg)
+                R.rmm_swiglu_scored(b["UG"][:, half:], b["UG"][:, :half], H=b["H"], scores=b["s"], ws=ws_h)
+                R.rmm_topk(b["s"], kd, out=ix["d"])
+                R.rmm_gemm(b["H"], Wd, ix["d"], kd, out=b["Yd"], ws=wsg)
+                torch.add(b["X2"], b["Yd"], out=b["X3"])
+
+        ms, _ = time_steps(_Layer(), steps, warmup)
+        out[name + "_ms"] = round(ms, 4)
+        del ix, If, It, wsg, wsa
+        torch.cuda.empty_cache()
+    if "rho1_ms" in out:
+        out["speedup_vs_rho1"] = round(out["rho1_ms"] / out["rho_ms"], 3)
+    return out
+
+
 def csrc_sha256():
     import glob
     import hashlib
@@ -704,6 +795,11 @@ def main():
     producers = None
     if not args.no_producers:
         producers = producer_fused(R, wl, args, args.steps, args.warmup, dev)
+    layer_fused = None
+    if not args.no_fused_attention and not args.no_producers:
+        layer_fused = fused_layer(R, layer, args.steps, args.warmup, dense=not args.no_dense)
+        if layer_fused:
+            print(f"[bench] fused layer {layer_fused['rho_ms']:.3f} ms", file=sys.stderr, flush=True)
 
     speedup = dense_ms = None
     if not args.no_dense:
@@ -735,7 +831,7 @@ def main():
         "rho1_ms_per_step": round(dense_ms, 4) if dense_ms else None,
         "gemm_kept_mfma_frac": round(mfma_frac, 4) if mfma_frac is not None else None,
         "roofline": roof, "cpu_baseline": cpu, "kernels": detail, "fused_attention": fused,
-        "producer_fused": producers,
+        "producer_fused": producers, "fused_layer": layer_fused,
         "step_times": {"hot": hot, "cold_cache": cold},
         "context": {"rmm_projections_ms": round(proj_ms, 4), "torch_matmul_projections_ms": torch_proj_ms},
     }
