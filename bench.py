@@ -630,6 +630,16 @@ def fused_layer(R, layer, steps, warmup, dense=True):
     return out
 
 
+def system_info(dev):
+    """The device the line was measured on (name, compute units, HIP runtime) and the host's cores."""
+    import torch
+
+    p = torch.cuda.get_device_properties(dev)
+    return {"gpu": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2 ** 30, 1), "hip": torch.version.hip,
+            "host_cores": os.cpu_count()}
+
+
 def csrc_sha256():
     import glob
     import hashlib
@@ -833,6 +843,7 @@ def main():
         "roofline": roof, "cpu_baseline": cpu, "kernels": detail, "fused_attention": fused,
         "producer_fused": producers, "fused_layer": layer_fused,
         "step_times": {"hot": hot, "cold_cache": cold},
+        "system": system_info(dev),
         "context": {"rmm_projections_ms": round(proj_ms, 4), "torch_matmul_projections_ms": torch_proj_ms},
     }
     print(json.dumps(out), flush=True)
