@@ -167,3 +167,38 @@ def test_decode_batch_in_a_graph():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(O, ref[0]) and torch.equal(I, ref[1]) and torch.equal(J, ref[2]), f"replay {rep}"
+
+
+def test_decode_batch_bench_shape_sampled():
+    """The bench's batched step: 16 sequences with contexts drawn uniformly from
+    [4096, 16384] in a 16384-token cache, 32 query / 8 kv heads, rho = 0.5;
+    every sequence checked on a sample of its heads."""
+    rng = np.random.default_rng([0, 91, 16])
+    lens = [int(x) for x in np.sort(rng.integers(4096, 16384 + 1, size=16))]
+    Hq, Hkv, kf = 32, 8, 64
+    kts = [oracle.retained_count(0.5, L) for L in lens]
+    B, Lmax, dh = len(lens), 16384, 128
+    Qb = np.zeros((B, Hq, dh), np.float32)
+    Ktb = np.zeros((B, Hkv, dh, Lmax), np.float32)
+    Vb = np.zeros((B, Lmax, Hkv, dh), np.float32)
+    per = []
+    for b, L in enumerate(lens):
+        Q, Kt, V = synth.attention_operands(W, seed=100 + b, L=L, Hq=Hq, Hkv=Hkv)
+        Qb[b] = Q[L - 1]
+        Ktb[b, :, :, :L] = Kt
+        Vb[b, :L] = V
+        per.append((Q[L - 1:], Kt, V))
+    O, I, J, ts = _run(Qb, Ktb, Vb, lens, kts, kf, max(kts))
+    pick = np.random.default_rng(7)
+    for b, (L, kt) in enumerate(zip(lens, kts)):
+        Q, Kt, V = per[b]
+        for h in pick.choice(Hq, size=3, replace=False):
+            r = b * Hq + h
+            check_selection(I[r], np.abs(Qb[b, h].astype(np.float64)), oracle.column_scores(Q[:, h, :]), kf)
+            S = oracle.reduced_product(Q[:, h, :], Kt[oracle.kv_head(h, Hq, Hkv)], I[r][:kf])[None]
+            P = oracle.causal_softmax(S, 128 ** -0.5)[0]
+            tok = oracle.column_scores(P)
+            np.testing.assert_allclose(ts[r, :L], tok, rtol=2e-5, atol=1e-6 * tok.max())
+            check_selection(J[r], ts[r, :L], tok, kt)
+            want = oracle.reduced_product(P, V[:, oracle.kv_head(h, Hq, Hkv), :], J[r][:kt])
+            assert rel_fro(O[b, h][None], want) < TOL_BF16, f"sequence {b} head {h}"
