@@ -41,7 +41,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
                                                         int32_t *__restrict__ idx,
                                                         const int32_t *__restrict__ k_rows, int k_div) {
   __shared__ uint32_t keys[IN_LDS ? (NT == 256 ? 4096 : kLdsKeys) : 1];
-  __shared__ uint32_t hist[256];
+  // Long rows: kRep copies of the histogram, lane l adding to copy l % kRep
+  // (padded to 257 words so the copies' bins sit in different banks): scores
+  // that crowd into a few digits then collide kRep times less.
+  constexpr int kRep = NT == 1024 ? 4 : 1;
+  __shared__ uint32_t hist[kRep == 1 ? 256 : kRep * 257];
   constexpr int kThreads = NT, kWaves = NT / 64;
   __shared__ uint32_t red_or[kWaves], red_and[kWaves];
   __shared__ uint32_t sel_digit, sel_above;
@@ -108,7 +112,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
     const int shift = lo - width;
     const uint32_t hmask = lo >= 32 ? 0u : (0xFFFFFFFFu << lo);
     const uint32_t dmask = (1u << width) - 1u;
-    if (tid < 256) hist[tid] = 0u;
+    for (int i = tid; i < (kRep == 1 ? 256 : kRep * 257); i += kThreads) hist[i] = 0u;
     __syncthreads();
     for (int64_t j0 = tid; j0 < d; j0 += 8 * kThreads) {
       uint32_t kk[8];
@@ -120,14 +124,22 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int64_t j = j0 + (int64_t)u * kThreads;
-        if (j < d && (kk[u] & hmask) == prefix) atomicAdd(&hist[(kk[u] >> shift) & dmask], 1u);
+        if (j < d && (kk[u] & hmask) == prefix)
+          atomicAdd(&hist[(kRep == 1 ? 0 : (lane % kRep) * 257) + ((kk[u] >> shift) & dmask)], 1u);
       }
     }
     __syncthreads();
     if (wave == 0) {
       // lane l holds bins 4l..4l+3; count keys in strictly higher bins.
-      const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
-                     h3 = hist[4 * lane + 3];
+      uint32_t h0 = 0u, h1 = 0u, h2 = 0u, h3 = 0u;
+#pragma unroll
+      for (int c = 0; c < kRep; ++c) {
+        const uint32_t *hc = hist + (kRep == 1 ? 0 : c * 257);
+        h0 += hc[4 * lane];
+        h1 += hc[4 * lane + 1];
+        h2 += hc[4 * lane + 2];
+        h3 += hc[4 * lane + 3];
+      }
       const uint32_t mine = h0 + h1 + h2 + h3;
       uint32_t suf = mine;  // inclusive suffix sum over lanes >= lane
 #pragma unroll
