@@ -44,7 +44,7 @@ def _linear_case(i):
     return m, d, n, _rho(rng), int(rng.integers(0, 2)) * int(rng.integers(1, 9))
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(60))
 def test_sweep_linear_bf16(i):
     m, d, n, rho, pad = _linear_case(i)
     print(f"  m={m} d={d} n={n} rho={rho} lda=d+{pad}", flush=True)
@@ -64,7 +64,7 @@ def test_sweep_linear_bf16(i):
     assert rel_fro(Y.float().cpu().numpy()[rows], want) < TOL_BF16
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(16))
 def test_sweep_linear_f32(i):
     rng = _rng(4, i)
     m, d, n = int(rng.integers(1, 300)), int(rng.integers(1, 1100)), int(rng.integers(1, 700))
@@ -80,7 +80,7 @@ def test_sweep_linear_f32(i):
     assert rel_fro(Y.cpu().numpy(), want) < TOL_F32
 
 
-@pytest.mark.parametrize("i", range(10))
+@pytest.mark.parametrize("i", range(30))
 def test_sweep_topk_batched(i):
     rng = _rng(6, i)
     batch, d = int(rng.integers(1, 40)), int(rng.integers(1, 40000))
@@ -102,7 +102,7 @@ def test_sweep_topk_batched(i):
         assert np.array_equal(got[:k], oracle.select_top(s[b].astype(np.float64), k))
 
 
-@pytest.mark.parametrize("i", range(10))
+@pytest.mark.parametrize("i", range(30))
 def test_sweep_qk_pv(i):
     rng = _rng(7, i)
     Lq = int(rng.integers(1, 700))
@@ -142,7 +142,7 @@ def test_sweep_qk_pv(i):
         assert rel_fro(O[:, h, :], want) < TOL_BF16
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(24))
 def test_sweep_fused_attention(i):
     from test_gpu_attention import W4K, _operands, check_fused
 
@@ -160,7 +160,7 @@ def test_sweep_fused_attention(i):
     print(f"  near ties: {check_fused(Q, Kt, V, kf, kt, causal, rows=128, seed=i)}")
 
 
-@pytest.mark.parametrize("i", range(6))
+@pytest.mark.parametrize("i", range(16))
 def test_sweep_gemm_w8(i):
     rng = _rng(9, i)
     m = int([rng.integers(1, 33), rng.integers(33, 400)][i % 2])
@@ -179,7 +179,7 @@ def test_sweep_gemm_w8(i):
     assert rel_fro(Y.float().cpu().numpy(), want) < TOL_BF16
 
 
-@pytest.mark.parametrize("i", range(6))
+@pytest.mark.parametrize("i", range(16))
 def test_sweep_producers(i):
     rng = _rng(11, i)
     m = int(rng.integers(1, 3000))
