@@ -78,10 +78,11 @@ const char *rmm_last_error(void);
 /*
  * rmm_k_from_rho - number of kept indices, k = ceil(rho * d).
  * Source: "Estrategia de Selección" (k = ceil(rho d), rho the retention ratio).
- * rho is read as the decimal the caller wrote: the exact product rho*d is
- * formed, and when it lies within the representation error of rho (d * 2^-52)
- * of an integer, that integer is k; otherwise k is the ceiling.  So rho = 0.55,
- * d = 100 gives 55 (a naive binary product gives 56).
+ * rho is read as the decimal the caller wrote: the shortest decimal string
+ * that reads back as the same double (of equally short ones, the nearest),
+ * p * 10^-q, and k = ceil(p * d / 10^q) in exact integer arithmetic.  So
+ * rho = 0.55, d = 100 gives 55 (a naive binary product gives 56), and
+ * rho = 0.1 + 0.2 (shortest string 0.30000000000000004), d = 10 gives 4.
  *   rho  in (0, 1]; d >= 1; k (host) receives the result, 1 <= k <= d.
  * Returns RMM_ERR_INVALID_ARG for rho outside (0, 1] (or NaN), d < 1 or k NULL.
  */
@@ -228,13 +229,24 @@ rmm_status_t rmm_rmsnorm_scored(const void *X, int64_t ldx, const void *w, float
  *   Hq >= 1, 1 <= Hkv <= Hq, Hq % Hkv == 0; 1 <= k <= dh.
  *   S (device, float) element (h, t, u) at S + h*s_head_stride + t*lds + u.
  *   idx (device, int32) [Hq][rmm_k_pad(k)], written as by rmm_topk.
+ *   feat_scores (device, float, optional) [Hq][dh]: receives the column
+ *   scores the selection used; NULL keeps them in the workspace.
+ *   causal != 0: only the entries a causal softmax reads are promised, those
+ *   with u <= t + (Lk - Lq).  S is written in 128 x 128 tiles; tiles lying
+ *   wholly above that diagonal are not written at all (the memory keeps what
+ *   it held), and tiles that cross it are written whole, so entries above the
+ *   diagonal inside them hold the unmasked products.  causal == 0 writes all
+ *   of S.  Q and K are only read.
+ * Layouts the kernels cannot address (the feature rows of one key head
+ * spanning 4 GiB or more) are rejected with RMM_ERR_UNSUPPORTED before
+ * anything is enqueued, like every other rejection.
  */
 size_t rmm_qk_workspace_bytes(int64_t Lq, int64_t Hq, int64_t dh, int64_t k);
 rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, int64_t q_tok_stride,
                     int64_t q_head_stride, const void *Kt, int64_t Lk, int64_t Hkv,
                     int64_t kt_head_stride, int64_t ldkt, int64_t k, int causal, float *S,
-                    int64_t s_head_stride, int64_t lds, int32_t *idx, void *ws, size_t ws_bytes,
-                    rmm_stream_t stream);
+                    int64_t s_head_stride, int64_t lds, int32_t *idx, float *feat_scores, void *ws,
+                    size_t ws_bytes, rmm_stream_t stream);
 
 /*
  * rmm_pv - token-reduced attention output for every query head (bf16).
@@ -257,6 +269,9 @@ rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, int64_t q
  *   head must each span less than 4 GiB (RMM_ERR_UNSUPPORTED otherwise).
  *   O (device, bf16) element (t, h, j) at O + t*o_tok_stride + h*o_head_stride + j.
  *   idx (device, int32) [Hq][rmm_k_pad(k)], written as by rmm_topk.
+ *   tok_scores (device, float, optional) [Hq][Lk]: receives the token scores
+ *   the selection used (column norms of P over the Lq rows, causal zeros
+ *   included as zeros); NULL keeps them in the workspace.
  * The product reads P at 64-token tile granularity: tiles holding no kept
  * token are skipped, dropped tokens inside a kept tile are zeroed in both P
  * and V before the multiply, so the result equals the reduced product exactly
@@ -266,7 +281,7 @@ size_t rmm_pv_workspace_bytes(int64_t Hq, int64_t Lq, int64_t Lk, int64_t k);
 rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, int64_t p_head_stride,
                     int64_t ldp, const void *V, int64_t Hkv, int64_t dh, int64_t v_tok_stride,
                     int64_t v_head_stride, int64_t k, int causal, void *O, int64_t o_tok_stride,
-                    int64_t o_head_stride, int32_t *idx, void *ws, size_t ws_bytes,
+                    int64_t o_head_stride, int32_t *idx, float *tok_scores, void *ws, size_t ws_bytes,
                     rmm_stream_t stream);
 
 /*

@@ -17,7 +17,7 @@ HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",
     # Keep the compiler from emitting packed FP32 ALU ops.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function", "-Werror=return-type",
+    "-Wall", "-Wextra", "-Wno-unused-parameter", "-Wno-unused-function", "-Werror",
 ]
 
 

@@ -57,7 +57,7 @@ _PROTOS = {
                                 _i64, _vp, _sz, _vp]),
     "rmm_qk_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "rmm_qk": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
-                              ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
+                              ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
     "rmm_pv_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "rmm_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "rmm_timing_set_tag": (ctypes.c_int, [ctypes.c_char_p]),
@@ -67,7 +67,7 @@ _PROTOS = {
                                         ctypes.POINTER(_i64)]),
     "rmm_timing_reset": (ctypes.c_int, []),
     "rmm_pv": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
-                              ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
+                              ctypes.c_int, _vp, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
     "rmm_attention_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
     "rmm_gemm_w8_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "rmm_swiglu_scored_workspace_bytes": (_sz, [_i64, _i64]),
@@ -320,11 +320,22 @@ def rmm_rmsnorm_scored(X: torch.Tensor, w: torch.Tensor, eps: float = 1e-5, Y: t
     return Y, scores
 
 
+def _scores_ptr(t: torch.Tensor | None, shape, dev):
+    """Pointer of an optional float32 score output of the given shape (None: NULL)."""
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape) or t.device != dev:
+        raise ValueError(f"scores must be contiguous float32 {tuple(shape)} on {dev}")
+    return _ptr(t)
+
+
 def rmm_qk(Q: torch.Tensor, Kt: torch.Tensor, k: int, S: torch.Tensor | None = None,
-           idx: torch.Tensor | None = None, ws: torch.Tensor | None = None, causal: bool = False):
+           idx: torch.Tensor | None = None, ws: torch.Tensor | None = None, causal: bool = False,
+           feat_scores: torch.Tensor | None = None):
     """Feature-reduced scores. Q [Lq, Hq, dh], Kt [Hkv, dh, Lk] (bf16) ->
     (S float32 [Hq, Lq, Lk], idx int32 [Hq, k_pad]).  causal=True leaves tiles
-    above the causal diagonal unwritten."""
+    above the causal diagonal unwritten.  feat_scores (optional float32 [Hq, dh])
+    receives the column scores the selection used."""
     lib = load()
     dev = _dev(Q, Kt)
     if Q.dtype != torch.bfloat16 or Kt.dtype != torch.bfloat16:
@@ -343,16 +354,17 @@ def rmm_qk(Q: torch.Tensor, Kt: torch.Tensor, k: int, S: torch.Tensor | None = N
     ws, wsb = _ws(int(lib.rmm_qk_workspace_bytes(Lq, Hq, dh, int(k))), dev, ws)
     _check(lib.rmm_qk(_ptr(Q), Lq, Hq, dh, Q.stride(0), Q.stride(1), _ptr(Kt), Lk, Hkv, Kt.stride(0),
                       Kt.stride(1), int(k), 1 if causal else 0, _ptr(S), S.stride(0), S.stride(1), _ptr(idx),
-                      _ptr(ws), wsb,
-                      _stream(dev)))
+                      _scores_ptr(feat_scores, (Hq, dh), dev), _ptr(ws), wsb, _stream(dev)))
     return S, idx
 
 
 def rmm_pv(P: torch.Tensor, V: torch.Tensor, k: int, O: torch.Tensor | None = None,
-           idx: torch.Tensor | None = None, ws: torch.Tensor | None = None, causal: bool = False):
+           idx: torch.Tensor | None = None, ws: torch.Tensor | None = None, causal: bool = False,
+           tok_scores: torch.Tensor | None = None):
     """Token-reduced output. P [Hq, Lq, Lk], V [Lk, Hkv, dh] (bf16) ->
     (O bf16 [Lq, Hq, dh], idx int32 [Hq, k_pad]).  causal=True: P above the
-    causal diagonal is taken as zero and never read."""
+    causal diagonal is taken as zero and never read.  tok_scores (optional
+    float32 [Hq, Lk]) receives the token scores the selection used."""
     lib = load()
     dev = _dev(P, V)
     if P.dtype != torch.bfloat16 or V.dtype != torch.bfloat16:
@@ -371,8 +383,7 @@ def rmm_pv(P: torch.Tensor, V: torch.Tensor, k: int, O: torch.Tensor | None = No
     ws, wsb = _ws(int(lib.rmm_pv_workspace_bytes(Hq, Lq, Lk, int(k))), dev, ws)
     _check(lib.rmm_pv(_ptr(P), Hq, Lq, Lk, P.stride(0), P.stride(1), _ptr(V), Hkv, dh, V.stride(0),
                       V.stride(1), int(k), 1 if causal else 0, _ptr(O), O.stride(0), O.stride(1), _ptr(idx),
-                      _ptr(ws), wsb,
-                      _stream(dev)))
+                      _scores_ptr(tok_scores, (Hq, Lk), dev), _ptr(ws), wsb, _stream(dev)))
     return O, idx
 
 

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "mfma_gemm.h"
@@ -98,26 +99,77 @@ RMM_API const char *rmm_status_string(int s) {
 
 RMM_API const char *rmm_last_error(void) { return g_last_error; }
 
+// rho as the decimal the caller wrote: the shortest decimal string that reads
+// back as the same double, mantissa digits p and exponent q (rho = p * 10^-q),
+// among equally short strings the one nearest rho.  Returns false only if no
+// string of at most 17 significant digits round-trips (cannot happen for a
+// finite double).
+static bool shortest_decimal(double rho, uint64_t *p_out, int *q_out) {
+  for (int prec = 0; prec <= 16; ++prec) {
+    char buf[64];
+    snprintf(buf, sizeof(buf), "%.*e", prec, rho);
+    // digits before 'e' (any decimal separator skipped), then the exponent
+    uint64_t mant = 0;
+    int ndig = 0;
+    const char *c = buf;
+    for (; *c && *c != 'e' && *c != 'E'; ++c)
+      if (*c >= '0' && *c <= '9') {
+        mant = mant * 10 + (uint64_t)(*c - '0');
+        ++ndig;
+      }
+    if (*c != 'e' && *c != 'E') return false;
+    const int e10 = atoi(c + 1);
+    // rho = mant * 10^(e10 - (ndig - 1)).  The nearest string of this length
+    // (the correctly rounded one) is tried first; when it does not read back
+    // (rho a power of two, whose rounding interval is lopsided), the one
+    // neighbour on the far side of rho may.  No other string of this length
+    // can: the rounding interval is contiguous and holds rho.
+    const int q = (ndig - 1) - e10;
+    uint64_t best = 0;
+    const uint64_t cands[3] = {mant, mant - 1, mant + 1};
+    for (int ci = 0; ci < 3 && best == 0; ++ci) {
+      if (cands[ci] == 0) continue;
+      char tb[64];
+      snprintf(tb, sizeof(tb), "%llue%d", (unsigned long long)cands[ci], -q);
+      if (strtod(tb, nullptr) == rho) best = cands[ci];
+    }
+    if (best != 0) {
+      // strip trailing zeros so that p and q are in lowest decimal form
+      int qq = q;
+      while (best % 10 == 0 && best != 0) {
+        best /= 10;
+        --qq;
+      }
+      *p_out = best;
+      *q_out = qq;
+      return true;
+    }
+  }
+  return false;
+}
+
 RMM_API rmm_status_t rmm_k_from_rho(double rho, int64_t d, int64_t *k) {
   if (!k) return fail(RMM_ERR_INVALID_ARG, "k_from_rho: k is NULL");
   if (!(rho > 0.0 && rho <= 1.0)) return fail(RMM_ERR_INVALID_ARG, "k_from_rho: rho must lie in (0, 1]");
   if (d < 1 || d >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "k_from_rho: d out of range");
-  // Exact product rho*d = hi + lo (error-free transformation with an fma).
-  const double dd = (double)d;
-  const double hi = rho * dd;
-  const double lo = fma(rho, dd, -hi);
-  const double n = nearbyint(hi);
-  // rho carries a relative representation error of at most 2^-53; its
-  // product with d is therefore within d*2^-53 of the decimal value.  Allow
-  // twice that before treating the product as a non-integer.
-  const double tol = dd * ldexp(1.0, -52);
+  // k = ceil(p * d / 10^q), exact in 128-bit integers: p < 10^17 and d < 2^31,
+  // so p * d < 10^27; for q >= 27 the quotient lies in (0, 1) and k = 1.
+  uint64_t p = 0;
+  int q = 0;
+  if (!shortest_decimal(rho, &p, &q)) return fail(RMM_ERR_INVALID_ARG, "k_from_rho: rho has no decimal form");
+  const unsigned __int128 num = (unsigned __int128)p * (unsigned __int128)(uint64_t)d;
   int64_t kk;
-  if (fabs((hi - n) + lo) <= tol) {
-    kk = (int64_t)n;
+  if (q <= 0) {
+    // rho = p * 10^|q| <= 1 means p = 1, q = 0
+    unsigned __int128 v = num;
+    for (int i = 0; i < -q; ++i) v *= 10;
+    kk = v > (unsigned __int128)d ? d : (int64_t)v;
+  } else if (q >= 27) {
+    kk = 1;
   } else {
-    double c = ceil(hi);
-    if (c == hi && lo > 0.0) c += 1.0;  // hi integral but the exact product exceeds it
-    kk = (int64_t)c;
+    unsigned __int128 den = 1;
+    for (int i = 0; i < q; ++i) den *= 10;
+    kk = (int64_t)((num + den - 1) / den);
   }
   if (kk < 1) kk = 1;
   if (kk > d) kk = d;
@@ -183,13 +235,11 @@ RMM_API rmm_status_t rmm_topk(const float *scores, int64_t batch, int64_t d, int
 // Many-row bf16 products also keep a transposed copy of the kept weight rows.
 // The persistent 256 x 256 NT kernel needs enough output tiles to occupy the
 // chip; smaller outputs (e.g. 2048 x 2048) run on the 128 x 128 row-gather core.
-#ifndef RMM_NT_MIN_TILES
-#define RMM_NT_MIN_TILES 192
-#endif
+constexpr int64_t kNtMinTiles = 192;
 static bool gemm_uses_nt(rmm_dtype_t dt, int64_t m, int64_t n = -1) {
   if (dt != RMM_BF16 || m < 1024) return false;
   if (n < 0) return true;
-  return ((m + 255) / 256) * ((n + 255) / 256) >= RMM_NT_MIN_TILES;
+  return ((m + 255) / 256) * ((n + 255) / 256) >= kNtMinTiles;
 }
 
 RMM_API size_t rmm_gemm_workspace_bytes(rmm_dtype_t dt, int64_t m, int64_t n, int64_t k) {
@@ -410,8 +460,8 @@ RMM_API size_t rmm_qk_workspace_bytes(int64_t Lq, int64_t Hq, int64_t dh, int64_
 RMM_API rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, int64_t q_tok_stride,
                             int64_t q_head_stride, const void *Kt, int64_t Lk, int64_t Hkv,
                             int64_t kt_head_stride, int64_t ldkt, int64_t k, int causal, float *S,
-                            int64_t s_head_stride, int64_t lds, int32_t *idx, void *ws,
-                            size_t ws_bytes, rmm_stream_t stream) {
+                            int64_t s_head_stride, int64_t lds, int32_t *idx, float *feat_scores,
+                            void *ws, size_t ws_bytes, rmm_stream_t stream) {
   if (!Q || !Kt || !S || !idx) return fail(RMM_ERR_INVALID_ARG, "qk: NULL pointer");
   if (Lq < 1 || Lk < 1 || dh < 1 || Lk >= kMaxDim || dh >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "qk: bad Lq, Lk or dh");
   if (Hq < 1 || Hq > kMaxBatch || Hkv < 1 || Hkv > Hq || Hq % Hkv != 0)
@@ -420,15 +470,21 @@ RMM_API rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, i
   if (q_tok_stride < 0 || q_head_stride < 0 || kt_head_stride < 0 || s_head_stride < 0)
     return fail(RMM_ERR_INVALID_ARG, "qk: negative stride");
   if (ldkt < Lk || lds < Lk || q_tok_stride < dh) return fail(RMM_ERR_INVALID_ARG, "qk: leading dimension too small");
-  if (!aligned(Q, 2) || !aligned(Kt, 2) || !aligned(S, 4) || !aligned(idx, 4))
+  if (!aligned(Q, 2) || !aligned(Kt, 2) || !aligned(S, 4) || !aligned(idx, 4) ||
+      (feat_scores && !aligned(feat_scores, 4)))
     return fail(RMM_ERR_INVALID_ARG, "qk: misaligned pointer");
+  const int64_t k_pad = rmm_k_pad(k);
+  if (!rmm::qk_layout_ok(Lq, dh, ldkt, Lk, k_pad))
+    return fail(RMM_ERR_UNSUPPORTED, "qk: the rows of one key head exceed 4 GiB");
+  if (!rmm::qk_tiles_ok(Lq, Lk, causal != 0))
+    return fail(RMM_ERR_UNSUPPORTED, "qk: the tile list of Lq = %lld, Lk = %lld is not served",
+                (long long)Lq, (long long)Lk);
   size_t o_sc, o_part, o_pack, o_idx;
   const size_t need = qk_layout(Lq, Hq, dh, k, &o_sc, &o_part, &o_pack, &o_idx);
   if (!ws || ws_bytes < need || !aligned(ws, 256)) return fail(RMM_ERR_WORKSPACE, "qk: workspace needs %zu bytes (256-byte aligned)", need);
   char *w = static_cast<char *>(ws);
-  float *scores = reinterpret_cast<float *>(w + o_sc);
+  float *scores = feat_scores ? feat_scores : reinterpret_cast<float *>(w + o_sc);
   hipStream_t st = (hipStream_t)stream;
-  const int64_t k_pad = rmm_k_pad(k);
 
   const rmm::ColnormPlan p = plan_for(RMM_BF16, Q, Lq, dh, q_tok_stride, Hq, q_head_stride);
   hipError_t he = rmm::launch_colnorm(RMM_BF16, Q, Lq, dh, q_tok_stride, Hq, q_head_stride, scores,
@@ -440,8 +496,6 @@ RMM_API rmm_status_t rmm_qk(const void *Q, int64_t Lq, int64_t Hq, int64_t dh, i
   he = rmm::launch_pack(RMM_BF16, Q, q_tok_stride, q_head_stride, idx, k_pad, Hq, Lq, dh, k, k_pad,
                         w + o_pack, idx_clean, st);
   if (he != hipSuccess) return hip_status(he, "qk pack launch");
-  if (!rmm::qk_layout_ok(Lq, dh, ldkt, Lk, k_pad))
-    return fail(RMM_ERR_UNSUPPORTED, "qk: the rows of one key head exceed 4 GiB");
   return hip_status(rmm::launch_qk(w + o_pack, idx_clean, Kt, kt_head_stride, ldkt, S, s_head_stride, lds, Hq,
                                    Hkv, Lq, Lk, dh, k_pad, causal != 0, st),
                     "qk gemm launch");
@@ -469,8 +523,8 @@ RMM_API size_t rmm_pv_workspace_bytes(int64_t Hq, int64_t Lq, int64_t Lk, int64_
 RMM_API rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, int64_t p_head_stride,
                             int64_t ldp, const void *V, int64_t Hkv, int64_t dh,
                             int64_t v_tok_stride, int64_t v_head_stride, int64_t k, int causal, void *O,
-                            int64_t o_tok_stride, int64_t o_head_stride, int32_t *idx, void *ws,
-                            size_t ws_bytes, rmm_stream_t stream) {
+                            int64_t o_tok_stride, int64_t o_head_stride, int32_t *idx, float *tok_scores,
+                            void *ws, size_t ws_bytes, rmm_stream_t stream) {
   if (!P || !V || !O || !idx) return fail(RMM_ERR_INVALID_ARG, "pv: NULL pointer");
   if (Lq < 1 || Lk < 1 || dh < 1 || Lk >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "pv: bad Lq, Lk or dh");
   if (Lk > rmm::pv_max_tokens()) return fail(RMM_ERR_UNSUPPORTED, "pv: Lk above %lld", (long long)rmm::pv_max_tokens());
@@ -480,7 +534,8 @@ RMM_API rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, i
   if (p_head_stride < 0 || v_tok_stride < 0 || v_head_stride < 0 || o_tok_stride < 0 || o_head_stride < 0)
     return fail(RMM_ERR_INVALID_ARG, "pv: negative stride");
   if (ldp < Lk) return fail(RMM_ERR_INVALID_ARG, "pv: ldp < Lk");
-  if (!aligned(P, 2) || !aligned(V, 2) || !aligned(O, 2) || !aligned(idx, 4))
+  if (!aligned(P, 2) || !aligned(V, 2) || !aligned(O, 2) || !aligned(idx, 4) ||
+      (tok_scores && !aligned(tok_scores, 4)))
     return fail(RMM_ERR_INVALID_ARG, "pv: misaligned pointer");
   if (!rmm::pv_layout_ok(P, ldp, p_head_stride, V, v_tok_stride, v_head_stride, Lk, dh))
     return fail(RMM_ERR_UNSUPPORTED, "pv: a 256-row block of P or the rows of one V head exceed 4 GiB");
@@ -488,7 +543,7 @@ RMM_API rmm_status_t rmm_pv(const void *P, int64_t Hq, int64_t Lq, int64_t Lk, i
   const size_t need = pv_layout(Hq, Lq, Lk, k, &o_sc, &o_part, &o_plan);
   if (!ws || ws_bytes < need || !aligned(ws, 256)) return fail(RMM_ERR_WORKSPACE, "pv: workspace needs %zu bytes (256-byte aligned)", need);
   char *w = static_cast<char *>(ws);
-  float *scores = reinterpret_cast<float *>(w + o_sc);
+  float *scores = tok_scores ? tok_scores : reinterpret_cast<float *>(w + o_sc);
   hipStream_t st = (hipStream_t)stream;
   const int64_t k_pad = rmm_k_pad(k);
 
@@ -808,7 +863,7 @@ RMM_API rmm_status_t rmm_attention_decode_batch(
   if (he != hipSuccess) return hip_status(he, "attention_decode_batch scores launch");
   he = rmm::launch_attn_decode(1, dd, st);
   if (he != hipSuccess) return hip_status(he, "attention_decode_batch token scores launch");
-  he = rmm::launch_topk(tokd, rows, Lmax, kt_max, ktp, idx_tok, st, k_tok, (int)Hq);
+  he = rmm::launch_topk(tokd, rows, Lmax, kt_max, ktp, idx_tok, st, k_tok, (int)Hq, lens);
   if (he != hipSuccess) return hip_status(he, "attention_decode_batch token topk launch");
   he = rmm::launch_attn_decode(2, dd, st);
   if (he != hipSuccess) return hip_status(he, "attention_decode_batch output launch");

@@ -484,14 +484,8 @@ __global__ __launch_bounds__(kThreads) void attn_out_kernel(AttnArgs g) {
 constexpr int kWaves2 = 4;
 constexpr int kThreads2 = 64 * kWaves2;
 
-#ifndef RMM_ATTN_OUT2_WPE
-#define RMM_ATTN_OUT2_WPE 2
-#endif
-#ifndef RMM_ATTN_OUT2_KCACHE
-#define RMM_ATTN_OUT2_KCACHE 0
-#endif
 template <int KF>
-__global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(RMM_ATTN_OUT2_WPE))) void attn_out2_kernel(AttnArgs g) {
+__global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(2))) void attn_out2_kernel(AttnArgs g) {
   constexpr int VT_BYTES = 128 * kT * 2;                      // V_J^T tile [128 d][64 kept]
   constexpr int STAGE = Tile<KF>::BYTES + VT_BYTES + kT * 4;  // + kept token ids
   constexpr int K_PER_WAVE = Tile<KF>::BLOCKS / kWaves2;
@@ -569,11 +563,6 @@ __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(RMM_A
     const uint16_t *vt = reinterpret_cast<const uint16_t *>(cur + Tile<KF>::BYTES);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-#if RMM_ATTN_OUT2_KCACHE
-      bf16x8_t kfr[KF / 16];
-#pragma unroll
-      for (int ks = 0; ks < KF / 16; ++ks) kfr[ks] = lds_frag<KF>(cur, sub * 32 + (lane & 31), ks, lk);
-#endif
       const int js0 = t * kT + sub * 32;
       const int last_tok = jt[sub * 32 + 31];
       bf16x8_t pf[2][2];
@@ -584,11 +573,7 @@ __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(RMM_A
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KF / 16; ++ks) {
-#if RMM_ATTN_OUT2_KCACHE
-          const bf16x8_t kf8 = kfr[ks];
-#else
           const bf16x8_t kf8 = lds_frag<KF>(cur, sub * 32 + (lane & 31), ks, lk);
-#endif
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf8, qf[gq][ks], acc, 0, 0, 0);
         }
         // Every query of the group sees every token of the slice unless the
@@ -734,11 +719,7 @@ hipError_t launch_attn_passes(int pass, const AttnDesc &d, hipStream_t st) {
     KernelTimer timer("attn_out", st);
     dim3 grid((unsigned)(g.blocks_q * g.hq));
     if (kf128) hipLaunchKernelGGL(attn_out_kernel<128>, grid, dim3(kThreads), 0, st, g);
-#ifndef RMM_ATTN_OUT1
     else hipLaunchKernelGGL(attn_out2_kernel<64>, grid, dim3(kThreads2), 0, st, g);
-#else
-    else hipLaunchKernelGGL(attn_out_kernel<64>, grid, dim3(kThreads), 0, st, g);
-#endif
   }
   return hipGetLastError();
 }

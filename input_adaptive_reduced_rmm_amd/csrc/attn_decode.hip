@@ -33,10 +33,7 @@ namespace rmm {
 namespace {
 
 constexpr int kDB = 256;   // keys (or kept tokens) per workgroup pass, one per thread
-#ifndef RMM_DEC_TOKSUB
-#define RMM_DEC_TOKSUB 1
-#endif
-constexpr int kTokSub = RMM_DEC_TOKSUB;   // 256-token sub-tiles per output workgroup
+constexpr int kTokSub = 1;   // 256-token sub-tiles per output workgroup
 constexpr float kNegInfD = -__builtin_inff();
 
 __device__ __forceinline__ float dexp2(float x) { return __builtin_amdgcn_exp2f(x); }

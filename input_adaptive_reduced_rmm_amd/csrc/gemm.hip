@@ -342,9 +342,7 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, OutType out, hipStream_t st) {
       return launch_core<128, 128, float, 2>(g, "gemm_f32out", st);
     }
     const int64_t t256 = ((g.m + 255) / 256) * ((g.n + 255) / 256) * g.batch;
-#ifndef RMM_PROBE_NO_256
     if (t256 >= 200) return launch_core<256, 256, uint16_t, 2>(g, "gemm_256", st);
-#endif
     return launch_core<128, 128, uint16_t, 2>(g, "gemm_128", st);
   }
   const bool bvec = (reinterpret_cast<uintptr_t>(g.B) % 16 == 0) && (g.ldb % 8 == 0) &&

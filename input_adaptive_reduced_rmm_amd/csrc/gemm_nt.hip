@@ -272,12 +272,7 @@ __global__ __launch_bounds__(128 * WGN) __attribute__((amdgpu_waves_per_eu(WGN /
 #pragma unroll
       for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(fa[c]), "+v"(fb[c]));
       const uint32_t so = (uint32_t)(kt & 1) * TILE;
-#ifndef RMM_NT_IGLP
-#define RMM_NT_IGLP 1
-#endif
-#if RMM_NT_IGLP >= 0
-      __builtin_amdgcn_iglp_opt(RMM_NT_IGLP);   // interleave fragment reads with the MFMAs
-#endif
+      __builtin_amdgcn_iglp_opt(1);   // interleave fragment reads with the MFMAs
 #pragma unroll
       for (int ks = 0; ks < KS - 1; ++ks) {
         frags(so, ks + 1, (ks + 1) & 1);

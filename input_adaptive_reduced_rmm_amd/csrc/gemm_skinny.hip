@@ -70,17 +70,8 @@ __device__ __forceinline__ uint32_t i8_to_bf16_bits(uint32_t w, int byte) {
   return __float_as_uint((float)v) >> 16;
 }
 
-#ifndef RMM_SKINNY_W8_BN
-#define RMM_SKINNY_W8_BN 256
-#endif
-constexpr int kW8BN = RMM_SKINNY_W8_BN;
-#ifndef RMM_SKINNY_PD_BF16
-#define RMM_SKINNY_PD_BF16 2
-#endif
-#ifndef RMM_SKINNY_PD_W8
-#define RMM_SKINNY_PD_W8 4
-#endif
-constexpr int kPdBf16 = RMM_SKINNY_PD_BF16, kPdW8 = RMM_SKINNY_PD_W8;
+constexpr int kW8BN = 256;
+constexpr int kPdBf16 = 2, kPdW8 = 4;
 
 template <bool W8>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
@@ -298,19 +289,14 @@ struct SkinnyPlan {
 // Workgroups per CU the grid aims at: about one resident round (LDS allows
 // 3 bf16 or 2 int8 workgroups per CU), so each workgroup streams a long run
 // of K-tiles instead of paying the pipeline fill many times.
-#ifndef RMM_SKINNY_WG_BF16
-#define RMM_SKINNY_WG_BF16 4
-#endif
-#ifndef RMM_SKINNY_WG_W8
-#define RMM_SKINNY_WG_W8 2
-#endif
+constexpr int kWgBf16 = 4, kWgW8 = 2;
 
 SkinnyPlan skinny_plan(bool w8, int64_t n, int64_t k_pad) {
   const int64_t bn = w8 ? kW8BN : 128;
   SkinnyPlan p;
   p.tiles_n = (int)((n + bn - 1) / bn);
   const int64_t nk = k_pad / kBK;
-  const int64_t target = 256 * (w8 ? RMM_SKINNY_WG_W8 : RMM_SKINNY_WG_BF16);
+  const int64_t target = 256 * (w8 ? kWgW8 : kWgBf16);
   // Enough workgroups for the target, at least 4 K-tiles each, at most what LDS stages.
   int64_t splits = (target + p.tiles_n - 1) / p.tiles_n;
   const int64_t max_by_depth = nk / 4 > 0 ? nk / 4 : 1;

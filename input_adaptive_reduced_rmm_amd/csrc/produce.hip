@@ -96,10 +96,7 @@ __global__ __launch_bounds__(64 * kWaves) void swiglu_scored_kernel(const uint16
 // threads.  kRmsRows rows are in flight per thread; their sums of squares meet
 // through a double-buffered LDS array (one barrier per kRmsRows rows, the
 // waves' parts added in wave order).
-#ifndef RMM_RMS_ROWS
-#define RMM_RMS_ROWS 4
-#endif
-constexpr int kRmsRows = RMM_RMS_ROWS;
+constexpr int kRmsRows = 4;
 
 __global__ __launch_bounds__(1024) void rmsnorm_scored_kernel(const uint16_t *__restrict__ X, int64_t ldx,
                                                                const uint16_t *__restrict__ w, float eps, int64_t m,
@@ -195,11 +192,9 @@ SwigluPlan swiglu_plan(int64_t m, int64_t n) {
   return p;
 }
 
-#ifndef RMM_RMS_BLOCKS
-#define RMM_RMS_BLOCKS 512
-#endif
-// About RMM_RMS_BLOCKS workgroups, each a whole number of row groups.
-int64_t rmsnorm_rows_per_chunk(int64_t m) { return ceil_div(ceil_div(m, RMM_RMS_BLOCKS), kRmsRows) * kRmsRows; }
+// About 512 workgroups, each a whole number of row groups.
+constexpr int64_t kRmsBlocks = 512;
+int64_t rmsnorm_rows_per_chunk(int64_t m) { return ceil_div(ceil_div(m, kRmsBlocks), kRmsRows) * kRmsRows; }
 
 }  // namespace
 

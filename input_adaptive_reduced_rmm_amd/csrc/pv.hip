@@ -178,10 +178,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int row = (tid >> 3) + 32 * i;
-#ifndef RMM_PV_POL
-#define RMM_PV_POL mg::kCached
-#endif
-      ra[S][i] = mg::load_chunk<AVEC, RMM_PV_POL>(rp, (uint32_t)(((int64_t)row * g.ldp + c0 + akc * 8) * 2));
+      ra[S][i] = mg::load_chunk<AVEC, mg::kCached>(rp, (uint32_t)(((int64_t)row * g.ldp + c0 + akc * 8) * 2));
     }
 #pragma unroll
     for (int r = 0; r < KB; ++r) {
@@ -344,13 +341,7 @@ hipError_t launch_pv(const void *P, int64_t ldp, int64_t p_hs, const void *V, in
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-#ifndef RMM_PV_BM
-#define RMM_PV_BM 128
-#endif
-#ifndef RMM_PV_PD
-#define RMM_PV_PD 2
-#endif
-  constexpr int BM = RMM_PV_BM, PD = RMM_PV_PD;
+  constexpr int BM = 128, PD = 2;
   PvArgs a{};
   a.P = static_cast<const uint16_t *>(P);
   a.ldp = ldp;

@@ -58,9 +58,7 @@ constexpr int kStageBytes = 4 * 32 * kPitch * 4;           // 4 waves x 32 rows
 constexpr int kSmemBytes = kOperandBytes > kStageBytes ? kOperandBytes : kStageBytes;
 
 // Resident workgroups per CU (four waves each; the register count allows two).
-#ifndef RMM_QK_BPC
-#define RMM_QK_BPC 2
-#endif
+constexpr int kQkBlocksPerCu = 2;
 
 // BSTORE: S is written with buffer stores whose resource drops rows past Lq
 // and whose offsets drop columns past Lk, so every tile issues the same number
@@ -272,6 +270,42 @@ bool qk_layout_ok(int64_t Lq, int64_t dh, int64_t ldkt, int64_t Lk, int64_t k_pa
          (uint64_t)((dh - 1) * ldkt + Lk) * 2 < mg::kMaxRecords && Lq > 0;
 }
 
+namespace {
+// The tile list of one head: tiles_m rows of 128-query tiles, row r holding
+// column tiles 0 .. clamp(r + c0, 0, tiles_n) - 1, per_head tiles in all.
+struct QkTiles {
+  int64_t tiles_m, tiles_n, c0, per_head;
+  bool ok;   // the closed form agrees with the direct sum
+};
+QkTiles qk_tiles(int64_t Lq, int64_t Lk, bool causal) {
+  QkTiles t;
+  t.tiles_m = ceil_div(Lq, kT);
+  t.tiles_n = ceil_div(Lk, kT);
+  if (causal) {
+    // row r of tiles spans rows r*128 .. r*128+127; it needs columns up to
+    // r*128 + 127 + (Lk - Lq), i.e. tiles 0 .. r + floor((127 + off) / 128).
+    const int64_t off = Lk - Lq;
+    const int64_t num = kT - 1 + off;
+    const int64_t fl = num >= 0 ? num / kT : -((-num + kT - 1) / kT);
+    t.c0 = 1 + fl;
+  } else {
+    t.c0 = t.tiles_n;  // every row holds all tiles
+  }
+  // The kernel locates tiles with the closed form; cross-check it against the
+  // direct sum.
+  int64_t direct = 0;
+  for (int64_t r = 0; r < t.tiles_m; ++r) {
+    const int64_t c = r + t.c0;
+    direct += c < 0 ? 0 : (c > t.tiles_n ? t.tiles_n : c);
+  }
+  t.per_head = tiles_before(t.tiles_m, t.c0, t.tiles_n);
+  t.ok = t.per_head == direct;
+  return t;
+}
+}  // namespace
+
+bool qk_tiles_ok(int64_t Lq, int64_t Lk, bool causal) { return Lq > 0 && Lk > 0 && qk_tiles(Lq, Lk, causal).ok; }
+
 hipError_t launch_qk(const void *Apacked, const int32_t *idx_clean, const void *Kt, int64_t kt_hs,
                      int64_t ldkt, float *S, int64_t s_hs, int64_t lds, int64_t hq, int64_t hkv,
                      int64_t Lq, int64_t Lk, int64_t dh, int64_t k_pad, bool causal, hipStream_t st) {
@@ -290,26 +324,11 @@ hipError_t launch_qk(const void *Apacked, const int32_t *idx_clean, const void *
   g.Lk = Lk;
   g.dh = dh;
   g.k_pad = k_pad;
-  g.tiles_m = ceil_div(Lq, kT);
-  g.tiles_n = ceil_div(Lk, kT);
-  if (causal) {
-    // row r of tiles spans rows r*128 .. r*128+127; it needs columns up to
-    // r*128 + 127 + (Lk - Lq), i.e. tiles 0 .. r + floor((127 + off) / 128).
-    const int64_t off = Lk - Lq;
-    const int64_t num = kT - 1 + off;
-    const int64_t fl = num >= 0 ? num / kT : -((-num + kT - 1) / kT);
-    g.c0 = 1 + fl;
-  } else {
-    g.c0 = g.tiles_n;  // every row holds all tiles
-  }
-  // Closed form, cross-checked against the direct sum (the kernel relies on it).
-  int64_t direct = 0;
-  for (int64_t r = 0; r < g.tiles_m; ++r) {
-    int64_t c = r + g.c0;
-    direct += c < 0 ? 0 : (c > g.tiles_n ? g.tiles_n : c);
-  }
-  g.per_head = tiles_before(g.tiles_m, g.c0, g.tiles_n);
-  if (g.per_head != direct) return hipErrorInvalidValue;
+  const QkTiles t = qk_tiles(Lq, Lk, causal);   // rmm_qk has checked t.ok before any launch
+  g.tiles_m = t.tiles_m;
+  g.tiles_n = t.tiles_n;
+  g.c0 = t.c0;
+  g.per_head = t.per_head;
   g.total = g.per_head * hq;
   if (g.total == 0) return hipSuccess;
   const bool bvec = reinterpret_cast<uintptr_t>(Kt) % 16 == 0 && ldkt % 8 == 0 && kt_hs % 8 == 0;
@@ -319,7 +338,7 @@ hipError_t launch_qk(const void *Apacked, const int32_t *idx_clean, const void *
   // 3.29 ms at k_pad = 64).
   const bool bstore = k_pad > mg::kBK && reinterpret_cast<uintptr_t>(S) % 16 == 0 && lds % 4 == 0 &&
                       s_hs % 4 == 0 && Lk % 4 == 0 && (uint64_t)32 * lds * 4 < mg::kMaxRecords;
-  int64_t grid = 256 * RMM_QK_BPC;
+  int64_t grid = 256 * kQkBlocksPerCu;
   if (grid > g.total) grid = g.total;
   KernelTimer timer("qk_gemm", st);
   const dim3 gr((unsigned)grid), blk(256);

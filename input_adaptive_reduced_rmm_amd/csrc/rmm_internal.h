@@ -65,8 +65,11 @@ hipError_t launch_rmsnorm_scored(const void *X, int64_t ldx, const void *w, floa
                                  int64_t ldy, float *scores, float *part, hipStream_t stream);
 
 // ------------------------------------------------------------------ top-k
+// k_rows / len_rows (optional, device): per-row kept count and valid length of
+// row b read at [b / k_div]; the count is clamped to [1, min(k, d, length)].
 hipError_t launch_topk(const float *scores, int64_t batch, int64_t d, int64_t k, int64_t k_pad,
-                       int32_t *idx, hipStream_t stream, const int32_t *k_rows = nullptr, int k_div = 1);
+                       int32_t *idx, hipStream_t stream, const int32_t *k_rows = nullptr, int k_div = 1,
+                       const int32_t *len_rows = nullptr);
 
 // ------------------------------------------------------------------ pack
 // out[b][i][t] = A[b][i][idx[b][t]] for t < k (0 when idx is out of [0,d)), 0 for k <= t < k_pad.
@@ -119,6 +122,8 @@ hipError_t launch_gemm_nt(const void *A_packed, const int32_t *idx_clean, const 
 
 // ------------------------------------------------------------------ feature-reduced Q K^T
 bool qk_layout_ok(int64_t Lq, int64_t dh, int64_t ldkt, int64_t Lk, int64_t k_pad);
+// The closed-form tile list of the (causal) product agrees with its direct sum.
+bool qk_tiles_ok(int64_t Lq, int64_t Lk, bool causal);
 hipError_t launch_qk(const void *Apacked, const int32_t *idx_clean, const void *Kt, int64_t kt_hs,
                      int64_t ldkt, float *S, int64_t s_hs, int64_t lds, int64_t hq, int64_t hkv,
                      int64_t Lq, int64_t Lk, int64_t dh, int64_t k_pad, bool causal, hipStream_t stream);

@@ -33,13 +33,17 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 // NT threads per workgroup: 1024 for long rows, 256 for short ones (fewer
 // waves meet at each of the select's barriers).
 // k_rows (optional): row b keeps k_rows[b / k_div] indices instead of k,
-// clamped to [1, min(k, d)] (ragged batches: one count per sequence, shared
-// by its heads; k is then the largest count, which sizes the output rows).
+// clamped to [1, min(k, d, len)] (ragged batches: one count per sequence,
+// shared by its heads; k is then the largest count, which sizes the output
+// rows).  len_rows (optional, with k_rows): the row's valid length
+// len_rows[b / k_div], itself clamped to [1, d]; scores past it are never
+// kept, so no more than len indices are.
 template <bool IN_LDS, int NT>
 __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scores, int64_t d,
                                                         int64_t k, int64_t k_pad,
                                                         int32_t *__restrict__ idx,
-                                                        const int32_t *__restrict__ k_rows, int k_div) {
+                                                        const int32_t *__restrict__ k_rows,
+                                                        const int32_t *__restrict__ len_rows, int k_div) {
   __shared__ uint32_t keys[IN_LDS ? (NT == 256 ? 4096 : kLdsKeys) : 1];
   // Long rows: kRep copies of the histogram, lane l adding to copy l % kRep
   // (padded to 257 words so the copies' bins sit in different banks): scores
@@ -52,7 +56,13 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (k_rows) {
-    const int64_t kr = k_rows[blockIdx.x / k_div], kmax = k < d ? k : d;
+    int64_t kmax = k < d ? k : d;
+    if (len_rows) {
+      const int64_t L = len_rows[blockIdx.x / k_div];
+      const int64_t Lc = L < 1 ? 1 : (L > d ? d : L);
+      if (Lc < kmax) kmax = Lc;
+    }
+    const int64_t kr = k_rows[blockIdx.x / k_div];
     k = kr < 1 ? 1 : (kr > kmax ? kmax : kr);
   }
   const float *s = scores + (int64_t)blockIdx.x * d;
@@ -254,7 +264,7 @@ __global__ __launch_bounds__(256) void iota_kernel(int64_t d, int64_t k_pad, int
 }  // namespace
 
 hipError_t launch_topk(const float *scores, int64_t batch, int64_t d, int64_t k, int64_t k_pad,
-                       int32_t *idx, hipStream_t st, const int32_t *k_rows, int k_div) {
+                       int32_t *idx, hipStream_t st, const int32_t *k_rows, int k_div, const int32_t *len_rows) {
   KernelTimer timer("topk", st);
   if (k == d && !k_rows) {
     unsigned gx = (unsigned)ceil_div(k_pad, 256);
@@ -265,13 +275,13 @@ hipError_t launch_topk(const float *scores, int64_t batch, int64_t d, int64_t k,
   if (k_div < 1) k_div = 1;
   if (d <= 4096)
     hipLaunchKernelGGL((topk_kernel<true, 256>), dim3((unsigned)batch), dim3(256), 0, st, scores, d, k, k_pad, idx,
-                       k_rows, k_div);
+                       k_rows, len_rows, k_div);
   else if (d <= kLdsKeys)
     hipLaunchKernelGGL((topk_kernel<true, kMaxThreads>), dim3((unsigned)batch), dim3(kMaxThreads), 0, st, scores,
-                       d, k, k_pad, idx, k_rows, k_div);
+                       d, k, k_pad, idx, k_rows, len_rows, k_div);
   else
     hipLaunchKernelGGL((topk_kernel<false, kMaxThreads>), dim3((unsigned)batch), dim3(kMaxThreads), 0, st, scores,
-                       d, k, k_pad, idx, k_rows, k_div);
+                       d, k, k_pad, idx, k_rows, len_rows, k_div);
   return hipGetLastError();
 }
 

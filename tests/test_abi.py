@@ -6,6 +6,7 @@ validation, so they run without a GPU.
 """
 import ctypes
 import json
+import math
 import os
 import re
 
@@ -69,6 +70,56 @@ def test_k_from_rho_matches_oracle_on_random_decimals(lib):
         assert B.rmm_k_from_rho(rho, d) == oracle.retained_count(rho, d), (rho, d)
 
 
+def _adversarial_ratios(rng, n):
+    """Doubles in (0, 1] whose shortest decimal strings are long: random bit
+    patterns, sums of short decimals, the binary neighbours of short decimals,
+    and every power of two down to the smallest subnormal."""
+    out = [0.1 + 0.2, 0.7 + 0.1, 0.1 * 3, 1.0 - 1e-16, 5e-324, 2.2250738585072014e-308,
+           math.nextafter(0.5, 1.0), math.nextafter(0.7, 1.0), math.nextafter(0.7, 0.0),
+           math.nextafter(1.0, 0.0), math.nextafter(0.3, 1.0), math.nextafter(0.55, 0.0)]
+    out += [math.ldexp(1.0, -e) for e in range(0, 1075)]
+    bits = rng.integers(1, 0x3FF0000000000000, size=n // 3, dtype=np.int64)
+    out += [float(x) for x in bits.view(np.float64)]
+    u = rng.random(n // 3)
+    out += [float(x) for x in u if x > 0.0]
+    for _ in range(n // 3):
+        q = int(rng.integers(1, 9))
+        p = int(rng.integers(1, 10 ** q + 1))
+        r = float(f"{p}e-{q}")
+        step = int(rng.integers(-3, 4))
+        for _ in range(abs(step)):
+            r = math.nextafter(r, 1.0 if step > 0 else 0.0)
+        if 0.0 < r <= 1.0:
+            out.append(r)
+    return out
+
+
+def test_k_from_rho_matches_oracle_on_long_decimals(lib):
+    """Integer result: bit-exact against the oracle's exact rational ceiling for
+    ratios whose shortest decimal strings run to 15-17 digits, with d up to 2^31 - 1."""
+    rng = np.random.default_rng(22)
+    ratios = _adversarial_ratios(rng, 100000)
+    ds = rng.integers(1, 2 ** 31 - 1, size=len(ratios))
+    small = rng.integers(1, 1000, size=len(ratios))
+    bad = []
+    for rho, d, ds_ in zip(ratios, ds, small):
+        for dd in (int(d), int(ds_), 10, 100):
+            if B.rmm_k_from_rho(rho, dd) != oracle.retained_count(rho, dd):
+                bad.append((repr(rho), dd))
+    assert not bad, bad[:10]
+
+
+def test_k_from_rho_long_decimal_examples(lib):
+    # worked by hand from the shortest decimal strings
+    assert B.rmm_k_from_rho(0.1 + 0.2, 10) == 4          # 0.30000000000000004 * 10 = 3.0000000000000004
+    assert B.rmm_k_from_rho(0.1 + 0.2, 100) == 31
+    assert B.rmm_k_from_rho(math.nextafter(0.5, 1.0), 2) == 2    # 0.5000000000000001 * 2
+    assert B.rmm_k_from_rho(math.nextafter(0.7, 1.0), 10) == 8   # 0.7000000000000001 * 10
+    assert B.rmm_k_from_rho(math.nextafter(0.7, 0.0), 10) == 7   # 0.6999999999999998 * 10
+    assert B.rmm_k_from_rho(5e-324, 2 ** 31 - 1) == 1
+    assert B.rmm_k_from_rho(1.0, 2 ** 31 - 1) == 2 ** 31 - 1
+
+
 @pytest.mark.parametrize("rho,d", [(0.0, 10), (-0.5, 10), (1.5, 10), (float("nan"), 10), (0.5, 0)])
 def test_k_from_rho_rejects(lib, rho, d):
     with pytest.raises(B.RMMError) as e:
@@ -130,19 +181,19 @@ def test_gemm_rejects(lib):
 def test_qk_pv_reject(lib):
     q = lib.rmm_qk
     # Hq % Hkv != 0
-    assert q(FAKE, 64, 6, 128, 768, 128, FAKE, 64, 4, 8192, 64, 32, 0, FAKE, 4096, 64, FAKE, FAKE, 1 << 30, None) == 1
+    assert q(FAKE, 64, 6, 128, 768, 128, FAKE, 64, 4, 8192, 64, 32, 0, FAKE, 4096, 64, FAKE, None, FAKE, 1 << 30, None) == 1
     # k > dh
-    assert q(FAKE, 64, 4, 128, 512, 128, FAKE, 64, 2, 8192, 64, 129, 0, FAKE, 4096, 64, FAKE, FAKE, 1 << 30, None) == 1
+    assert q(FAKE, 64, 4, 128, 512, 128, FAKE, 64, 2, 8192, 64, 129, 0, FAKE, 4096, 64, FAKE, None, FAKE, 1 << 30, None) == 1
     # q_tok_stride < dh
-    assert q(FAKE, 64, 4, 128, 100, 128, FAKE, 64, 2, 8192, 64, 64, 1, FAKE, 4096, 64, FAKE, FAKE, 1 << 30, None) == 1
+    assert q(FAKE, 64, 4, 128, 100, 128, FAKE, 64, 2, 8192, 64, 64, 1, FAKE, 4096, 64, FAKE, None, FAKE, 1 << 30, None) == 1
     need = lib.rmm_qk_workspace_bytes(64, 4, 128, 64)
-    assert q(FAKE, 64, 4, 128, 512, 128, FAKE, 64, 2, 8192, 64, 64, 0, FAKE, 4096, 64, FAKE, FAKE, need - 1, None) == 3
+    assert q(FAKE, 64, 4, 128, 512, 128, FAKE, 64, 2, 8192, 64, 64, 0, FAKE, 4096, 64, FAKE, None, FAKE, need - 1, None) == 3
     p = lib.rmm_pv
-    assert p(FAKE, 4, 64, 64, 4096, 64, FAKE, 2, 128, 256, 128, 65, 0, FAKE, 512, 128, FAKE, FAKE, 1 << 30, None) == 1
-    assert p(FAKE, 4, 64, 64, 4096, 63, FAKE, 2, 128, 256, 128, 32, 1, FAKE, 512, 128, FAKE, FAKE, 1 << 30, None) == 1
+    assert p(FAKE, 4, 64, 64, 4096, 64, FAKE, 2, 128, 256, 128, 65, 0, FAKE, 512, 128, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert p(FAKE, 4, 64, 64, 4096, 63, FAKE, 2, 128, 256, 128, 32, 1, FAKE, 512, 128, FAKE, None, FAKE, 1 << 30, None) == 1
     need = lib.rmm_pv_workspace_bytes(4, 64, 64, 32)
     assert need > 0
-    assert p(FAKE, 4, 64, 64, 4096, 64, FAKE, 2, 128, 256, 128, 32, 0, FAKE, 512, 128, FAKE, FAKE, need - 1, None) == 3
+    assert p(FAKE, 4, 64, 64, 4096, 64, FAKE, 2, 128, 256, 128, 32, 0, FAKE, 512, 128, FAKE, None, FAKE, need - 1, None) == 3
 
 
 def test_gemm_w8_rejects(lib):

@@ -125,6 +125,8 @@ def test_decode_batch_counts_are_clamped():
             S = oracle.reduced_product(Q[:, h, :], Kt[oracle.kv_head(h, Hq, Hkv)], I[r][:kf])[None]
             P = oracle.causal_softmax(S, 128 ** -0.5)[0]
             assert np.array_equal(J[r][:kt], oracle.select_top(ts[r, :L].astype(np.float64), kt))
+            # the rest of the row is padding: no position at or past lens[b] is listed
+            assert np.all(J[r][kt:] == -1), (b, h, J[r][kt:][J[r][kt:] != -1][:8])
             want = oracle.reduced_product(P, V[:, oracle.kv_head(h, Hq, Hkv), :], J[r][:kt])
             assert rel_fro(O[b, h][None], want) < TOL_BF16
 

@@ -217,8 +217,7 @@ def test_llama70b_decode_projection(name):
     _free()
 
 
-@pytest.mark.parametrize("name", sorted([l.name for l in W70.linears if "@m8192@" in l.name and
-                                         l.rho in (0.3, 0.5, 1.0)]))
+@pytest.mark.parametrize("name", sorted([l.name for l in W70.linears if "@m8192@" in l.name]))
 def test_llama70b_prefill_projection(name):
     lin = [l for l in W70.linears if l.name == name][0]
     check_projection(W70, lin, sample_rows=64)
