@@ -56,37 +56,41 @@ def parse():
                     help="skip the separate timing of the fused reduced attention (rmm_attention)")
     ap.add_argument("--no-producers", action="store_true",
                     help="skip the separate timing of the producer-fused scoring kernels")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the compact timings of the other workloads (default workload only)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
 
 
 # ------------------------------------------------------------------ workload
-def build_layer(wl, args, dev):
-    import numpy as np
+def build_layer(wl, args, dev, cache=None):
+    """The projections and attention of the run's workload, as build_layer_for builds them."""
+    return build_layer_for(wl, _selected(wl, args), dev, args.no_fuse, _has_attention(wl, args), cache)
+
+
+def build_layer_for(wl, lins, dev, no_fuse=False, with_attention=True, cache=None):
+    """Device tensors of the given projections (and the workload's attention):
+    seeded synthetic activations and weights, resident in HBM.  `cache` (a dict)
+    keeps generated tensors for later layers of the same workload (other
+    ratios reuse the same activations and weights)."""
     import torch
 
     import synth
 
+    cache = {} if cache is None else cache
     dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
-    lins = list(wl.linears)
-    if args.rho is not None:
-        lins = [l for l in lins if abs(l.rho - args.rho) < 1e-12]
-    elif wl.key == "llama3.2-1b-proj-2k":
-        lins = [l for l in lins if l.rho == 0.5]
-    if wl.key == "llama3.1-70b-layer":
-        m = args.m if args.m is not None else 8192
-        rho = args.rho if args.rho is not None else 0.5
-        lins = [l for l in wl.linears if l.m == m and abs(l.rho - rho) < 1e-12]
     layer = {"linears": [], "attention": None, "dtype": dt}
-    acts = {}
     for lin in lins:
         key = synth.activation_key(wl, lin)
-        if key not in acts:
-            acts[key] = torch.from_numpy(synth.linear_activation(wl, lin)).to(dev, dt)
-        B = torch.from_numpy(synth.linear_weight(wl, lin)).to(dev, dt)
+        if ("A", key) not in cache:
+            cache[("A", key)] = torch.from_numpy(synth.linear_activation(wl, lin)).to(dev, dt)
+        bkey = ("B", lin.tensor_b, lin.d, lin.n)
+        if bkey not in cache:
+            cache[bkey] = torch.from_numpy(synth.linear_weight(wl, lin)).to(dev, dt)
+        B = cache[bkey]
         prev = [e for e in layer["linears"] if e["akey"] == key and e["rho"] == lin.rho]
-        if prev and not args.no_fuse:
+        if prev and not no_fuse:
             # Same activation and ratio: the selection is the same, so the
             # products are one reduced product over the weights side by side
             # ([d][n1 + n2 ...]), as a fused q|k|v or up|gate projection.
@@ -94,20 +98,22 @@ def build_layer(wl, args, dev):
             e["B"] = torch.cat([e["B"], B], dim=1).contiguous()
             e["n"] += lin.n
             e["name"] = e["name"].split("@")[0] + "+" + lin.name
-            del B
             continue
         layer["linears"].append({
             "name": lin.name, "m": lin.m, "d": lin.d, "n": lin.n, "rho": lin.rho,
-            "A": acts[key], "akey": key, "B": B,
+            "A": cache[("A", key)], "akey": key, "B": B,
         })
-    if wl.attention is not None and (wl.key != "llama3.1-70b-layer" or args.m in (None, 8192)):
+    if wl.attention is not None and with_attention:
         at = wl.attention
-        Q, Kt, V = synth.attention_operands(wl)
-        Qd = torch.from_numpy(Q).to(dev, torch.bfloat16)
-        Ktd = torch.from_numpy(Kt).to(dev, torch.bfloat16)
-        Vd = torch.from_numpy(V).to(dev, torch.bfloat16)
-        del Q, Kt, V
-        P = synth.causal_probs(Qd, Ktd, 1.0 / math.sqrt(at.dh), device=dev)
+        if "attention" not in cache:
+            Q, Kt, V = synth.attention_operands(wl)
+            Qd = torch.from_numpy(Q).to(dev, torch.bfloat16)
+            Ktd = torch.from_numpy(Kt).to(dev, torch.bfloat16)
+            Vd = torch.from_numpy(V).to(dev, torch.bfloat16)
+            del Q, Kt, V
+            P = synth.causal_probs(Qd, Ktd, 1.0 / math.sqrt(at.dh), device=dev)
+            cache["attention"] = (Qd, Ktd, Vd, P)
+        Qd, Ktd, Vd, P = cache["attention"]
         layer["attention"] = {"Q": Qd, "Kt": Ktd, "V": Vd, "P": P, "L": at.L, "Hq": at.Hq, "Hkv": at.Hkv,
                               "dh": at.dh, "rho": at.rho}
     return layer
@@ -713,6 +719,120 @@ def copy_calibration(dev):
     torch.cuda.synchronize()
 
 
+def summarize(run, kern, dtype):
+    """Per-kernel detail of a step, the roofline of its dominant kernel (largest
+    time per step) and the kept-work MFMA fraction of its projection GEMMs."""
+    import torch
+
+    detail = {}
+    best = None
+    for key, v in kern.items():
+        bound, amount, unit = algorithmic_work(run, key)
+        tot = v["avg_ms"] * v["launches_per_step"]
+        ent = {"avg_ms": round(v["avg_ms"], 4), "per_step": v["launches_per_step"]}
+        if bound:
+            rate = amount / (v["avg_ms"] * 1e-3)
+            if unit == "flops":
+                peak = PEAK_F32_TFLOPS if dtype == torch.float32 else PEAK_BF16_TFLOPS
+                ent["tflops"] = round(rate / 1e12, 1)
+                ent["frac"] = round(rate / 1e12 / peak, 4)
+            else:
+                ent["gbs"] = round(rate / 1e9, 1)
+                ent["frac"] = round(rate / 1e9 / PEAK_HBM_GBS, 4)
+        detail[key] = ent
+        if bound and (best is None or tot > best[0]):
+            best = (tot, key, bound, amount, unit, v["avg_ms"])
+    roof = None
+    if best:
+        _, key, bound, amount, unit, avg = best
+        if unit == "flops":
+            peak = PEAK_F32_TFLOPS if dtype == torch.float32 else PEAK_BF16_TFLOPS
+            ach = amount / (avg * 1e-3) / 1e12
+            roof = {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(ach / peak, 4), "kernel": key, "per_launch": f"{amount:.4g} flops",
+                    "avg_launch_ms": round(avg, 4)}
+        else:
+            ach = amount / (avg * 1e-3) / 1e9
+            roof = {"bound": bound, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(ach / PEAK_HBM_GBS, 4), "kernel": key, "per_launch": f"{amount:.4g} bytes",
+                    "avg_launch_ms": round(avg, 4)}
+    g_fl = g_ms = 0.0
+    for key, v in kern.items():
+        bound, amount, unit = algorithmic_work(run, key)
+        if unit == "flops":
+            g_fl += amount * v["launches_per_step"]
+            g_ms += v["avg_ms"] * v["launches_per_step"]
+    peak = PEAK_F32_TFLOPS if dtype == torch.float32 else PEAK_BF16_TFLOPS
+    mfma_frac = (g_fl / (g_ms * 1e-3) / 1e12 / peak) if g_ms > 0 else None
+    return detail, roof, mfma_frac
+
+
+def other_workloads(R, dev, steps, warmup):
+    """Compact timings of the other synthetic workloads, each at its ratios and at
+    rho = 1 (the same pipeline keeping every index): ms per step (mean of `steps`
+    back-to-back steps after `warmup`), effective TFLOP/s, speedup, and the
+    dominant kernel with its roofline fraction.  Launch-bound shapes (the fp32
+    64 x 512 product, the 16-row decode batch) replay the step from a HIP graph."""
+    import torch
+
+    import synth
+
+    out = {}
+    plans = [
+        ("xw-fp32-64x512", [(0.5, None)], True),
+        ("llama3.2-1b-proj-2k", [(0.5, None), (0.7, None), (0.8, None)], False),
+        ("attn-32h-4k", [(None, None)], False),
+        ("llama3.1-70b-layer", [(r, 8192) for r in (0.3, 0.5, 0.7, 0.8, 1.0)] + [(0.5, 16)], None),
+    ]
+    for key, cases, graph in plans:
+        wl = synth.WORKLOADS[key]
+        cache = {}
+        t0 = time.perf_counter()
+        for rho, m in cases:
+            lins = list(wl.linears)
+            if rho is not None:
+                lins = [l for l in lins if abs(l.rho - rho) < 1e-12]
+            if m is not None:
+                lins = [l for l in lins if l.m == m]
+            with_att = wl.attention is not None and (m is None or m == wl.attention.L)
+            layer = build_layer_for(wl, lins, dev, False, with_att, cache)
+            use_graph = graph if graph is not None else (m is not None and m <= 32)
+            run = Runner(R, layer, dev)
+            stepper = GraphStep(run) if use_graph else run
+            ms, _ = time_steps(stepper, steps, warmup)
+            kern = kernel_breakdown(run, max(2, min(steps, 5)))
+            _, roof, mfma = summarize(run, kern, layer["dtype"])
+            run.free()
+            del run, stepper
+            all_kept = all(l.rho == 1.0 for l in lins) and (not with_att or wl.attention.rho == 1.0)
+            if all_kept:
+                ms1 = ms
+            else:
+                run1 = Runner(R, layer, dev, rho_scale_one=True)
+                ms1, _ = time_steps(GraphStep(run1) if use_graph else run1, steps, warmup)
+                run1.free()
+                del run1
+            name = key
+            if rho is not None:
+                name += f"@rho{rho}"
+            if m is not None:
+                name += f"@m{m}"
+            ent = {"ms": round(ms, 4), "effective_tflops": round(dense_flops(layer) / (ms * 1e-3) / 1e12, 2),
+                   "rho1_ms": round(ms1, 4), "speedup_vs_rho1": round(ms1 / ms, 3),
+                   "launch": "hip graph replay" if use_graph else "eager"}
+            if roof:
+                ent["dominant"] = {"kernel": roof["kernel"], "bound": roof["bound"], "frac": roof["frac"]}
+            if mfma is not None:
+                ent["gemm_kept_mfma_frac"] = round(mfma, 4)
+            out[name] = ent
+            del layer
+            torch.cuda.empty_cache()
+        cache.clear()
+        torch.cuda.empty_cache()
+        print(f"[bench] {key}: {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -738,55 +858,26 @@ def main():
         copy_calibration(dev)
 
     run = Runner(R, layer, dev)
-    ms, wall = time_steps(GraphStep(run) if args.graph else run, args.steps, args.warmup)
-    print(f"[bench] rho step {ms:.3f} ms (wall {wall:.3f})", file=sys.stderr, flush=True)
     stepper = GraphStep(run) if args.graph else run
-    hot = step_distribution(stepper, max(args.steps, 20))
+    # Headline: exactly `steps` steps after `warmup`, each with the 256 MB
+    # memory-side cache flushed first (untimed), each bracketed by HIP events
+    # with a device synchronisation after it; the median step.
+    for _ in range(args.warmup):
+        stepper.step()
+    torch.cuda.synchronize()
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    cold = step_distribution(stepper, max(args.steps, 20), flush)
+    cold = step_distribution(stepper, args.steps, flush)
+    ms = cold["median_ms"]
+    print(f"[bench] rho step {ms:.3f} ms (cold-cache median of {args.steps})", file=sys.stderr, flush=True)
+    hot_ms, wall = time_steps(stepper, args.steps, args.warmup)
+    hot = step_distribution(stepper, args.steps)
+    hot["mean_ms"] = round(hot_ms, 4)
     del flush, stepper
     kern = kernel_breakdown(run, max(2, min(args.steps, 5)))
     flops = dense_flops(layer)
-    # Dominant kernel and its roofline.
-    detail = {}
-    best = None
-    for key, v in kern.items():
-        bound, amount, unit = algorithmic_work(run, key)
-        tot = v["avg_ms"] * v["launches_per_step"]
-        ent = {"avg_ms": round(v["avg_ms"], 4), "per_step": v["launches_per_step"]}
-        if bound:
-            rate = amount / (v["avg_ms"] * 1e-3)
-            if unit == "flops":
-                ent["tflops"] = round(rate / 1e12, 1)
-                ent["frac"] = round(rate / 1e12 / PEAK_BF16_TFLOPS, 4)
-            else:
-                ent["gbs"] = round(rate / 1e9, 1)
-                ent["frac"] = round(rate / 1e9 / PEAK_HBM_GBS, 4)
-        detail[key] = ent
-        if bound and (best is None or tot > best[0]):
-            best = (tot, key, bound, amount, unit, v["avg_ms"])
-    roof = None
-    if best:
-        _, key, bound, amount, unit, avg = best
-        if unit == "flops":
-            peak = PEAK_F32_TFLOPS if layer["dtype"] == torch.float32 else PEAK_BF16_TFLOPS
-            ach = amount / (avg * 1e-3) / 1e12
-            roof = {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(ach / peak, 4), "traffic": measured_traffic(wl.key, key), "kernel": key,
-                    "per_launch": f"{amount:.4g} flops", "avg_launch_ms": round(avg, 4)}
-        else:
-            ach = amount / (avg * 1e-3) / 1e9
-            roof = {"bound": bound, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(wl.key, key), "kernel": key,
-                    "per_launch": f"{amount:.4g} bytes", "avg_launch_ms": round(avg, 4)}
-    # Kept-work MFMA fraction over all projection GEMMs.
-    g_fl = g_ms = 0.0
-    for key, v in kern.items():
-        bound, amount, unit = algorithmic_work(run, key)
-        if unit == "flops":
-            g_fl += amount * v["launches_per_step"]
-            g_ms += v["avg_ms"] * v["launches_per_step"]
-    mfma_frac = (g_fl / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS) if g_ms > 0 else None
+    detail, roof, mfma_frac = summarize(run, kern, layer["dtype"])
+    if roof:
+        roof["traffic"] = measured_traffic(wl.key, roof["kernel"])
     # the step's own Q K^T and P V (P an input), for comparison with the fused call
     qkpv_ms = sum(v["avg_ms"] * v["launches_per_step"] for k, v in kern.items() if k.split("/")[0] in ("qk", "pv"))
     proj_ms = sum(v["avg_ms"] * v["launches_per_step"] for k, v in kern.items()
@@ -814,23 +905,34 @@ def main():
     speedup = dense_ms = None
     if not args.no_dense:
         run1 = Runner(R, layer, dev, rho_scale_one=True)
-        dense_ms, _ = time_steps(GraphStep(run1) if args.graph else run1, args.steps, args.warmup)
+        st1 = GraphStep(run1) if args.graph else run1
+        for _ in range(args.warmup):
+            st1.step()
+        torch.cuda.synchronize()
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dense_ms = step_distribution(st1, args.steps, flush)["median_ms"]
         speedup = dense_ms / ms
         print(f"[bench] rho=1 step {dense_ms:.3f} ms", file=sys.stderr, flush=True)
+        del flush, st1
         run1.free()
         del run1
         torch.cuda.empty_cache()
+    del layer
+    torch.cuda.empty_cache()
+
+    others = None
+    if not args.no_other_workloads and args.workload == DEFAULT_WORKLOAD:
+        others = other_workloads(R, dev, args.steps, args.warmup)
 
     cpu = None
     if not args.no_cpu_baseline:
-        del layer
-        torch.cuda.empty_cache()
         cpu = cpu_baseline(wl, {"linears": [l for l in wl.linears if l in _selected(wl, args)],
                                 "attention": wl.attention if _has_attention(wl, args) else None})
 
     value = flops / (ms * 1e-3) / 1e12
     cfg = {"workload": wl.key, "dtype": wl.dtype, "rho": _rho_desc(wl, args),
-           "products": _products_desc(wl, args), "launch": "hip graph replay" if args.graph else "eager"}
+           "products": _products_desc(wl, args), "launch": "hip graph replay" if args.graph else "eager",
+           "timing": "median step, memory-side cache flushed before each step"}
     out = {
         "metric": "effective TFLOP/s (dense-equivalent flops / RMM step time)",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -843,6 +945,7 @@ def main():
         "roofline": roof, "cpu_baseline": cpu, "kernels": detail, "fused_attention": fused,
         "producer_fused": producers, "fused_layer": layer_fused,
         "step_times": {"hot": hot, "cold_cache": cold},
+        "workloads": others,
         "system": system_info(dev),
         "context": {"rmm_projections_ms": round(proj_ms, 4), "torch_matmul_projections_ms": torch_proj_ms},
     }
