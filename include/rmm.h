@@ -148,6 +148,29 @@ rmm_status_t rmm_gemm(rmm_dtype_t dt, const void *A, int64_t lda, const void *B,
                       int64_t ldy, void *ws, size_t ws_bytes, rmm_stream_t stream);
 
 /*
+ * rmm_gemm_noalloc - rmm_gemm with no workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, results and
+ * errors as rmm_gemm (bitwise equal outputs), but the scratch memory (the
+ * packed A[:, I], the cleaned index copy, the transposed kept weight rows or
+ * the few-row kernel's partial sums) lives in a fixed device array inside the
+ * library, RMM_NOALLOC_SCRATCH_BYTES long, one per device, held until the
+ * process ends.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine).
+ *   A product whose rmm_gemm_workspace_bytes(dt, m, n, k) exceeds
+ *   RMM_NOALLOC_SCRATCH_BYTES is rejected with RMM_ERR_UNSUPPORTED before
+ *   anything is enqueued.
+ *   Every call on one device shares that device's array: calls that overlap
+ *   on one GPU (different streams or threads) race on it and must be
+ *   serialised by the caller.  The first call on a device looks up the
+ *   array's device address (a HIP symbol query, no allocation).
+ */
+#define RMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+rmm_status_t rmm_gemm_noalloc(rmm_dtype_t dt, const void *A, int64_t lda, const void *B, int64_t ldb,
+                              const int32_t *idx, int64_t m, int64_t d, int64_t n, int64_t k, void *Y,
+                              int64_t ldy, rmm_stream_t stream);
+
+/*
  * rmm_gemm_w8 - the reduced product with INT8 weights: Y = A[:, I] (Bq[I, :] * scale),
  * scale applied per output column.  Source: "Mecanismo Central" (the reduced
  * product) with the compatibility with INT8 weights stated in the abstract;

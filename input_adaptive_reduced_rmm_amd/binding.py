@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "RMMError", "load", "lib_path",
     "rmm_version", "rmm_k_from_rho", "rmm_k_pad",
-    "rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_gemm_w8", "rmm_swiglu_scored", "rmm_rmsnorm_scored", "rmm_attention_decode_batch", "rmm_qk", "rmm_pv",
+    "rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_gemm_noalloc", "rmm_gemm_w8", "rmm_swiglu_scored", "rmm_rmsnorm_scored", "rmm_attention_decode_batch", "rmm_qk", "rmm_pv",
     "rmm_attention",
     "rmm_colnorm_workspace_bytes", "rmm_topk_workspace_bytes", "rmm_gemm_workspace_bytes",
     "rmm_qk_workspace_bytes", "rmm_pv_workspace_bytes", "rmm_attention_workspace_bytes",
@@ -79,6 +79,8 @@ _PROTOS = {
                                                   _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "rmm_rmsnorm_scored": (ctypes.c_int, [_vp, _i64, _vp, ctypes.c_float, _i64, _i64, _vp, _i64, _vp, _vp, _sz,
                                           _vp]),
+    "rmm_gemm_noalloc": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp,
+                                        _i64, _vp]),
     "rmm_gemm_w8": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _sz,
                                    _vp]),
     "rmm_attention": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _vp,
@@ -219,6 +221,26 @@ def rmm_topk(scores: torch.Tensor, k: int, out: torch.Tensor | None = None):
         out = torch.empty((batch, max(kp, 1)), dtype=torch.int32, device=dev)
     _check(lib.rmm_topk(_ptr(s2), batch, d, int(k), _ptr(out), None, 0, _stream(dev)))
     return out[0] if squeeze else out
+
+
+def rmm_gemm_noalloc(A: torch.Tensor, B: torch.Tensor, idx: torch.Tensor, k: int, out: torch.Tensor):
+    """rmm_gemm with the library's fixed scratch array instead of a workspace:
+    Y = A[:, idx[:k]] @ B[idx[:k], :] written into `out` [m, n]; allocates nothing."""
+    lib = load()
+    dev = _dev(A, B, idx, out)
+    if A.dim() != 2 or B.dim() != 2 or out.dim() != 2 or A.stride(1) != 1 or B.stride(1) != 1 or out.stride(1) != 1:
+        raise ValueError("A [m, d], B [d, n] and out [m, n] must be 2-D with unit column stride")
+    if A.dtype != B.dtype or out.dtype != A.dtype:
+        raise TypeError("A, B and out must share a dtype")
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be contiguous int32")
+    m, d = A.shape
+    d2, n = B.shape
+    if d2 != d or tuple(out.shape) != (m, n):
+        raise ValueError("shapes of A, B and out disagree")
+    _check(lib.rmm_gemm_noalloc(_dt(A), _ptr(A), A.stride(0), _ptr(B), B.stride(0), _ptr(idx), m, d, n, int(k),
+                                _ptr(out), out.stride(0), _stream(dev)))
+    return out
 
 
 def rmm_gemm(A: torch.Tensor, B: torch.Tensor, idx: torch.Tensor, k: int, out: torch.Tensor | None = None,

@@ -83,6 +83,14 @@ size_t colnorm_ws(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch) {
 
 }  // namespace
 
+rmm_status_t rmm::set_error(rmm_status_t s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
 // ------------------------------------------------------------------ misc
 RMM_API int rmm_version(void) { return 100; }
 

@@ -23,6 +23,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)pack_bf16x2(f, 0.f); }
 
+// Record a one-line failure message for rmm_last_error() on this thread and
+// return s.
+rmm_status_t set_error(rmm_status_t s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
