@@ -58,6 +58,8 @@ def parse():
                     help="skip the separate timing of the producer-fused scoring kernels")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the compact timings of the other workloads (default workload only)")
+    ap.add_argument("--cpu-ops", action="store_true",
+                    help="only time the CPU oracle per op on every workload (baseline table) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -709,6 +711,78 @@ def cpu_baseline(wl, layer_meta):
             "sample": "; ".join(parts) + f" (float64 NumPy oracle, {t_total:.1f} s)", "seconds": round(t_total, 2)}
 
 
+def cpu_ops_table(max_single_s=20.0):
+    """The float64 oracle timed per op on this host's cores (median of 3 runs,
+    or one run when a run takes longer than `max_single_s`), for the CPU
+    baseline table: column scores, top-k and the reduced product of every
+    distinct projection shape of the five workloads at their ratios, and per
+    attention head the reduced Q K^T (scores, selection and product), the
+    causal softmax and the reduced P V (scores, selection and product) -
+    attention times are for one head and are multiplied by the head count in
+    `total_s`.  Seeded synthetic inputs as the GPU runs use."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max(i["num_threads"] for i in blas) if blas else os.cpu_count()
+    except Exception:
+        cores = os.cpu_count()
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        out = fn()
+        t = time.perf_counter() - t0
+        if t > max_single_s:
+            return out, t, 1
+        ts = [t]
+        for _ in range(2):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return out, float(np.median(ts)), 3
+
+    rows = []
+    for key in ("xw-fp32-64x512", "llama3.2-1b-proj-2k", "llama3.1-8b-layer-16k", "llama3.1-70b-layer"):
+        wl = synth.WORKLOADS[key]
+        seen = set()
+        for lin in wl.linears:
+            shape = (lin.m, lin.d, lin.n, lin.rho, synth.activation_key(wl, lin))
+            if shape in seen or lin.name.split("@")[0] in ("k", "v", "gate"):
+                continue
+            seen.add(shape)
+            A, B = synth.linear_operands(wl, lin)
+            k = oracle.retained_count(lin.rho, lin.d)
+            sc, t_s, n_s = timed(lambda: oracle.column_scores(A))
+            I, t_k, n_k = timed(lambda: oracle.select_top(sc, k))
+            _, t_g, n_g = timed(lambda: oracle.reduced_product(A, B, I))
+            name = lin.name.split("@")[0]
+            for op, t, n in (("colnorm", t_s, n_s), ("topk", t_k, n_k), ("gemm", t_g, n_g)):
+                rows.append({"workload": key, "product": f"{name} {lin.m}x{lin.d}x{lin.n}", "rho": lin.rho, "op": op,
+                             "seconds": round(t, 4), "runs": n, "total_s": round(t, 4)})
+            del A, B
+            print(f"[cpu-ops] {key} {lin.name} done", file=sys.stderr, flush=True)
+    for key in ("attn-32h-4k", "llama3.1-8b-layer-16k", "llama3.1-70b-layer"):
+        wl = synth.WORKLOADS[key]
+        at = wl.attention
+        Q, Kt, V = synth.attention_operands(wl, Hq=1, Hkv=1)
+        kf = oracle.retained_count(at.rho, at.dh)
+        kt = oracle.retained_count(at.rho, at.L)
+        (S, _, _), t_qk, n_qk = timed(lambda: oracle.reduced_qk(Q, Kt, kf))
+        P, t_sm, n_sm = timed(lambda: oracle.causal_softmax(S, 1.0 / math.sqrt(at.dh)))
+        _, t_pv, n_pv = timed(lambda: oracle.reduced_pv(P, V, kt))
+        for op, t, n in (("qk (1 head)", t_qk, n_qk), ("causal softmax (1 head)", t_sm, n_sm),
+                         ("pv (1 head)", t_pv, n_pv)):
+            rows.append({"workload": key, "product": f"L={at.L} Hq={at.Hq} Hkv={at.Hkv} dh={at.dh}", "rho": at.rho,
+                         "op": op, "seconds": round(t, 4), "runs": n, "total_s": round(t * at.Hq, 3)})
+        del Q, Kt, V, S, P
+        print(f"[cpu-ops] {key} attention done", file=sys.stderr, flush=True)
+    return {"cores": int(cores), "host_cores": os.cpu_count(), "rows": rows}
+
+
 def copy_calibration(dev):
     import torch
 
@@ -835,6 +909,9 @@ def other_workloads(R, dev, steps, warmup):
 
 def main():
     args = parse()
+    if args.cpu_ops:
+        print(json.dumps(cpu_ops_table()), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)

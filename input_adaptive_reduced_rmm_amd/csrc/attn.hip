@@ -181,7 +181,9 @@ __global__ __launch_bounds__(kThreads) void attn_stats_kernel(AttnArgs g) {
     } else {
       __builtin_amdgcn_s_waitcnt(vm_imm(0));
     }
-    __syncthreads();
+    // A bare barrier after the explicit wait: __syncthreads would also wait
+    // for the next tile's loads, which must stay in flight.
+    __builtin_amdgcn_s_barrier();
     const int tk0 = t * kT;
     if (tk0 < wave_keys) {
 #pragma unroll
@@ -220,7 +222,10 @@ __global__ __launch_bounds__(kThreads) void attn_stats_kernel(AttnArgs g) {
         }
       }
     }
-    __syncthreads();   // all waves are done with `cur` before it is refilled
+    // All waves are done reading `cur` before it is refilled (a bare barrier
+    // after the LDS reads drain: the next tile's loads stay in flight).
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
   }
   // merge the two lanes of each query
   const float m_p = __shfl_xor(m_run, 32, 64), l_p = __shfl_xor(l_run, 32, 64);
@@ -283,7 +288,9 @@ __global__ __launch_bounds__(kThreads) void attn_colsq_kernel(AttnArgs g) {
     } else {
       __builtin_amdgcn_s_waitcnt(vm_imm(0));
     }
-    __syncthreads();
+    // A bare barrier after the explicit wait: __syncthreads would also wait
+    // for the next tile's loads, which must stay in flight.
+    __builtin_amdgcn_s_barrier();
     const int qt0 = (int)((t_first + t) * kT);
     if (qt0 + kT > wave_qfirst) {
       const float *sm = reinterpret_cast<const float *>(cur + Tile<KF>::BYTES);   // n2ml
@@ -318,7 +325,8 @@ __global__ __launch_bounds__(kThreads) void attn_colsq_kernel(AttnArgs g) {
         }
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // LDS reads of `cur` drained; the next tile's loads stay in flight
+    __builtin_amdgcn_s_barrier();
   }
   const float c = c_lane + __shfl_xor(c_lane, 32, 64);
   if (lane < 32 && key < g.Lk) g.tok[h * g.Lk + key] = __builtin_sqrtf(c);
@@ -395,7 +403,9 @@ __global__ __launch_bounds__(kThreads) void attn_out_kernel(AttnArgs g) {
     } else {
       __builtin_amdgcn_s_waitcnt(vm_imm(0));
     }
-    __syncthreads();
+    // A bare barrier after the explicit wait: __syncthreads would also wait
+    // for the next tile's loads, which must stay in flight.
+    __builtin_amdgcn_s_barrier();
     const int32_t *jt = reinterpret_cast<const int32_t *>(cur + Tile<KF>::BYTES + VT_BYTES);
     const uint16_t *vt = reinterpret_cast<const uint16_t *>(cur + Tile<KF>::BYTES);
 #pragma unroll
@@ -452,7 +462,8 @@ __global__ __launch_bounds__(kThreads) void attn_out_kernel(AttnArgs g) {
         }
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // LDS reads of `cur` drained; the next tile's loads stay in flight
+    __builtin_amdgcn_s_barrier();
   }
   // acc_o[dt]: lane holds column d = dt*32 + l%32 and queries q0 + 8*(r/4) + 4*(l/32) + r%4
   uint16_t *Oh = g.O + h * g.o_hs;
@@ -558,7 +569,9 @@ __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(2))) 
     } else {
       __builtin_amdgcn_s_waitcnt(vm_imm(0));
     }
-    __syncthreads();
+    // A bare barrier after the explicit wait: __syncthreads would also wait
+    // for the next tile's loads, which must stay in flight.
+    __builtin_amdgcn_s_barrier();
     const int32_t *jt = reinterpret_cast<const int32_t *>(cur + Tile<KF>::BYTES + VT_BYTES);
     const uint16_t *vt = reinterpret_cast<const uint16_t *>(cur + Tile<KF>::BYTES);
 #pragma unroll
@@ -624,7 +637,8 @@ __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(2))) 
         }
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // LDS reads of `cur` drained; the next tile's loads stay in flight
+    __builtin_amdgcn_s_barrier();
   }
   uint16_t *Oh = g.O + h * g.o_hs;
   float cs[4] = {0.f, 0.f, 0.f, 0.f};

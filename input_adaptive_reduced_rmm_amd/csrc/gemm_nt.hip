@@ -261,7 +261,9 @@ __global__ __launch_bounds__(128 * WGN) __attribute__((amdgpu_waves_per_eu(WGN /
       if (had_stores) __builtin_amdgcn_s_waitcnt(vm_imm(kAfter1));
       else __builtin_amdgcn_s_waitcnt(vm_imm(0));
     }
-    __syncthreads();
+    // A bare barrier: every wave's part of K-tile 0 is in LDS.  (__syncthreads
+    // would also make each wave wait for its previous tile's stores.)
+    __builtin_amdgcn_s_barrier();
     frags(0, 0, 0);
 
     // One K-step on K-tile kt (stage kt & 1).  ISSUE: refill this stage with
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(128 * WGN) __attribute__((amdgpu_waves_per_eu(WGN /
         else __builtin_amdgcn_s_waitcnt(vm_imm(0));
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this tile's fragment reads are done
-      __syncthreads();
+      __builtin_amdgcn_s_barrier();
       if constexpr (ISSUE) {
         issue(cur, kt + NST, kt & 1);
         __builtin_amdgcn_sched_barrier(0);

@@ -78,13 +78,11 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const T *__restrict__ A,
   const int32_t *ib = idx + b * idx_bs;
   int32_t col[N];
 #pragma unroll
+  for (int e = 0; e < N; ++e) col[e] = ib[t0 + e < k ? t0 + e : k - 1];   // all loads first
+#pragma unroll
   for (int e = 0; e < N; ++e) {
-    int32_t c = -1;
-    if (t0 + e < k) {
-      const int32_t v = ib[t0 + e];
-      c = (v >= 0 && v < d) ? v : -1;
-    }
-    col[e] = c;
+    const int32_t v = col[e];
+    col[e] = (t0 + e < k && v >= 0 && v < d) ? v : -1;
   }
   if (idx_clean && blockIdx.y == 0 && sub == 0) {
 #pragma unroll
@@ -130,38 +128,50 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const T *__restrict__ A,
   }
 }
 
-// One block walks `rows_per_block` rows: the whole source row into LDS
-// (each wave moves 1 KiB per load instruction), then every thread writes up
-// to MAXC 16-byte chunks of the packed row (8 kept columns each, gathered
-// from LDS; padding slots are zero).  Several blocks per CU overlap one
-// block's loads with another's gathers.
+// One block walks `rows_per_block` rows through two LDS row buffers: while
+// the kept columns of row r are gathered from one buffer and written, the
+// whole of row r + 1 streams into the other (16-byte direct-to-LDS loads, one
+// 1 KiB piece per wave instruction).  Every thread writes MAXC 16-byte chunks
+// of each packed row (8 kept columns each; padding slots are zero) with
+// buffer stores; chunks past the row go to an offset outside the row's
+// resource and are dropped, so every wave issues exactly MAXC stores per row
+// and the wait for row r + 1's loads can leave the MAXC stores of row r in
+// flight (vmcnt counts loads and stores together, in issue order).
 __device__ __forceinline__ void lds_row_load16(mg::rsrc_t r, void *lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void *)lds, 16, voff, 0, 0, 0);
 }
+
+// Immediate of s_waitcnt vmcnt(n) with lgkmcnt and expcnt left alone.
+constexpr int vm_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
 
 template <int MAXC>
 __global__ __launch_bounds__(kThreads) void pack_rows_kernel(const uint16_t *__restrict__ A, int64_t lda,
                                                              const int32_t *__restrict__ idx, int64_t m,
                                                              int64_t d, int64_t k, int64_t k_pad,
-                                                             int64_t rows_per_block, uint16_t *__restrict__ out,
+                                                             int64_t rows_per_block, int64_t row_bytes,
+                                                             uint16_t *__restrict__ out,
                                                              int32_t *__restrict__ idx_clean) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char row_lds[];
-  const uint16_t *row16 = reinterpret_cast<const uint16_t *>(row_lds);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nchunk = k_pad / 8;
+  // Kept columns of this thread's chunks.  Every load is issued before any
+  // is used (slots past k read entry k - 1 and are then dropped), so the
+  // block pays one memory latency here rather than one per index.
   int32_t col[MAXC][8];
+#pragma unroll
+  for (int u = 0; u < MAXC; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t t = (tid + (int64_t)kThreads * u) * 8 + e;
+      col[u][e] = idx[t < k ? t : k - 1];
+    }
 #pragma unroll
   for (int u = 0; u < MAXC; ++u) {
     const int64_t c = tid + (int64_t)kThreads * u;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int64_t t = c * 8 + e;
-      int32_t v = -1;
-      if (c < nchunk && t < k) {
-        const int32_t x = idx[t];
-        v = (x >= 0 && x < d) ? x : -1;
-      }
-      col[u][e] = v;
+      const int32_t x = col[u][e];
+      col[u][e] = (c * 8 + e < k && x >= 0 && x < d) ? x : -1;
     }
     if (idx_clean && blockIdx.x == 0 && c < nchunk) {
 #pragma unroll
@@ -172,23 +182,40 @@ __global__ __launch_bounds__(kThreads) void pack_rows_kernel(const uint16_t *__r
   const int nblk1k = (int)((d * 2 + 1023) / 1024);   // 1 KiB pieces of a row
   const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
   const int64_t r1 = r0 + rows_per_block < m ? r0 + rows_per_block : m;
-  for (int64_t r = r0; r < r1; ++r) {
+  auto issue_row = [&](int64_t r, unsigned char *buf) {
     for (int q = wave; q < nblk1k; q += kThreads / 64)
-      lds_row_load16(ra, row_lds + q * 1024, (uint32_t)(r * lda * 2 + q * 1024 + lane * 16));
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    __syncthreads();
-    uint16_t *orow = out + r * k_pad;
+      lds_row_load16(ra, buf + q * 1024, (uint32_t)(r * lda * 2 + q * 1024 + lane * 16));
+  };
+  if (r0 < r1) issue_row(r0, row_lds);
+  for (int64_t r = r0; r < r1; ++r) {
+    const unsigned char *cur = row_lds + ((r - r0) & 1) * row_bytes;
+    // Row r landed: after its loads this wave issued only the MAXC stores of
+    // row r - 1.
+    if (r == r0) __builtin_amdgcn_s_waitcnt(vm_imm(0));
+    else __builtin_amdgcn_s_waitcnt(vm_imm(MAXC));
+    // Every wave's pieces of row r are in, and row r - 1's buffer is no
+    // longer read (its LDS reads were consumed before its stores were
+    // issued).  A bare barrier: __syncthreads would also wait for this
+    // wave's stores of row r - 1.
+    __builtin_amdgcn_s_barrier();
+    if (r + 1 < r1) issue_row(r + 1, row_lds + ((r + 1 - r0) & 1) * row_bytes);
+    __builtin_amdgcn_sched_barrier(0);   // the stores below stay after these loads
+    const uint16_t *row16 = reinterpret_cast<const uint16_t *>(cur);
+    const mg::rsrc_t ro = mg::make_rsrc(out + r * k_pad, (uint64_t)k_pad * 2);
 #pragma unroll
     for (int u = 0; u < MAXC; ++u) {
       const int64_t c = tid + (int64_t)kThreads * u;
-      if (c < nchunk) {
-        uint16_t v[8];
+      uint16_t v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = col[u][e] >= 0 ? row16[col[u][e]] : (uint16_t)0;
-        store16(orow + c * 8, v);
-      }
+      for (int e = 0; e < 8; ++e) v[e] = row16[col[u][e] >= 0 ? col[u][e] : 0];   // dropped slots read column 0
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (col[u][e] < 0) v[e] = 0;
+      typedef int v4i __attribute__((ext_vector_type(4)));
+      const v4i w = {(int)((uint32_t)v[0] | ((uint32_t)v[1] << 16)), (int)((uint32_t)v[2] | ((uint32_t)v[3] << 16)),
+                     (int)((uint32_t)v[4] | ((uint32_t)v[5] << 16)), (int)((uint32_t)v[6] | ((uint32_t)v[7] << 16))};
+      __builtin_amdgcn_raw_buffer_store_b128(w, ro, c < nchunk ? (int)(c * 16) : (int)mg::kOOB, 0, 0);
     }
-    __syncthreads();   // the row buffer is refilled next
   }
 }
 
@@ -203,14 +230,14 @@ hipError_t launch_pack(rmm_dtype_t dt, const void *A, int64_t lda, int64_t a_bs,
       reinterpret_cast<uintptr_t>(A) % 16 == 0 && lda % 8 == 0 && (uint64_t)((m - 1) * lda + d) * 2 < mg::kMaxRecords) {
     const int64_t nchunk = k_pad / 8;
     const int64_t per_thread = ceil_div(nchunk, (int64_t)kThreads);
-    // about 2048 blocks of at least one row
-    int64_t rpb = ceil_div(m, 2048);
+    // about 1024 blocks of at least one row, each with two row buffers
+    int64_t rpb = ceil_div(m, 1024);
     const int64_t blocks = ceil_div(m, rpb);
     KernelTimer timer("pack", st);
-#define RMM_PACK_ROWS(C)                                                                                     \
-  hipLaunchKernelGGL(pack_rows_kernel<C>, dim3((unsigned)blocks), dim3(kThreads), (unsigned)row_bytes, st,     \
-                     static_cast<const uint16_t *>(A), lda, idx, m, d, k, k_pad, rpb, static_cast<uint16_t *>(out), \
-                     idx_clean)
+#define RMM_PACK_ROWS(C)                                                                                      \
+  hipLaunchKernelGGL(pack_rows_kernel<C>, dim3((unsigned)blocks), dim3(kThreads), (unsigned)(2 * row_bytes), st, \
+                     static_cast<const uint16_t *>(A), lda, idx, m, d, k, k_pad, rpb, row_bytes,                  \
+                     static_cast<uint16_t *>(out), idx_clean)
     if (per_thread <= 1) RMM_PACK_ROWS(1);
     else if (per_thread <= 2) RMM_PACK_ROWS(2);
     else if (per_thread <= 4) RMM_PACK_ROWS(4);
