@@ -148,6 +148,25 @@ rmm_status_t rmm_gemm(rmm_dtype_t dt, const void *A, int64_t lda, const void *B,
                       int64_t ldy, void *ws, size_t ws_bytes, rmm_stream_t stream);
 
 /*
+ * rmm_gemm_scored - rmm_gemm that also returns the column scores of its
+ * output: y_scores[c] = ||Y[:, c]||_2 over the m rows of the values written
+ * (bf16-rounded for RMM_BF16), float32 accumulation in a fixed order.
+ * Source: "Estrategia de Selección" (a product's contraction index is scored
+ * by the column norm of its activation; when Y is the activation of a later
+ * reduced product, its producer scores it, so rmm_topk can follow without an
+ * rmm_colnorm pass over Y).  For the many-row bf16 products the squares are
+ * summed in the GEMM's epilogue from registers (one partial per 128-row slab,
+ * then a fixed-order finish); other shapes score Y in a second pass.
+ *   Arguments and results as rmm_gemm (Y bitwise equal to rmm_gemm's), plus
+ *   y_scores (device, float) [n], not NULL.
+ *   ws: at least rmm_gemm_scored_workspace_bytes(dt, m, n, k) bytes, 256-byte aligned.
+ */
+size_t rmm_gemm_scored_workspace_bytes(rmm_dtype_t dt, int64_t m, int64_t n, int64_t k);
+rmm_status_t rmm_gemm_scored(rmm_dtype_t dt, const void *A, int64_t lda, const void *B, int64_t ldb,
+                             const int32_t *idx, int64_t m, int64_t d, int64_t n, int64_t k, void *Y,
+                             int64_t ldy, float *y_scores, void *ws, size_t ws_bytes, rmm_stream_t stream);
+
+/*
  * rmm_gemm_noalloc - rmm_gemm with no workspace argument, for callers that
  * cannot allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  Same arguments, results and

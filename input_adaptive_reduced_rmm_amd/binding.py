@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "RMMError", "load", "lib_path",
     "rmm_version", "rmm_k_from_rho", "rmm_k_pad",
-    "rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_gemm_noalloc", "rmm_gemm_w8", "rmm_swiglu_scored", "rmm_rmsnorm_scored", "rmm_attention_decode_batch", "rmm_qk", "rmm_pv",
+    "rmm_colnorm", "rmm_topk", "rmm_gemm", "rmm_gemm_scored", "rmm_gemm_noalloc", "rmm_gemm_w8", "rmm_swiglu_scored", "rmm_rmsnorm_scored", "rmm_attention_decode_batch", "rmm_qk", "rmm_pv",
     "rmm_attention",
     "rmm_colnorm_workspace_bytes", "rmm_topk_workspace_bytes", "rmm_gemm_workspace_bytes",
     "rmm_qk_workspace_bytes", "rmm_pv_workspace_bytes", "rmm_attention_workspace_bytes",
@@ -79,6 +79,9 @@ _PROTOS = {
                                                   _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "rmm_rmsnorm_scored": (ctypes.c_int, [_vp, _i64, _vp, ctypes.c_float, _i64, _i64, _vp, _i64, _vp, _vp, _sz,
                                           _vp]),
+    "rmm_gemm_scored_workspace_bytes": (_sz, [ctypes.c_int, _i64, _i64, _i64]),
+    "rmm_gemm_scored": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _i64,
+                                       _vp, _vp, _sz, _vp]),
     "rmm_gemm_noalloc": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp,
                                         _i64, _vp]),
     "rmm_gemm_w8": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _sz,
@@ -221,6 +224,32 @@ def rmm_topk(scores: torch.Tensor, k: int, out: torch.Tensor | None = None):
         out = torch.empty((batch, max(kp, 1)), dtype=torch.int32, device=dev)
     _check(lib.rmm_topk(_ptr(s2), batch, d, int(k), _ptr(out), None, 0, _stream(dev)))
     return out[0] if squeeze else out
+
+
+def rmm_gemm_scored(A: torch.Tensor, B: torch.Tensor, idx: torch.Tensor, k: int, out: torch.Tensor | None = None,
+                    scores: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """Y = A[:, idx[:k]] @ B[idx[:k], :] and the column scores of Y -> (Y [m, n], scores float32 [n])."""
+    lib = load()
+    dev = _dev(A, B, idx)
+    if A.dim() != 2 or B.dim() != 2 or A.stride(1) != 1 or B.stride(1) != 1:
+        raise ValueError("A [m, d] and B [d, n] must be 2-D with unit column stride")
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must share a dtype")
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("idx must be contiguous int32")
+    m, d = A.shape
+    d2, n = B.shape
+    if d2 != d:
+        raise ValueError("inner dimensions differ")
+    if out is None:
+        out = torch.empty((m, n), dtype=A.dtype, device=dev)
+    if scores is None:
+        scores = torch.empty(n, dtype=torch.float32, device=dev)
+    dt = _dt(A)
+    ws, wsb = _ws(int(lib.rmm_gemm_scored_workspace_bytes(dt, m, n, int(k))), dev, ws)
+    _check(lib.rmm_gemm_scored(dt, _ptr(A), A.stride(0), _ptr(B), B.stride(0), _ptr(idx), m, d, n, int(k),
+                               _ptr(out), out.stride(0), _scores_ptr(scores, (n,), dev), _ptr(ws), wsb, _stream(dev)))
+    return out, scores
 
 
 def rmm_gemm_noalloc(A: torch.Tensor, B: torch.Tensor, idx: torch.Tensor, k: int, out: torch.Tensor):

@@ -259,56 +259,95 @@ RMM_API size_t rmm_gemm_workspace_bytes(rmm_dtype_t dt, int64_t m, int64_t n, in
   return b;
 }
 
+// The reduced product, and optionally the column scores of its output Y
+// (y_scores != NULL; the extra workspace starts at offset `base`).
+rmm_status_t rmm::gemm_args_check(const char *name, rmm_dtype_t dt, const void *A, int64_t lda, const void *B,
+                                   int64_t ldb, const int32_t *idx, int64_t m, int64_t d, int64_t n, int64_t k,
+                                   const void *Y, int64_t ldy, const float *y_scores) {
+  if (!dtype_ok(dt)) return fail(RMM_ERR_INVALID_ARG, "%s: unknown dtype", name);
+  if (!A || !B || !idx || !Y) return fail(RMM_ERR_INVALID_ARG, "%s: NULL pointer", name);
+  if (m < 1 || n < 1 || d < 1 || d >= kMaxDim || n >= kMaxDim)
+    return fail(RMM_ERR_INVALID_ARG, "%s: bad m, n or d", name);
+  if (k < 1 || k > d) return fail(RMM_ERR_INVALID_ARG, "%s: need 1 <= k <= d", name);
+  if (lda < d || ldb < n || ldy < n) return fail(RMM_ERR_INVALID_ARG, "%s: leading dimension too small", name);
+  const size_t e = esize(dt);
+  if (!aligned(A, e) || !aligned(B, e) || !aligned(Y, e) || !aligned(idx, 4) || (y_scores && !aligned(y_scores, 4)))
+    return fail(RMM_ERR_INVALID_ARG, "%s: misaligned pointer", name);
+  return RMM_OK;
+}
+
+static rmm_status_t gemm_impl(rmm_dtype_t dt, const void *A, int64_t lda, const void *B, int64_t ldb,
+                              const int32_t *idx, int64_t m, int64_t d, int64_t n, int64_t k, void *Y,
+                              int64_t ldy, float *y_scores, void *ws, size_t ws_bytes, hipStream_t st) {
+  const char *name = y_scores ? "gemm_scored" : "gemm";
+  const rmm_status_t chk = rmm::gemm_args_check(name, dt, A, lda, B, ldb, idx, m, d, n, k, Y, ldy, y_scores);
+  if (chk != RMM_OK) return chk;
+  const size_t e = esize(dt);
+  const size_t base = rmm_gemm_workspace_bytes(dt, m, n, k);
+  const size_t need = y_scores ? rmm_gemm_scored_workspace_bytes(dt, m, n, k) : base;
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(RMM_ERR_WORKSPACE, "%s: workspace needs %zu bytes (256-byte aligned)", name, need);
+  const int64_t k_pad = rmm_k_pad(k);
+  char *w = static_cast<char *>(ws);
+  int32_t *idx_clean = reinterpret_cast<int32_t *>(w + align256((size_t)m * k_pad * e));
+  hipError_t he = rmm::launch_pack(dt, A, lda, 0, idx, 0, 1, m, d, k, k_pad, ws, idx_clean, st);
+  if (he != hipSuccess) return hip_status(he, "gemm pack launch");
+  if (gemm_uses_nt(dt, m, n) && rmm::gemm_nt_ok(m, n, d, ldb, k_pad)) {
+    void *bt = w + align256((size_t)m * k_pad * e) + align256((size_t)k_pad * 4);
+    return hip_status(rmm::launch_gemm_nt(ws, idx_clean, B, ldb, d, bt, Y, ldy, m, n, k_pad, st, y_scores,
+                                          reinterpret_cast<float *>(w + base)),
+                      "gemm launch");
+  }
+  if (dt == RMM_BF16 && rmm::skinny_ok(m, B, ldb, false, d, n)) {
+    float *part = reinterpret_cast<float *>(w + align256((size_t)m * k_pad * e) + align256((size_t)k_pad * 4));
+    he = rmm::launch_gemm_skinny(ws, idx_clean, B, false, nullptr, ldb, d, m, n, k_pad, Y, ldy, part, st);
+  } else {
+    rmm::GemmArgs g{};
+    g.A = ws;
+    g.idx = idx_clean;
+    g.idx_stride = k_pad;
+    g.B = B;
+    g.ldb = ldb;
+    g.b_batch_stride = 0;
+    g.Y = Y;
+    g.ldy = ldy;
+    g.y_batch_stride = 0;
+    g.batch = 1;
+    g.hq = 1;
+    g.hkv = 1;
+    g.m = m;
+    g.n = n;
+    g.d = d;
+    g.k = k;
+    g.k_pad = k_pad;
+    he = dt == RMM_BF16 ? rmm::launch_gemm_bf16(g, rmm::OutType::BF16, st) : rmm::launch_gemm_f32(g, st);
+  }
+  if (he != hipSuccess || !y_scores) return hip_status(he, "gemm launch");
+  // Other kernels: the column scores of the written Y in a separate pass.
+  const rmm::ColnormPlan p = plan_for(dt, Y, m, n, ldy, 1, 0);
+  return hip_status(rmm::launch_colnorm(dt, Y, m, n, ldy, 1, 0, y_scores, w + base, p, st),
+                    "gemm scores launch");
+}
+
 RMM_API rmm_status_t rmm_gemm(rmm_dtype_t dt, const void *A, int64_t lda, const void *B,
                               int64_t ldb, const int32_t *idx, int64_t m, int64_t d, int64_t n,
                               int64_t k, void *Y, int64_t ldy, void *ws, size_t ws_bytes,
                               rmm_stream_t stream) {
-  if (!dtype_ok(dt)) return fail(RMM_ERR_INVALID_ARG, "gemm: unknown dtype");
-  if (!A || !B || !idx || !Y) return fail(RMM_ERR_INVALID_ARG, "gemm: NULL pointer");
-  if (m < 1 || n < 1 || d < 1 || d >= kMaxDim) return fail(RMM_ERR_INVALID_ARG, "gemm: bad m, n or d");
-  if (k < 1 || k > d) return fail(RMM_ERR_INVALID_ARG, "gemm: need 1 <= k <= d");
-  if (lda < d || ldb < n || ldy < n) return fail(RMM_ERR_INVALID_ARG, "gemm: leading dimension too small");
-  const size_t e = esize(dt);
-  if (!aligned(A, e) || !aligned(B, e) || !aligned(Y, e) || !aligned(idx, 4))
-    return fail(RMM_ERR_INVALID_ARG, "gemm: misaligned pointer");
-  const size_t need = rmm_gemm_workspace_bytes(dt, m, n, k);
-  if (!ws || ws_bytes < need || !aligned(ws, 256)) return fail(RMM_ERR_WORKSPACE, "gemm: workspace needs %zu bytes (256-byte aligned)", need);
-  const int64_t k_pad = rmm_k_pad(k);
-  hipStream_t st = (hipStream_t)stream;
-  int32_t *idx_clean = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + align256((size_t)m * k_pad * e));
-  hipError_t he = rmm::launch_pack(dt, A, lda, 0, idx, 0, 1, m, d, k, k_pad, ws, idx_clean, st);
-  if (he != hipSuccess) return hip_status(he, "gemm pack launch");
-  if (gemm_uses_nt(dt, m, n) && rmm::gemm_nt_ok(m, n, d, ldb, k_pad)) {
-    void *bt = static_cast<char *>(ws) + align256((size_t)m * k_pad * e) + align256((size_t)k_pad * 4);
-    return hip_status(rmm::launch_gemm_nt(ws, idx_clean, B, ldb, d, bt, Y, ldy, m, n, k_pad, st),
-                      "gemm launch");
-  }
-  if (dt == RMM_BF16 && rmm::skinny_ok(m, B, ldb, false, d, n)) {
-    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + align256((size_t)m * k_pad * e) +
-                                            align256((size_t)k_pad * 4));
-    return hip_status(rmm::launch_gemm_skinny(ws, idx_clean, B, false, nullptr, ldb, d, m, n, k_pad, Y, ldy, part, st),
-                      "gemm launch");
-  }
-  rmm::GemmArgs g{};
-  g.A = ws;
-  g.idx = idx_clean;
-  g.idx_stride = k_pad;
-  g.B = B;
-  g.ldb = ldb;
-  g.b_batch_stride = 0;
-  g.Y = Y;
-  g.ldy = ldy;
-  g.y_batch_stride = 0;
-  g.batch = 1;
-  g.hq = 1;
-  g.hkv = 1;
-  g.m = m;
-  g.n = n;
-  g.d = d;
-  g.k = k;
-  g.k_pad = k_pad;
-  he = dt == RMM_BF16 ? rmm::launch_gemm_bf16(g, rmm::OutType::BF16, st) : rmm::launch_gemm_f32(g, st);
-  return hip_status(he, "gemm launch");
+  return gemm_impl(dt, A, lda, B, ldb, idx, m, d, n, k, Y, ldy, nullptr, ws, ws_bytes, (hipStream_t)stream);
+}
+
+RMM_API size_t rmm_gemm_scored_workspace_bytes(rmm_dtype_t dt, int64_t m, int64_t n, int64_t k) {
+  const size_t base = rmm_gemm_workspace_bytes(dt, m, n, k);
+  if (!base) return 0;
+  const size_t extra = gemm_uses_nt(dt, m, n) ? rmm::gemm_nt_ypart_bytes(m, n) : colnorm_ws(dt, m, n, 1);
+  return base + (extra > 0 ? extra : 256);
+}
+
+RMM_API rmm_status_t rmm_gemm_scored(rmm_dtype_t dt, const void *A, int64_t lda, const void *B, int64_t ldb,
+                                     const int32_t *idx, int64_t m, int64_t d, int64_t n, int64_t k, void *Y,
+                                     int64_t ldy, float *y_scores, void *ws, size_t ws_bytes, rmm_stream_t stream) {
+  if (!y_scores) return fail(RMM_ERR_INVALID_ARG, "gemm_scored: y_scores is NULL");
+  return gemm_impl(dt, A, lda, B, ldb, idx, m, d, n, k, Y, ldy, y_scores, ws, ws_bytes, (hipStream_t)stream);
 }
 
 // ------------------------------------------------------------------ int8 weights

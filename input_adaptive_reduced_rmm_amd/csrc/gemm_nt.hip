@@ -98,6 +98,7 @@ struct NtArgs {
   const uint16_t *BT;  // [n][k_pad]
   uint16_t *Y;
   int64_t ldy, m, n, k_pad, tiles_m, tiles_n;
+  float *ypart;        // optional [2 tiles_m][n]: column sums of squares of the bf16 Y per 128-row slab
 };
 
 // LDS operand tiles are [256 rows][64] bf16: 8 16-byte chunks per row, the
@@ -135,7 +136,8 @@ constexpr int vm_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14);
 // WGN: waves across the tile's columns (2: four waves of 128 x 128, one per
 // SIMD; 4: eight waves of 128 x 64, two per SIMD, so that one wave's MFMAs
 // run while the other waits on LDS or on the barrier: about 10 % faster).
-template <int WGN>
+// SCORED: also write the per-slab column sums of squares of Y (g.ypart).
+template <int WGN, bool SCORED>
 __global__ __launch_bounds__(128 * WGN) __attribute__((amdgpu_waves_per_eu(WGN / 2))) void gemm_nt_persistent(
     NtArgs g) {
   constexpr int BM = 256, BN = 256, BK = 64, NST = 2;
@@ -309,6 +311,43 @@ __global__ __launch_bounds__(128 * WGN) __attribute__((amdgpu_waves_per_eu(WGN /
       prologue(cur);
     }
 
+    // Producer-fused column scores of Y (optional): the squares of the bf16
+    // values this wave stores, summed over its 128 rows (its four rows per
+    // lane, then the 32 lanes of each half in a fixed butterfly), one partial
+    // per (128-row slab, column); colnorm_finish adds the slabs in order.
+    // Rows past m were multiplied from zero rows of A and add nothing.
+    if constexpr (SCORED) {
+      float cs[TJ][16];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float t = 0.f;
+#pragma unroll
+          for (int i = 0; i < TI; ++i) {
+            const float v = __uint_as_float((uint32_t)f32_to_bf16(acc[j][i][r]) << 16);
+            t = fmaf(v, v, t);
+          }
+          cs[j][r] = t;
+        }
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) cs[j][r] += __shfl_xor(cs[j][r], off, 64);
+      if ((lane & 31) == 0) {
+        float *pr = g.ypart + (dm0 / 128 + wm) * g.n;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t col = dn0 + wn * WTN + j * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
+            if (col < g.n) pr[col] = cs[j][r];
+          }
+      }
+    }
+
     // Epilogue from registers: lane l of acc[j][i] holds four consecutive
     // columns j*32 + 8*(r/4) + 4*(l/32) of row i*32 + l%32.  Full tiles use
     // buffer stores: one lane offset, the column step in the immediate and
@@ -401,7 +440,7 @@ hipError_t launch_bt_pack(const void *B, int64_t ldb, int64_t d, int64_t n, cons
 
 hipError_t launch_gemm_nt(const void *A_packed, const int32_t *idx_clean, const void *B, int64_t ldb,
                           int64_t d, void *BT_ws, void *Y, int64_t ldy, int64_t m, int64_t n,
-                          int64_t k_pad, hipStream_t st) {
+                          int64_t k_pad, hipStream_t st, float *y_scores, float *ypart) {
   {
     KernelTimer timer("bt_pack", st);
     hipError_t e = launch_bt_pack(B, ldb, d, n, idx_clean, k_pad, BT_ws, 1, 1, 1, 0, 0, 0, st);
@@ -417,13 +456,21 @@ hipError_t launch_gemm_nt(const void *A_packed, const int32_t *idx_clean, const 
   g.k_pad = k_pad;
   g.tiles_m = ceil_div(m, 256);
   g.tiles_n = ceil_div(n, 256);
-  KernelTimer timer("gemm_nt", st);
+  g.ypart = y_scores ? ypart : nullptr;
   {
+    KernelTimer timer("gemm_nt", st);
     const int64_t tiles = g.tiles_m * g.tiles_n;
     const int64_t grid = tiles < 256 ? tiles : 256;
-    hipLaunchKernelGGL(gemm_nt_persistent<kWGN>, dim3((unsigned)grid), dim3(128 * kWGN), 0, st, g);
+    if (g.ypart)
+      hipLaunchKernelGGL((gemm_nt_persistent<kWGN, true>), dim3((unsigned)grid), dim3(128 * kWGN), 0, st, g);
+    else
+      hipLaunchKernelGGL((gemm_nt_persistent<kWGN, false>), dim3((unsigned)grid), dim3(128 * kWGN), 0, st, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !y_scores) return e;
   }
-  return hipGetLastError();
+  return launch_colnorm_finish(ypart, 2 * g.tiles_m, n, y_scores, st);
 }
+
+size_t gemm_nt_ypart_bytes(int64_t m, int64_t n) { return align_up((size_t)2 * ceil_div(m, 256) * n * 4, 256); }
 
 }  // namespace rmm

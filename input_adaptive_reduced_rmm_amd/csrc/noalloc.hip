@@ -53,10 +53,10 @@ hipError_t scratch_ptr(void **out) {
 RMM_API rmm_status_t rmm_gemm_noalloc(rmm_dtype_t dt, const void *A, int64_t lda, const void *B, int64_t ldb,
                                       const int32_t *idx, int64_t m, int64_t d, int64_t n, int64_t k, void *Y,
                                       int64_t ldy, rmm_stream_t stream) {
-  // Shape errors are reported by rmm_gemm itself (before anything is
-  // enqueued); here only the scratch size is checked.
-  const size_t need = (m >= 1 && n >= 1 && k >= 1 && (dt == RMM_BF16 || dt == RMM_F32))
-                          ? rmm_gemm_workspace_bytes(dt, m, n, k) : 0;
+  // Argument errors first, as rmm_gemm reports them; then the scratch size.
+  const rmm_status_t chk = rmm::gemm_args_check("gemm_noalloc", dt, A, lda, B, ldb, idx, m, d, n, k, Y, ldy, nullptr);
+  if (chk != RMM_OK) return chk;
+  const size_t need = rmm_gemm_workspace_bytes(dt, m, n, k);
   if (need > kScratchBytes)
     return rmm::set_error(RMM_ERR_UNSUPPORTED,
                           "gemm_noalloc: this product needs %zu bytes of scratch; the fixed array holds %zu "

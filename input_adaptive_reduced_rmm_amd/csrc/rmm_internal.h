@@ -27,6 +27,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)pack
 // return s.
 rmm_status_t set_error(rmm_status_t s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 
+// Host-side argument checks of the reduced product (everything but the
+// workspace); records the failure and returns its status, else RMM_OK.
+rmm_status_t gemm_args_check(const char *name, rmm_dtype_t dt, const void *A, int64_t lda, const void *B,
+                             int64_t ldb, const int32_t *idx, int64_t m, int64_t d, int64_t n, int64_t k,
+                             const void *Y, int64_t ldy, const float *y_scores);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -120,9 +126,12 @@ hipError_t launch_bt_pack(const void *B, int64_t ldb, int64_t d, int64_t n, cons
                           int64_t k_pad, void *BT, int64_t batch, int64_t hq, int64_t hkv, int64_t b_gs,
                           int64_t idx_bs, int64_t bt_bs, hipStream_t stream);
 bool gemm_nt_ok(int64_t m, int64_t n, int64_t d, int64_t ldb, int64_t k_pad);
+// y_scores (optional) [n]: column scores of the bf16 Y, formed in the epilogue
+// from per-slab partials in ypart (gemm_nt_ypart_bytes) and finished in order.
 hipError_t launch_gemm_nt(const void *A_packed, const int32_t *idx_clean, const void *B, int64_t ldb,
                           int64_t d, void *BT_ws, void *Y, int64_t ldy, int64_t m, int64_t n,
-                          int64_t k_pad, hipStream_t stream);
+                          int64_t k_pad, hipStream_t stream, float *y_scores = nullptr, float *ypart = nullptr);
+size_t gemm_nt_ypart_bytes(int64_t m, int64_t n);
 
 // ------------------------------------------------------------------ feature-reduced Q K^T
 bool qk_layout_ok(int64_t Lq, int64_t dh, int64_t ldkt, int64_t Lk, int64_t k_pad);

@@ -46,6 +46,11 @@ int main(int argc, char **argv) {
   EXPECT(rmm_gemm(RMM_BF16, F, 64, F, 32, Fi, 16, 64, 32, 65, F, 32, F, 1 << 30, NULL), INV);
   EXPECT(rmm_gemm(RMM_BF16, F, 64, F, 32, Fi, 16, 64, 32, 8, F, 32, F,
                   rmm_gemm_workspace_bytes(RMM_BF16, 16, 32, 8) - 1, NULL), WSE);
+  EXPECT(rmm_gemm_scored(RMM_BF16, F, 64, F, 32, Fi, 16, 64, 32, 8, F, 32, NULL, F, 1 << 30, NULL), INV);
+  EXPECT(rmm_gemm_scored(RMM_BF16, F, 64, F, 32, Fi, 16, 64, 32, 8, F, 32, Ff, F,
+                         rmm_gemm_scored_workspace_bytes(RMM_BF16, 16, 32, 8) - 1, NULL), WSE);
+  EXPECT(rmm_gemm_noalloc(RMM_BF16, F, 4096, F, 28672, Fi, 16384, 4096, 28672, 3277, F, 28672, NULL), UNS);
+  EXPECT(rmm_gemm_noalloc(RMM_BF16, F, 64, F, 32, Fi, 16, 64, 32, 65, F, 32, NULL), INV);
   EXPECT(rmm_gemm_w8(F, 64, F, 40, Ff, Fi, 16, 64, 32, 8, F, 32, F, 1 << 30, NULL), UNS);
   EXPECT(rmm_gemm_w8(F, 64, F, 32, NULL, Fi, 16, 64, 32, 8, F, 32, F, 1 << 30, NULL), INV);
   EXPECT(rmm_swiglu_scored(F, 64, F, 64, 100, 60, F, 64, Ff, F, 1 << 30, NULL), UNS);
@@ -78,6 +83,7 @@ int main(int argc, char **argv) {
       for (int64_t b = 1; b <= 64; b *= 8) {
         acc += rmm_colnorm_workspace_bytes(RMM_BF16, m, d, b) + rmm_colnorm_workspace_bytes(RMM_F32, m, d, b);
         acc += rmm_gemm_workspace_bytes(RMM_BF16, m, d, d) + rmm_gemm_w8_workspace_bytes(m, d, d);
+        acc += rmm_gemm_scored_workspace_bytes(RMM_BF16, m, d, d) + rmm_gemm_scored_workspace_bytes(RMM_F32, m, d, d);
         acc += rmm_qk_workspace_bytes(m, b, 128, 64) + rmm_pv_workspace_bytes(b, m, d, d);
         acc += rmm_attention_workspace_bytes(m, m, b, 128, 64, m) + rmm_swiglu_scored_workspace_bytes(m, d);
         acc += rmm_attention_decode_batch_workspace_bytes(b, 8, 128, d, d) + rmm_rmsnorm_scored_workspace_bytes(m, 512);

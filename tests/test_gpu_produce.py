@@ -15,7 +15,7 @@ import torch
 import oracle
 import synth
 from input_adaptive_reduced_rmm_amd import binding as R
-from _parity import check_selection, dev_tensor
+from _parity import TOL_BF16, TOL_F32, check_selection, dev_tensor, rel_fro
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -155,3 +155,32 @@ def test_rmsnorm_scored_rejects():
         R.rmm_rmsnorm_scored(X, torch.ones(512, dtype=BF, device=DEV), eps=-1.0)
     assert e.value.status == R.RMM_ERR_INVALID_ARG
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ scores of a GEMM's output
+@pytest.mark.parametrize("m,d,n,rho,dt", [
+    (2048, 2048, 6144, 0.5, torch.bfloat16),      # persistent NT kernel: scores from the epilogue
+    (1300, 1024, 12800, 0.7, torch.bfloat16),     # NT kernel with a ragged last row slab and column tile
+    (500, 1536, 1000, 0.8, torch.bfloat16),       # row-gather core, scores in a second pass
+    (16, 2048, 3000, 0.5, torch.bfloat16),        # few-row kernel
+    (64, 512, 512, 0.5, torch.float32),           # fp32 product
+])
+def test_gemm_scored(m, d, n, rho, dt):
+    """rmm_gemm_scored: Y bitwise equal to rmm_gemm's, and its column scores equal
+    the float64 column norms of the Y values written (1e-5 relative)."""
+    rng = synth.stream(0, 96, m + n)
+    A = synth.outlier_activations(rng, m, d, 0.01, 20.0)
+    B = synth.weight(synth.stream(0, 96, d + 7), d, n)
+    Ad, Bd = dev_tensor(A, dt), dev_tensor(B, dt)
+    k = R.rmm_k_from_rho(rho, d)
+    idx = R.rmm_topk(R.rmm_colnorm(Ad), k)
+    Y0 = R.rmm_gemm(Ad, Bd, idx, k)
+    Y, sc = R.rmm_gemm_scored(Ad, Bd, idx, k)
+    torch.cuda.synchronize()
+    bits = torch.int16 if dt == torch.bfloat16 else torch.int32
+    assert torch.equal(Y.view(bits), Y0.view(bits))
+    Yh = Y.float().cpu().numpy()
+    np.testing.assert_allclose(sc.cpu().numpy(), oracle.column_scores(Yh), rtol=1e-5, atol=1e-30)
+    I = idx.cpu().numpy()[:k]
+    tol = TOL_BF16 if dt == torch.bfloat16 else TOL_F32
+    assert rel_fro(Yh, oracle.reduced_product(A, B, I)) < tol
