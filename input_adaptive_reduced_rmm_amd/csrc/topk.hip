@@ -3,13 +3,17 @@
 //
 // One workgroup per batch row (1024 threads; 256 for rows of at most 4096).
 // Scores are mapped to order-preserving unsigned keys and (for d up to
-// kLdsKeys) parked in LDS.  The exact
-// k-th largest key T is found by MSD radix select: the bits every key shares
-// are skipped (found with a block OR/AND reduction), then <= 8-bit digits are
-// histogrammed in LDS and a single wave locates the digit that holds the k-th
-// key.  Emission walks the keys in index order, one contiguous run per wave:
-// keys > T are kept, and of the keys == T the lowest-index ones up to the
-// count still needed.  All integer work: the result is exact.
+// kLdsKeys) parked in LDS.  The exact k-th largest key T is found by MSD
+// radix select: the bits every key shares are skipped (found with a block
+// OR/AND reduction), then <= 8-bit digits are histogrammed in LDS and a
+// single wave locates the digit that holds the k-th key.  Two histograms
+// alternate, so while that wave scans one the others clear the other, and a
+// pass costs two barriers.  The select stops early when the digit's bin is
+// needed whole (every key in it ranks within k): T is then the bin's lowest
+// possible key and every key >= T is kept.  Emission walks the keys in index
+// order, one contiguous run per wave: keys > T are kept, and of the keys == T
+// the lowest-index ones up to the count still needed.  All integer work: the
+// result is exact.
 #include "rmm_internal.h"
 #include "timing.h"
 
@@ -49,10 +53,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
   // (padded to 257 words so the copies' bins sit in different banks): scores
   // that crowd into a few digits then collide kRep times less.
   constexpr int kRep = NT == 1024 ? 4 : 1;
-  __shared__ uint32_t hist[kRep == 1 ? 256 : kRep * 257];
+  constexpr int kHist = kRep == 1 ? 256 : kRep * 257;
+  __shared__ uint32_t hist[2][kHist];
   constexpr int kThreads = NT, kWaves = NT / 64;
   __shared__ uint32_t red_or[kWaves], red_and[kWaves];
-  __shared__ uint32_t sel_digit, sel_above;
+  __shared__ uint32_t sel_digit, sel_above, sel_count;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (k_rows) {
@@ -103,6 +108,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
     red_or[wave] = kor;
     red_and[wave] = kand;
   }
+  for (int i = tid; i < kHist; i += kThreads) hist[0][i] = 0u;
   __syncthreads();
   kor = 0u;
   kand = 0xFFFFFFFFu;
@@ -116,14 +122,14 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
   int lo = diff ? 32 - __clz(diff) : 0;
   uint32_t prefix = lo >= 32 ? 0u : (kand & (0xFFFFFFFFu << lo));
   uint32_t krem = (uint32_t)k;  // rank of the wanted key among keys matching `prefix` above lo
+  int hb_cur = 0;
 
   while (lo > 0) {
     const int width = lo < 8 ? lo : 8;
     const int shift = lo - width;
     const uint32_t hmask = lo >= 32 ? 0u : (0xFFFFFFFFu << lo);
     const uint32_t dmask = (1u << width) - 1u;
-    for (int i = tid; i < (kRep == 1 ? 256 : kRep * 257); i += kThreads) hist[i] = 0u;
-    __syncthreads();
+    uint32_t *hist_c = hist[hb_cur];
     for (int64_t j0 = tid; j0 < d; j0 += 8 * kThreads) {
       uint32_t kk[8];
 #pragma unroll
@@ -135,7 +141,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
       for (int u = 0; u < 8; ++u) {
         const int64_t j = j0 + (int64_t)u * kThreads;
         if (j < d && (kk[u] & hmask) == prefix)
-          atomicAdd(&hist[(kRep == 1 ? 0 : (lane % kRep) * 257) + ((kk[u] >> shift) & dmask)], 1u);
+          atomicAdd(&hist_c[(kRep == 1 ? 0 : (lane % kRep) * 257) + ((kk[u] >> shift) & dmask)], 1u);
       }
     }
     __syncthreads();
@@ -144,7 +150,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
       uint32_t h0 = 0u, h1 = 0u, h2 = 0u, h3 = 0u;
 #pragma unroll
       for (int c = 0; c < kRep; ++c) {
-        const uint32_t *hc = hist + (kRep == 1 ? 0 : c * 257);
+        const uint32_t *hc = hist_c + (kRep == 1 ? 0 : c * 257);
         h0 += hc[4 * lane];
         h1 += hc[4 * lane + 1];
         h2 += hc[4 * lane + 2];
@@ -164,18 +170,31 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
         if (above < krem && krem <= above + hb[q]) {
           sel_digit = (uint32_t)(4 * lane + q);
           sel_above = above;
+          sel_count = hb[q];
         }
         above += hb[q];
       }
+    } else {
+      // the next pass's histogram, last read before this pass's first barrier
+      uint32_t *hist_n = hist[hb_cur ^ 1];
+      for (int i = tid - 64; i < kHist; i += kThreads - 64) hist_n[i] = 0u;
     }
     __syncthreads();
+    // sel_* are written again only after two more barriers: no third one here
     krem -= sel_above;
     prefix |= sel_digit << shift;
     lo = shift;
-    __syncthreads();
+    hb_cur ^= 1;
+    if (krem == sel_count) {
+      // every key of the bin ranks within k: keep all keys >= prefix
+      krem = 0xFFFFFFFFu;
+      break;
+    }
   }
 
-  // prefix is now the k-th largest key T; krem of the keys equal to T are kept.
+  // prefix is now T, the k-th largest key (or after an early stop the lowest
+  // key of its bin); krem of the keys equal to T are kept (all after an early
+  // stop).
   // Emission: each wave owns a contiguous run of indices and walks it 64 keys
   // at a time (lane = key, conflict-free LDS reads).  A counting walk gives
   // each wave its kept keys; the waves' output offsets and shares of the keys
@@ -208,7 +227,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
     gt += __shfl_xor(gt, off, 64);
     eq += __shfl_xor(eq, off, 64);
   }
-  __syncthreads();   // the wave arrays are reused below
+  __syncthreads();   // the wave arrays (last read before the first pass) are reused below
   if (lane == 0) {
     red_or[wave] = gt;
     red_and[wave] = eq;
