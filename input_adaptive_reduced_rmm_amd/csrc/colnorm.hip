@@ -17,13 +17,9 @@ namespace rmm {
 namespace {
 
 constexpr int kThreads = 256;
-#ifndef RMM_CN_UNROLL
-#define RMM_CN_UNROLL 4
-#endif
-#ifndef RMM_CN_ROWS
-#define RMM_CN_ROWS 1024
-#endif
-constexpr int kUnroll = RMM_CN_UNROLL;
+constexpr int kUnroll = 4;             // rows in flight per lane
+constexpr int64_t kChunkRows = 1024;   // rows per block at most, where the grid allows
+constexpr int kCausalTpr = 32;         // lanes across a row segment of a causal matrix (512 bytes)
 constexpr int kWaves = kThreads / 64;
 
 template <typename T, int VEC>
@@ -252,10 +248,7 @@ ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch, bo
   // grid of uneven blocks ends in a ragged last round; narrower column tiles
   // (32 lanes, 512-byte row segments) keep the tail short.  On 32 heads of
   // 16384 x 16384: 256-byte segments 1.44 ms, 512-byte 1.36 ms, 1 KiB 1.68 ms.
-#ifndef RMM_CN_CAUSAL_TPR
-#define RMM_CN_CAUSAL_TPR 32
-#endif
-  const int max_tpr = causal ? RMM_CN_CAUSAL_TPR : 64;
+  const int max_tpr = causal ? kCausalTpr : 64;
   int tpr = 1;
   while (tpr < max_tpr && tpr < lanes_needed) tpr <<= 1;
   p.tpr = tpr;
@@ -265,7 +258,7 @@ ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t m, int64_t d, int64_t batch, bo
   // 8 steps of rows.
   const int64_t tiles = p.col_tiles * batch;
   int64_t want_chunks = ceil_div(4096, tiles);
-  if (want_chunks < ceil_div(m, RMM_CN_ROWS)) want_chunks = ceil_div(m, RMM_CN_ROWS);
+  if (want_chunks < ceil_div(m, kChunkRows)) want_chunks = ceil_div(m, kChunkRows);
   if (want_chunks > 256) want_chunks = 256;
   int64_t max_chunks = ceil_div(m, rpb * 8);
   int64_t chunks = want_chunks < max_chunks ? want_chunks : max_chunks;
