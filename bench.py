@@ -794,12 +794,16 @@ def copy_calibration(dev):
 
 
 def summarize(run, kern, dtype):
-    """Per-kernel detail of a step, the roofline of its dominant kernel (largest
-    time per step) and the kept-work MFMA fraction of its projection GEMMs."""
+    """Per-kernel detail of a step, the roofline of its dominant kernel and the
+    kept-work MFMA fraction of its projection GEMMs.  The dominant kernel is the
+    one with the largest GPU time per step summed over every launch of it (the
+    four projections' GEMMs are one kernel); its achieved rate is the algorithmic
+    work of those launches over their time, i.e. the average work per launch over
+    the average launch time."""
     import torch
 
     detail = {}
-    best = None
+    groups = {}
     for key, v in kern.items():
         bound, amount, unit = algorithmic_work(run, key)
         tot = v["avg_ms"] * v["launches_per_step"]
@@ -813,23 +817,31 @@ def summarize(run, kern, dtype):
             else:
                 ent["gbs"] = round(rate / 1e9, 1)
                 ent["frac"] = round(rate / 1e9 / PEAK_HBM_GBS, 4)
+            tag, name = key.split("/", 1) if "/" in key else ("", key)
+            g = groups.setdefault((name, bound, unit), {"ms": 0.0, "amount": 0.0, "launches": 0.0, "tags": []})
+            g["ms"] += tot
+            g["amount"] += amount * v["launches_per_step"]
+            g["launches"] += v["launches_per_step"]
+            g["tags"].append(tag)
         detail[key] = ent
-        if bound and (best is None or tot > best[0]):
-            best = (tot, key, bound, amount, unit, v["avg_ms"])
     roof = None
-    if best:
-        _, key, bound, amount, unit, avg = best
+    if groups:
+        (name, bound, unit), g = max(groups.items(), key=lambda kv: kv[1]["ms"])
+        per_launch, avg = g["amount"] / g["launches"], g["ms"] / g["launches"]
+        kernel = name if len(g["tags"]) > 1 else f"{g['tags'][0]}/{name}"
         if unit == "flops":
             peak = PEAK_F32_TFLOPS if dtype == torch.float32 else PEAK_BF16_TFLOPS
-            ach = amount / (avg * 1e-3) / 1e12
+            ach = per_launch / (avg * 1e-3) / 1e12
             roof = {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(ach / peak, 4), "kernel": key, "per_launch": f"{amount:.4g} flops",
-                    "avg_launch_ms": round(avg, 4)}
+                    "frac": round(ach / peak, 4), "kernel": kernel, "per_launch": f"{per_launch:.4g} flops",
+                    "avg_launch_ms": round(avg, 4), "launches_per_step": g["launches"]}
         else:
-            ach = amount / (avg * 1e-3) / 1e9
+            ach = per_launch / (avg * 1e-3) / 1e9
             roof = {"bound": bound, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(ach / PEAK_HBM_GBS, 4), "kernel": key, "per_launch": f"{amount:.4g} bytes",
-                    "avg_launch_ms": round(avg, 4)}
+                    "frac": round(ach / PEAK_HBM_GBS, 4), "kernel": kernel, "per_launch": f"{per_launch:.4g} bytes",
+                    "avg_launch_ms": round(avg, 4), "launches_per_step": g["launches"]}
+        if len(g["tags"]) > 1:
+            roof["tags"] = g["tags"]
     g_fl = g_ms = 0.0
     for key, v in kern.items():
         bound, amount, unit = algorithmic_work(run, key)
