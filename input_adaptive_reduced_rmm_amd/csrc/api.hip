@@ -692,13 +692,20 @@ RMM_API rmm_status_t rmm_attention(const void *Q, int64_t Lq, int64_t Hq, int64_
   if (rmm::attn_decode_ok(Lq, dh) && aligned(V, 16) && v_tok_stride % 8 == 0 && v_head_stride % 8 == 0) {
     // a few queries after a long context: passes split over keys
     const AttnDecLayout D = attn_dec_layout(Lq, Lk, Hq, dh, k_tok);
-    float *tokd = tok_scores ? tok_scores : reinterpret_cast<float *>(w + D.tok);
-    const rmm::ColnormPlan p = plan_for(RMM_BF16, Q, Lq, dh, q_tok_stride, Hq, q_head_stride);
-    hipError_t he = rmm::launch_colnorm(RMM_BF16, Q, Lq, dh, q_tok_stride, Hq, q_head_stride,
-                                        reinterpret_cast<float *>(w + D.sc), w + D.part, p, st);
-    if (he != hipSuccess) return hip_status(he, "attention colnorm launch");
-    he = rmm::launch_topk(reinterpret_cast<float *>(w + D.sc), Hq, dh, k_feat, kfp, idx_feat, st);
-    if (he != hipSuccess) return hip_status(he, "attention topk launch");
+    const bool fused_sel = rmm::attn_decode_select_fused(Lk);
+    float *tokd = tok_scores ? tok_scores : fused_sel ? nullptr : reinterpret_cast<float *>(w + D.tok);
+    hipError_t he;
+    if (Lq == 1) {
+      he = rmm::launch_dec_feat1(Q, 0, q_head_stride, 1, Hq, k_feat, kfp, idx_feat, st);
+      if (he != hipSuccess) return hip_status(he, "attention feature selection launch");
+    } else {
+      const rmm::ColnormPlan p = plan_for(RMM_BF16, Q, Lq, dh, q_tok_stride, Hq, q_head_stride);
+      he = rmm::launch_colnorm(RMM_BF16, Q, Lq, dh, q_tok_stride, Hq, q_head_stride,
+                               reinterpret_cast<float *>(w + D.sc), w + D.part, p, st);
+      if (he != hipSuccess) return hip_status(he, "attention colnorm launch");
+      he = rmm::launch_topk(reinterpret_cast<float *>(w + D.sc), Hq, dh, k_feat, kfp, idx_feat, st);
+      if (he != hipSuccess) return hip_status(he, "attention topk launch");
+    }
     rmm::AttnDecodeDesc dd{};
     dd.Q = Q;
     dd.q_ts = q_tok_stride;
@@ -731,10 +738,15 @@ RMM_API rmm_status_t rmm_attention(const void *Q, int64_t Lq, int64_t Hq, int64_
     dd.causal = causal != 0;
     he = rmm::launch_attn_decode(0, dd, st);
     if (he != hipSuccess) return hip_status(he, "attention scores launch");
-    he = rmm::launch_attn_decode(1, dd, st);
-    if (he != hipSuccess) return hip_status(he, "attention token scores launch");
-    he = rmm::launch_topk(tokd, Hq, Lk, k_tok, ktp, idx_tok, st);
-    if (he != hipSuccess) return hip_status(he, "attention token topk launch");
+    if (fused_sel) {
+      he = rmm::launch_attn_decode(4, dd, st);
+      if (he != hipSuccess) return hip_status(he, "attention token selection launch");
+    } else {
+      he = rmm::launch_attn_decode(1, dd, st);
+      if (he != hipSuccess) return hip_status(he, "attention token scores launch");
+      he = rmm::launch_topk(tokd, Hq, Lk, k_tok, ktp, idx_tok, st);
+      if (he != hipSuccess) return hip_status(he, "attention token topk launch");
+    }
     he = rmm::launch_attn_decode(2, dd, st);
     if (he != hipSuccess) return hip_status(he, "attention output launch");
     return hip_status(rmm::launch_attn_decode(3, dd, st), "attention output merge launch");
@@ -863,12 +875,10 @@ RMM_API rmm_status_t rmm_attention_decode_batch(
   hipStream_t st = (hipStream_t)stream;
   const AttnBatchLayout D = attn_batch_layout(nseq, Hq, Lmax, kt_max);
   const int64_t kfp = rmm_k_pad(k_feat), ktp = rmm_k_pad(kt_max), rows = nseq * Hq;
-  float *sc = reinterpret_cast<float *>(w + D.sc);
-  float *tokd = tok_scores ? tok_scores : reinterpret_cast<float *>(w + D.tok);
-  hipError_t he = rmm::launch_dec_qabs(Q, q_seq_stride, q_head_stride, nseq, Hq, sc, st);
-  if (he != hipSuccess) return hip_status(he, "attention_decode_batch feature scores launch");
-  he = rmm::launch_topk(sc, rows, dh, k_feat, kfp, idx_feat, st);
-  if (he != hipSuccess) return hip_status(he, "attention_decode_batch feature topk launch");
+  const bool fused_sel = rmm::attn_decode_select_fused(Lmax);
+  float *tokd = tok_scores ? tok_scores : fused_sel ? nullptr : reinterpret_cast<float *>(w + D.tok);
+  hipError_t he = rmm::launch_dec_feat1(Q, q_seq_stride, q_head_stride, nseq, Hq, k_feat, kfp, idx_feat, st);
+  if (he != hipSuccess) return hip_status(he, "attention_decode_batch feature selection launch");
   rmm::AttnDecodeDesc dd{};
   dd.Q = Q;
   dd.q_ts = dh;
@@ -908,10 +918,15 @@ RMM_API rmm_status_t rmm_attention_decode_batch(
   dd.kts = k_tok;
   he = rmm::launch_attn_decode(0, dd, st);
   if (he != hipSuccess) return hip_status(he, "attention_decode_batch scores launch");
-  he = rmm::launch_attn_decode(1, dd, st);
-  if (he != hipSuccess) return hip_status(he, "attention_decode_batch token scores launch");
-  he = rmm::launch_topk(tokd, rows, Lmax, kt_max, ktp, idx_tok, st, k_tok, (int)Hq, lens);
-  if (he != hipSuccess) return hip_status(he, "attention_decode_batch token topk launch");
+  if (fused_sel) {
+    he = rmm::launch_attn_decode(4, dd, st);
+    if (he != hipSuccess) return hip_status(he, "attention_decode_batch token selection launch");
+  } else {
+    he = rmm::launch_attn_decode(1, dd, st);
+    if (he != hipSuccess) return hip_status(he, "attention_decode_batch token scores launch");
+    he = rmm::launch_topk(tokd, rows, Lmax, kt_max, ktp, idx_tok, st, k_tok, (int)Hq, lens);
+    if (he != hipSuccess) return hip_status(he, "attention_decode_batch token topk launch");
+  }
   he = rmm::launch_attn_decode(2, dd, st);
   if (he != hipSuccess) return hip_status(he, "attention_decode_batch output launch");
   return hip_status(rmm::launch_attn_decode(3, dd, st), "attention_decode_batch output merge launch");

@@ -11,15 +11,19 @@
 //               (each kept feature row of a 256-key block is 512 contiguous
 //               bytes), written to the workspace (Lq x Lk floats per head),
 //               with each block's per-query max and sum of 2^(c (S - max));
-//   dec_tok     merges those partial statistics and writes the token scores
-//               sqrt(sum_i P_ij^2), P_ij = 2^(c S_ij + nml_i);
-//   top-k       per head over the Lk token scores;
+//   dec_tok_select  one workgroup per head: merges those partial
+//               statistics, forms the token scores sqrt(sum_i P_ij^2),
+//               P_ij = 2^(c S_ij + nml_i), keeps them in LDS and selects the
+//               kept tokens there (contexts up to kSelKeys; longer ones write
+//               the scores with dec_tok and select with the top-k kernel);
 //   dec_out     per block of 256 kept tokens: P_ij from S, the kept V rows
 //               (16-byte loads), partial O sums per (block, head);
 //   dec_merge   adds the partial O in block order, rounds to bf16 and (when
 //               asked) forms the column scores of O.
-// Everything is float32 except the bf16 inputs and O; all sums run in a fixed
-// order, so results are deterministic.
+// With one new token, the feature selection (|q_f| over the 128 features,
+// top k_feat) is one wave per head (dec_feat1).  Everything is float32
+// except the bf16 inputs and O; all sums run in a fixed order, so results
+// are deterministic.
 //
 // A batch of sequences (a decode step over several caches) runs through the
 // same passes with the (sequence, head) pairs as the rows: each pair reads
@@ -27,6 +31,7 @@
 // and kept-token count come from device arrays, and keys past a sequence's
 // length score -inf (never selected, weight zero).
 #include "rmm_internal.h"
+#include "select.h"
 #include "timing.h"
 
 namespace rmm {
@@ -34,6 +39,8 @@ namespace {
 
 constexpr int kDB = 256;   // keys (or kept tokens) per workgroup pass, one per thread
 constexpr int kTokSub = 1;   // 256-token sub-tiles per output workgroup
+constexpr int kSelThreads = 1024;   // token selection workgroup
+constexpr int kSelKeys = 32768;     // token scores held in LDS by the selection (128 KiB)
 constexpr float kNegInfD = -__builtin_inff();
 
 __device__ __forceinline__ float dexp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -47,10 +54,11 @@ struct DecArgs {
   int64_t v_ts, v_hs;
   const int32_t *I;       // [hq][kf_pad] kept features, ascending
   const int32_t *J;       // [hq][kt_pad] kept tokens, ascending
+  int32_t *Jw;            // the same rows, written by the token selection
   float *S;               // [hq][Lq][Lk]
   float2 *pstat;          // [hq][nblk][Lq] (block max of S, sum of 2^(c (S - max)))
   float *nml;             // [hq][Lq]
-  float *tok;             // [hq][Lk]
+  float *tok;             // [hq][Lk] (the fused selection writes it only when not null)
   float *opart;           // [nsplit][hq][Lq][128]
   uint16_t *O;            // element (i, h, d) at O + i*o_ts + h*o_hs + d
   int64_t o_ts, o_hs;
@@ -90,9 +98,10 @@ __device__ __forceinline__ SeqRow seq_row(const DecArgs &g, int64_t r) {
   return q;
 }
 
-// Block-wide reduction of LQ values per thread (max or sum); returns the result
-// to every thread.  red: LDS scratch of 4 * LQ floats.
-template <int LQ, bool MAX>
+// Block-wide reduction of LQ values per thread (max or sum) over NW waves;
+// returns the result to every thread.  Waves are combined by a pairwise tree
+// in wave order.  red: LDS scratch of NW * LQ floats.
+template <int LQ, bool MAX, int NW = 4>
 __device__ __forceinline__ void block_reduce(float (&v)[LQ], float *red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -111,8 +120,14 @@ __device__ __forceinline__ void block_reduce(float (&v)[LQ], float *red) {
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < LQ; ++i) {
-    const float a = red[i], b = red[LQ + i], c = red[2 * LQ + i], d = red[3 * LQ + i];
-    v[i] = MAX ? fmaxf(fmaxf(a, b), fmaxf(c, d)) : (a + b) + (c + d);
+    float t[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t[w] = red[w * LQ + i];
+#pragma unroll
+    for (int st = 1; st < NW; st *= 2)
+#pragma unroll
+      for (int w = 0; w + st < NW; w += 2 * st) t[w] = MAX ? fmaxf(t[w], t[w + st]) : t[w] + t[w + st];
+    v[i] = t[0];
   }
 }
 
@@ -275,7 +290,7 @@ __global__ __launch_bounds__(kDB) void dec_scores1_kernel(DecArgs g) {
 // Merge the key blocks' statistics of head h: every thread takes the blocks
 // b = tid, tid + 256, ... (loads independent of each other), then block-wide
 // max and sum in a fixed order.  Returns nml_i = -c max_i - log2(sum_i).
-template <int LQ>
+template <int LQ, int NW = 4>
 __device__ __forceinline__ void merge_stats(const DecArgs &g, int64_t h, float (&nml)[LQ], float *red) {
   const int tid = threadIdx.x, Lq = (int)g.Lq;
   // blocks this row has (a shorter sequence has fewer)
@@ -283,21 +298,21 @@ __device__ __forceinline__ void merge_stats(const DecArgs &g, int64_t h, float (
   float M[LQ], L[LQ];
 #pragma unroll
   for (int i = 0; i < LQ; ++i) M[i] = kNegInfD;
-  for (int b = tid; b < nb; b += kDB)
+  for (int b = tid; b < nb; b += 64 * NW)
 #pragma unroll
     for (int i = 0; i < LQ; ++i)
       if (i < Lq) M[i] = fmaxf(M[i], g.pstat[(h * g.nblk + b) * g.Lq + i].x);
-  block_reduce<LQ, true>(M, red);
+  block_reduce<LQ, true, NW>(M, red);
 #pragma unroll
   for (int i = 0; i < LQ; ++i) L[i] = 0.f;
-  for (int b = tid; b < nb; b += kDB)
+  for (int b = tid; b < nb; b += 64 * NW)
 #pragma unroll
     for (int i = 0; i < LQ; ++i)
       if (i < Lq) {
         const float2 p = g.pstat[(h * g.nblk + b) * g.Lq + i];
         if (p.x != kNegInfD) L[i] += p.y * dexp2((p.x - M[i]) * g.c2);
       }
-  block_reduce<LQ, false>(L, red);
+  block_reduce<LQ, false, NW>(L, red);
 #pragma unroll
   for (int i = 0; i < LQ; ++i) nml[i] = (i < Lq && L[i] > 0.f) ? -M[i] * g.c2 - log2f(L[i]) : kNegInfD;
 }
@@ -338,6 +353,78 @@ __global__ __launch_bounds__(kDB) void dec_tok_kernel(DecArgs g) {
       if (sv != kNegInfD) t += dexp2(fmaf(sv, c4, 2.f * snml[i]));
     }
   g.tok[h * g.Lk + j] = __builtin_sqrtf(t);
+}
+
+// Token scores and token selection of row h in one workgroup (Lk <= kSelKeys):
+// the statistics merge of dec_tok (same partial order, so the same nml and
+// scores), every score computed once, parked in LDS as an order-preserving
+// key and, when asked, written to tok; then sel::block_select keeps the row's
+// kt highest (ties to the lower index) into J.  Keys past the row's context
+// score -inf and are never kept (kt <= the row's context).
+template <int LQ>
+__global__ __launch_bounds__(kSelThreads) void dec_tok_select_kernel(DecArgs g) {
+  constexpr int NW = kSelThreads / 64;
+  __shared__ uint32_t keys[kSelKeys];
+  __shared__ sel::BlockShared<kSelThreads> sh;
+  __shared__ float red[NW * LQ];
+  const int tid = threadIdx.x;
+  const int64_t h = blockIdx.x;
+  const int Lq = (int)g.Lq;
+  const SeqRow sr = seq_row(g, h);
+  float snml[LQ];
+  merge_stats<LQ, NW>(g, h, snml, red);
+  if (tid < Lq) {
+    float v = snml[0];
+#pragma unroll
+    for (int i = 1; i < LQ; ++i)
+      if (tid == i) v = snml[i];
+    g.nml[h * g.Lq + tid] = v;
+  }
+  const float c4 = 2.f * g.c2;
+  // Every token of the context kept: the selection is the identity (as the
+  // top-k kernel's k == d case), and the scores are formed only when asked.
+  const bool keep_all = sr.kt >= sr.Lk;
+  if (keep_all && !g.tok) {
+    for (int64_t t = tid; t < g.kt_pad; t += kSelThreads) g.Jw[h * g.kt_pad + t] = t < sr.kt ? (int32_t)t : -1;
+    return;
+  }
+  // U keys per thread at a time: their S loads are in flight together
+  constexpr int U = LQ <= 2 ? 8 : LQ <= 4 ? 4 : 2;
+  uint32_t kor = 0u, kand = 0xFFFFFFFFu;
+  for (int64_t j0 = tid; j0 < g.Lk; j0 += (int64_t)U * kSelThreads) {
+    float sv[U][LQ];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = j0 + (int64_t)u * kSelThreads;
+#pragma unroll
+      for (int i = 0; i < LQ; ++i)
+        sv[u][i] = (i < Lq && j < sr.Lk) ? g.S[(h * g.Lq + i) * g.Lk + j] : kNegInfD;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = j0 + (int64_t)u * kSelThreads;
+      if (j >= g.Lk) break;
+      float t = kNegInfD;   // past this sequence's context: never kept
+      if (j < sr.Lk) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < LQ; ++i)
+          if (i < Lq && sv[u][i] != kNegInfD) a += dexp2(fmaf(sv[u][i], c4, 2.f * snml[i]));
+        t = __builtin_sqrtf(a);
+      }
+      if (g.tok) g.tok[h * g.Lk + j] = t;
+      const uint32_t key = sel::score_key(t);
+      keys[j] = key;
+      kor |= key;
+      kand &= key;
+    }
+  }
+  if (keep_all) {
+    for (int64_t t = tid; t < g.kt_pad; t += kSelThreads) g.Jw[h * g.kt_pad + t] = t < sr.kt ? (int32_t)t : -1;
+    return;
+  }
+  sel::block_select<kSelThreads>([&](int64_t j) -> uint32_t { return keys[j]; }, g.Lk, kor, kand, sr.kt,
+                                 g.kt_pad, g.Jw + h * g.kt_pad, sh);
 }
 
 template <int LQ>
@@ -451,24 +538,35 @@ __global__ __launch_bounds__(256) void dec_merge_kernel(DecArgs g) {
   }
 }
 
-// Feature scores of one new token per (sequence, head) row: the column norm
-// over a single row is |q_f| (sqrt of an exact square).
-__global__ __launch_bounds__(128) void dec_qabs_kernel(const uint16_t *__restrict__ Q, int64_t q_ss, int64_t q_hs,
-                                                       int64_t hq, float *__restrict__ sc) {
-  const int64_t r = blockIdx.x, b = r / hq, h = r - b * hq;
-  const float q = bf16_to_f32(Q[b * q_ss + h * q_hs + threadIdx.x]);
-  sc[r * 128 + threadIdx.x] = __builtin_sqrtf(q * q);
+// Feature selection of one new token per (sequence, head) row, one wave per
+// row: scores |q_f| = sqrt(q_f^2) (the column norm over a single row, as the
+// column-score kernel forms it), then the k_feat highest of the 128 features
+// (ties to the lower index) into I, ascending.
+__global__ __launch_bounds__(256) void dec_feat1_kernel(const uint16_t *__restrict__ Q, int64_t q_ss, int64_t q_hs,
+                                                        int64_t hq, int64_t nrows, int kf, int kf_pad,
+                                                        int32_t *__restrict__ I) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= nrows) return;   // whole waves
+  const int64_t b = r / hq, h = r - b * hq;
+  const uint16_t *q = Q + b * q_ss + h * q_hs;
+  const float x0 = bf16_to_f32(q[lane]), x1 = bf16_to_f32(q[64 + lane]);
+  sel::wave_select128(sel::score_key(__builtin_sqrtf(x0 * x0)), sel::score_key(__builtin_sqrtf(x1 * x1)), kf,
+                      kf_pad, I + r * kf_pad);
 }
 
 }  // namespace
 
-hipError_t launch_dec_qabs(const void *Q, int64_t q_ss, int64_t q_hs, int64_t nseq, int64_t hq, float *scores,
-                           hipStream_t st) {
-  KernelTimer timer("colnorm", st);
-  hipLaunchKernelGGL(dec_qabs_kernel, dim3((unsigned)(nseq * hq)), dim3(128), 0, st,
-                     static_cast<const uint16_t *>(Q), q_ss, q_hs, hq, scores);
+hipError_t launch_dec_feat1(const void *Q, int64_t q_ss, int64_t q_hs, int64_t nseq, int64_t hq, int64_t kf,
+                            int64_t kf_pad, int32_t *I, hipStream_t st) {
+  KernelTimer timer("dec_feat", st);
+  const int64_t rows = nseq * hq;
+  hipLaunchKernelGGL(dec_feat1_kernel, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, st,
+                     static_cast<const uint16_t *>(Q), q_ss, q_hs, hq, rows, (int)kf, (int)kf_pad, I);
   return hipGetLastError();
 }
+
+bool attn_decode_select_fused(int64_t Lk) { return Lk <= kSelKeys; }
 
 bool attn_decode_ok(int64_t Lq, int64_t dh) { return Lq >= 1 && Lq <= 16 && dh == 128; }
 
@@ -508,6 +606,7 @@ hipError_t launch_attn_decode(int pass, const AttnDecodeDesc &d, hipStream_t st)
   g.v_hs = d.v_hs;
   g.I = d.I;
   g.J = d.J;
+  g.Jw = d.J;
   g.S = d.S;
   g.pstat = reinterpret_cast<float2 *>(d.pstat);
   g.nml = d.nml;
@@ -552,6 +651,17 @@ hipError_t launch_attn_decode(int pass, const AttnDecodeDesc &d, hipStream_t st)
   } else if (pass == 1) {
     KernelTimer timer("dec_tok", st);
     RMM_DEC_LAUNCH(dec_tok_kernel, lq, dim3((unsigned)z.ntokblk, (unsigned)g.nrows), g, st);
+  } else if (pass == 4) {
+    // token scores and selection in one launch (attn_decode_select_fused)
+    if (d.Lk > kSelKeys) return hipErrorInvalidValue;
+    KernelTimer timer("dec_tok_select", st);
+    switch (lq) {
+      case 1: hipLaunchKernelGGL(dec_tok_select_kernel<1>, dim3((unsigned)g.nrows), dim3(kSelThreads), 0, st, g); break;
+      case 2: hipLaunchKernelGGL(dec_tok_select_kernel<2>, dim3((unsigned)g.nrows), dim3(kSelThreads), 0, st, g); break;
+      case 4: hipLaunchKernelGGL(dec_tok_select_kernel<4>, dim3((unsigned)g.nrows), dim3(kSelThreads), 0, st, g); break;
+      case 8: hipLaunchKernelGGL(dec_tok_select_kernel<8>, dim3((unsigned)g.nrows), dim3(kSelThreads), 0, st, g); break;
+      default: hipLaunchKernelGGL(dec_tok_select_kernel<16>, dim3((unsigned)g.nrows), dim3(kSelThreads), 0, st, g); break;
+    }
   } else if (pass == 2) {
     KernelTimer timer("dec_out", st);
     RMM_DEC_LAUNCH(dec_out_kernel, lq, dim3((unsigned)z.nsplit, (unsigned)g.nrows), g, st);

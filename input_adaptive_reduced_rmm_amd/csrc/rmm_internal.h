@@ -179,8 +179,8 @@ struct AttnDecodeDesc {
   const void *Kt; int64_t kt_hs, ldkt;    // bf16, feature-major
   const void *V;  int64_t v_ts, v_hs;     // bf16
   const int32_t *I;                       // [hq][kf_pad] kept features
-  const int32_t *J;                       // [hq][kt_pad] kept tokens
-  float *S, *pstat, *nml, *tok, *opart;   // workspace (attn_decode_sizes), tok [hq][Lk]
+  int32_t *J;                             // [hq][kt_pad] kept tokens
+  float *S, *pstat, *nml, *tok, *opart;   // workspace (attn_decode_sizes), tok [hq][Lk] (may be null for pass 4)
   void *O; int64_t o_ts, o_hs;            // bf16
   float *o_scores;                        // [hq][128] or null
   int64_t hq, hkv, Lq, Lk, kf, kf_pad, kt, kt_pad;
@@ -198,9 +198,15 @@ struct AttnDecodeSizes {
 };
 bool attn_decode_ok(int64_t Lq, int64_t dh);
 AttnDecodeSizes attn_decode_sizes(int64_t Lq, int64_t Lk, int64_t Hq, int64_t kt);
+// pass 0: scores and block statistics; 1: token scores (dec_tok); 4: token
+// scores and token selection in one launch (needs attn_decode_select_fused);
+// 2: output partials; 3: output merge.
 hipError_t launch_attn_decode(int pass, const AttnDecodeDesc &d, hipStream_t stream);
-// scores[r][f] = |Q[b][h][f]| for row r = b * hq + h (one new token per sequence; dh == 128)
-hipError_t launch_dec_qabs(const void *Q, int64_t q_ss, int64_t q_hs, int64_t nseq, int64_t hq, float *scores,
-                           hipStream_t stream);
+bool attn_decode_select_fused(int64_t Lk);
+// Feature selection of one new token per (sequence, head) row r = b * hq + h:
+// the k_feat largest |Q[b][h][f]| of the 128 features, ties to the lower
+// index, ascending in I[r][0, kf), then -1 up to kf_pad.
+hipError_t launch_dec_feat1(const void *Q, int64_t q_ss, int64_t q_hs, int64_t nseq, int64_t hq, int64_t kf,
+                            int64_t kf_pad, int32_t *I, hipStream_t stream);
 
 }  // namespace rmm

@@ -124,6 +124,10 @@ DECODE = [
     (16, 16, 2, 2, 128, 16, True),
     (7, 2000, 4, 4, 100, 1999, False),
     (2, 513, 2, 1, 1, 1, True),
+    # contexts longer than the one-workgroup token selection holds in LDS
+    # (32768 scores): token scores and top-k as two launches
+    (1, 40000, 2, 1, 64, 20000, True),
+    (4, 33000, 2, 2, 32, 1000, True),
 ]
 
 
@@ -133,6 +137,22 @@ def test_fused_attention_decode(case):
     Lq, Lk, Hq, Hkv, kf, kt, causal = case
     Q, Kt, V = _operands(W4K, Lq, Lk, Hq, Hkv)
     print(f"  near ties: {check_fused(Q, Kt, V, kf, kt, causal)}")
+
+
+@pytest.mark.parametrize("Lq,Lk", [(1, 3000), (5, 3000), (1, 40000)])
+def test_fused_attention_decode_without_token_scores(Lq, Lk):
+    """Asking for the token scores changes no output: O, I and J are bitwise the same."""
+    Hq, Hkv, kf, kt = 4, 2, 64, Lk // 2
+    Q, Kt, V = (dev_tensor(x, torch.bfloat16) for x in _operands(W4K, Lq, Lk, Hq, Hkv))
+    ts = torch.empty((Hq, Lk), dtype=torch.float32, device=DEV)
+    a = R.rmm_attention(Q, Kt, V, kf, kt, causal=True, tok_scores=ts)
+    b = R.rmm_attention(Q, Kt, V, kf, kt, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    J = b[2].cpu().numpy()
+    for h in range(Hq):
+        assert np.array_equal(J[h][:kt], oracle.select_top(ts[h].cpu().numpy().astype(np.float64), kt))
 
 
 def test_fused_attention_decode_unaligned_values_use_the_general_path():
