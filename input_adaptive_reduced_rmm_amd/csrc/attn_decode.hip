@@ -364,7 +364,7 @@ __global__ __launch_bounds__(kDB) void dec_tok_kernel(DecArgs g) {
 template <int LQ>
 __global__ __launch_bounds__(kSelThreads) void dec_tok_select_kernel(DecArgs g) {
   constexpr int NW = kSelThreads / 64;
-  __shared__ uint32_t keys[kSelKeys];
+  __shared__ __attribute__((aligned(16))) uint32_t keys[kSelKeys];
   __shared__ sel::BlockShared<kSelThreads> sh;
   __shared__ float red[NW * LQ];
   const int tid = threadIdx.x;
@@ -388,35 +388,79 @@ __global__ __launch_bounds__(kSelThreads) void dec_tok_select_kernel(DecArgs g) 
     for (int64_t t = tid; t < g.kt_pad; t += kSelThreads) g.Jw[h * g.kt_pad + t] = t < sr.kt ? (int32_t)t : -1;
     return;
   }
-  // U keys per thread at a time: their S loads are in flight together
-  constexpr int U = LQ <= 2 ? 8 : LQ <= 4 ? 4 : 2;
   uint32_t kor = 0u, kand = 0xFFFFFFFFu;
-  for (int64_t j0 = tid; j0 < g.Lk; j0 += (int64_t)U * kSelThreads) {
-    float sv[U][LQ];
+  // Token score of key j from its Lq values of S (-inf past the context).
+  auto score = [&](const float (&sv)[LQ], int64_t j) -> float {
+    if (j >= sr.Lk) return kNegInfD;   // past this sequence's context: never kept
+    float a = 0.f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t j = j0 + (int64_t)u * kSelThreads;
+    for (int i = 0; i < LQ; ++i)
+      if (i < Lq && sv[i] != kNegInfD) a += dexp2(fmaf(sv[i], c4, 2.f * snml[i]));
+    return __builtin_sqrtf(a);
+  };
+  if (g.Lk % 4 == 0) {
+    // four keys per thread and load (S rows are 16-byte aligned), U groups
+    // of them with their loads in flight together
+    constexpr int U = LQ <= 2 ? 2 : 1;
+    const int64_t n4 = g.Lk / 4;
+    const bool tok16 = g.tok && reinterpret_cast<uintptr_t>(g.tok) % 16 == 0;
+    const float4 *S4 = reinterpret_cast<const float4 *>(g.S);
+    for (int64_t t0 = tid; t0 < n4; t0 += (int64_t)U * kSelThreads) {
+      float4 v[U][LQ];
 #pragma unroll
-      for (int i = 0; i < LQ; ++i)
-        sv[u][i] = (i < Lq && j < sr.Lk) ? g.S[(h * g.Lq + i) * g.Lk + j] : kNegInfD;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t j = j0 + (int64_t)u * kSelThreads;
-      if (j >= g.Lk) break;
-      float t = kNegInfD;   // past this sequence's context: never kept
-      if (j < sr.Lk) {
-        float a = 0.f;
+      for (int u = 0; u < U; ++u) {
+        const int64_t t = t0 + (int64_t)u * kSelThreads;
 #pragma unroll
         for (int i = 0; i < LQ; ++i)
-          if (i < Lq && sv[u][i] != kNegInfD) a += dexp2(fmaf(sv[u][i], c4, 2.f * snml[i]));
-        t = __builtin_sqrtf(a);
+          v[u][i] = (i < Lq && t < n4) ? S4[(h * g.Lq + i) * n4 + t]
+                                       : make_float4(kNegInfD, kNegInfD, kNegInfD, kNegInfD);
       }
-      if (g.tok) g.tok[h * g.Lk + j] = t;
-      const uint32_t key = sel::score_key(t);
-      keys[j] = key;
-      kor |= key;
-      kand &= key;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t t = t0 + (int64_t)u * kSelThreads;
+        if (t >= n4) break;
+        float sc[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float sv[LQ];
+#pragma unroll
+          for (int i = 0; i < LQ; ++i) sv[i] = e == 0 ? v[u][i].x : e == 1 ? v[u][i].y : e == 2 ? v[u][i].z : v[u][i].w;
+          sc[e] = score(sv, 4 * t + e);
+        }
+        if (tok16) *reinterpret_cast<float4 *>(&g.tok[h * g.Lk + 4 * t]) = make_float4(sc[0], sc[1], sc[2], sc[3]);
+        else if (g.tok)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) g.tok[h * g.Lk + 4 * t + e] = sc[e];
+        const uint4 key = make_uint4(sel::score_key(sc[0]), sel::score_key(sc[1]), sel::score_key(sc[2]),
+                                     sel::score_key(sc[3]));
+        *reinterpret_cast<uint4 *>(&keys[4 * t]) = key;
+        kor |= key.x | key.y | key.z | key.w;
+        kand &= key.x & key.y & key.z & key.w;
+      }
+    }
+  } else {
+    // U keys per thread at a time: their S loads are in flight together
+    constexpr int U = LQ <= 2 ? 8 : LQ <= 4 ? 4 : 2;
+    for (int64_t j0 = tid; j0 < g.Lk; j0 += (int64_t)U * kSelThreads) {
+      float sv[U][LQ];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = j0 + (int64_t)u * kSelThreads;
+#pragma unroll
+        for (int i = 0; i < LQ; ++i)
+          sv[u][i] = (i < Lq && j < sr.Lk) ? g.S[(h * g.Lq + i) * g.Lk + j] : kNegInfD;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = j0 + (int64_t)u * kSelThreads;
+        if (j >= g.Lk) break;
+        const float t = score(sv[u], j);
+        if (g.tok) g.tok[h * g.Lk + j] = t;
+        const uint32_t key = sel::score_key(t);
+        keys[j] = key;
+        kor |= key;
+        kand &= key;
+      }
     }
   }
   if (keep_all) {
