@@ -155,6 +155,32 @@ def test_fused_attention_decode_without_token_scores(Lq, Lk):
         assert np.array_equal(J[h][:kt], oracle.select_top(ts[h].cpu().numpy().astype(np.float64), kt))
 
 
+@pytest.mark.parametrize("Lq,Lk", [(1, 1000), (1, 20000), (3, 5000)])
+def test_fused_attention_decode_ties_keep_lowest_indices(Lq, Lk):
+    """All-equal scores in both selections of a decode step: |q| equal over the
+    features (q = +-1) and every key zero, so every token's probability and score
+    tie. Both selections must then keep the lowest indices, and O the mean of the
+    kept V rows."""
+    Hq, Hkv, kf, kt = 4, 2, 37, Lk // 3
+    rng = np.random.default_rng(17)
+    Q = np.where(rng.random((Lq, Hq, 128)) < 0.5, -1.0, 1.0).astype(np.float32)
+    Kt = np.zeros((Hkv, 128, Lk), np.float32)
+    V = rng.standard_normal((Lk, Hkv, 128)).astype(np.float32)
+    Qd, Ktd, Vd = dev_tensor(Q, torch.bfloat16), dev_tensor(Kt, torch.bfloat16), dev_tensor(V, torch.bfloat16)
+    ts = torch.empty((Hq, Lk), dtype=torch.float32, device=DEV)
+    O, I, J = R.rmm_attention(Qd, Ktd, Vd, kf, kt, causal=False, tok_scores=ts)
+    torch.cuda.synchronize()
+    I, J, O, ts = I.cpu().numpy(), J.cpu().numpy(), O.float().cpu().numpy(), ts.cpu().numpy()
+    Vk = Vd.float().cpu().numpy().astype(np.float64)     # V as the kernels read it (bf16)
+    P = np.full((Lq, Lk), 1.0 / Lk)                       # every key scores zero: uniform probabilities
+    for h in range(Hq):
+        assert np.array_equal(I[h][:kf], np.arange(kf)) and np.all(I[h][kf:] == -1)
+        assert np.all(ts[h] == ts[h][0])
+        assert np.array_equal(J[h][:kt], np.arange(kt)) and np.all(J[h][kt:] == -1)
+        want = oracle.reduced_product(P, Vk[:, oracle.kv_head(h, Hq, Hkv), :], J[h][:kt])
+        assert rel_fro(O[:, h, :], want) < TOL_BF16
+
+
 def test_fused_attention_decode_unaligned_values_use_the_general_path():
     """V rows that are not 16-byte aligned go through the general passes: same results."""
     Lq, Lk, Hq, Hkv, kf, kt = 4, 700, 4, 2, 64, 350
