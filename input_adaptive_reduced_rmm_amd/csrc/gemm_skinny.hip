@@ -12,9 +12,13 @@
 //
 // Per K-tile of 64 kept rows each thread loads one 16-byte chunk from each of
 // its rows (the row offsets come from the cleaned index list staged in LDS;
-// -1 rows read as zero through the buffer range), converts int8 to bf16
-// (exact: |q| <= 128 needs 8 significant bits), transposes its block in
-// registers into K-runs and writes them to a swizzled K-contiguous LDS tile.
+// -1 rows read as zero through the buffer range).  The loads are
+// non-temporal: a decode step reads each weight row once, and a load that
+// does not allocate in the caches neither evicts other data nor has to wait
+// for the dirty lines an allocation would evict to be written back.  Each
+// thread converts int8 to bf16 (exact: |q| <= 128 needs 8 significant bits),
+// transposes its block in registers into K-runs and writes them to a
+// swizzled K-contiguous LDS tile.
 // Waves then multiply with v_mfma_f32_32x32x16_bf16: the packed A_I rows are
 // the first operand (read straight from global memory, rows >= m read zero),
 // the B^T fragments the second, so each lane ends with one output column and
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
     for (int r = 0; r < RPT; ++r) {
       const int32_t s = sidx[q * kBK + bkb * RPT + r];
       const uint32_t off = s >= 0 ? (uint32_t)(((int64_t)s * g.ldb) * E + bnb * 16) : mg::kOOB;
-      rb[slot][r] = mg::bload16(rb_r, off);
+      rb[slot][r] = mg::bload16<mg::kNonTemporal>(rb_r, off);
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -286,9 +290,11 @@ struct SkinnyPlan {
   int tiles_n, splits, tiles_per_split;
 };
 
-// Workgroups per CU the grid aims at: about one resident round (LDS allows
-// 3 bf16 or 2 int8 workgroups per CU), so each workgroup streams a long run
-// of K-tiles instead of paying the pipeline fill many times.
+// Workgroups per CU the grid aims at: about one resident round, so each
+// workgroup streams a long run of K-tiles instead of paying the pipeline fill
+// many times.  Registers hold the bf16 kernel to 3 resident workgroups per CU
+// and LDS the int8 kernel to 2; aiming at 3 or 4 bf16 workgroups per CU
+// measures the same.
 constexpr int kWgBf16 = 4, kWgW8 = 2;
 
 SkinnyPlan skinny_plan(bool w8, int64_t n, int64_t k_pad) {
