@@ -15,8 +15,9 @@
 // XOR-swizzled by the row; since one direct load writes 64 consecutive
 // 16-byte LDS chunks, each lane fetches the global chunk that the swizzle maps
 // onto its LDS slot.  The MFMA takes the B fragment as its first operand so
-// each lane ends up with four consecutive output columns of one row, which the
-// epilogue writes straight from registers with 8-byte buffer stores.
+// each lane ends up with four consecutive output columns of one row.  The
+// epilogue passes the tile through the remaining 32 KiB of LDS, 64 rows at a
+// time, and writes whole 512-byte rows with 16-byte stores.
 #include "mfma_gemm.h"
 #include "rmm_internal.h"
 #include "timing.h"
@@ -119,10 +120,19 @@ constexpr int vm_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14);
 // 256 x 256 x 64 tiles, two LDS stages, persistent: one workgroup per CU
 // walks its XCD's tile range.  After the last K-step's barrier (every wave is
 // done reading LDS) it issues the first two K-tiles of its next output tile,
-// and only then converts and stores the finished accumulators straight from
-// registers, so the next tile's loads fly while the epilogue runs and the
-// pipeline never drains between tiles.  The stores come after those loads in
-// issue order, so waiting for the loads does not wait for them.
+// and only then converts and stores the finished accumulators, so the next
+// tile's loads fly while the epilogue runs and the pipeline never drains
+// between tiles.  The stores come after those loads in issue order, so
+// waiting for the loads does not wait for them.
+//
+// Epilogue.  Straight from the accumulators, one store instruction would put
+// 16 bytes into each of 32 rows: every CU finishing a tile at about the same
+// time then sends millions of small writes to L2, and the next tile's second
+// K-step waits behind them (about 10 us per round of tiles).  Instead, for
+// each of the four 32-row groups of every wave, the eight waves write their
+// 32 x 64 pieces (rows of both 128-row slabs) into a 64 x 256 staging area in
+// the LDS left over by the operand stages, and the workgroup writes the area
+// out as whole 512-byte rows: 16 stores per wave, each covering two rows.
 //
 // Register budget: the accumulators take half the register file, so the rest
 // must hold only fragments and a few addresses.  The LDS fragment addresses
@@ -147,7 +157,8 @@ __global__ __launch_bounds__(128 * WGN) __attribute__((amdgpu_waves_per_eu(WGN /
   constexpr int TILE = 256 * BK * 2;                 // one operand tile, 32 KiB
   constexpr int LPW = 32 / NWAVE;                    // direct loads per wave per operand
   constexpr int KS = BK / 16;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * NST * TILE];   // [A0 | A1 | B0 | B1]
+  constexpr int EPI = 64 * BN * 2;                   // epilogue staging: 64 rows of the tile
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * NST * TILE + EPI];   // [A0 | A1 | B0 | B1 | E]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
@@ -241,12 +252,12 @@ __global__ __launch_bounds__(128 * WGN) __attribute__((amdgpu_waves_per_eu(WGN /
   Ctx cur = ctx_of(w);
   prologue(cur);
   // Stores this wave issued after the current tile's first two K-tiles (the
-  // previous tile's epilogue): kStores when it took the buffer-store path,
-  // else the waits below count none.  vmcnt holds at most 63.
-  constexpr int kStores = TI * TJ * 4;
-  constexpr int kAfter0 = 2 * LPW + kStores > 63 ? 63 : 2 * LPW + kStores;
-  constexpr int kAfter1 = kStores > 63 ? 63 : kStores;
-  bool had_stores = false;
+  // previous tile's epilogue): kStLds on the staged path, kStReg on the
+  // register path of a partial column tile; on the element path the waits
+  // below count none.  vmcnt holds at most 63.
+  constexpr int kStLds = 4 * TI, kStReg = TI * TJ * 4;
+  static_assert(2 * LPW + kStReg <= 63, "store count exceeds vmcnt");
+  int nstores = 0;
   for (;;) {
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -257,10 +268,12 @@ __global__ __launch_bounds__(128 * WGN) __attribute__((amdgpu_waves_per_eu(WGN /
     // K-tile 0 landed: K-tile 1 (if any) and then the previous tile's stores
     // were issued after it.
     if (nk > 1) {
-      if (had_stores) __builtin_amdgcn_s_waitcnt(vm_imm(kAfter0));
+      if (nstores == kStLds) __builtin_amdgcn_s_waitcnt(vm_imm(2 * LPW + kStLds));
+      else if (nstores == kStReg) __builtin_amdgcn_s_waitcnt(vm_imm(2 * LPW + kStReg));
       else __builtin_amdgcn_s_waitcnt(vm_imm(2 * LPW));
     } else {
-      if (had_stores) __builtin_amdgcn_s_waitcnt(vm_imm(kAfter1));
+      if (nstores == kStLds) __builtin_amdgcn_s_waitcnt(vm_imm(kStLds));
+      else if (nstores == kStReg) __builtin_amdgcn_s_waitcnt(vm_imm(kStReg));
       else __builtin_amdgcn_s_waitcnt(vm_imm(0));
     }
     // A bare barrier: every wave's part of K-tile 0 is in LDS.  (__syncthreads
@@ -285,7 +298,8 @@ __global__ __launch_bounds__(128 * WGN) __attribute__((amdgpu_waves_per_eu(WGN /
       if constexpr (!LAST) {
         // K-tile kt+1 landed.  On the first step only the previous tile's
         // stores can follow it.
-        if (kt == 0 && had_stores) __builtin_amdgcn_s_waitcnt(vm_imm(kAfter1));
+        if (kt == 0 && nstores == kStLds) __builtin_amdgcn_s_waitcnt(vm_imm(kStLds));
+        else if (kt == 0 && nstores == kStReg) __builtin_amdgcn_s_waitcnt(vm_imm(kStReg));
         else __builtin_amdgcn_s_waitcnt(vm_imm(0));
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this tile's fragment reads are done
@@ -348,20 +362,91 @@ __global__ __launch_bounds__(128 * WGN) __attribute__((amdgpu_waves_per_eu(WGN /
       }
     }
 
-    // Epilogue from registers: lane l of acc[j][i] holds four consecutive
-    // columns j*32 + 8*(r/4) + 4*(l/32) of row i*32 + l%32.  Full tiles use
-    // buffer stores: one lane offset, the column step in the immediate and
-    // the 32-row step in the scalar offset; rows past m fall outside the
-    // resource and are dropped.
+    // Epilogue: lane l of acc[j][i] holds four consecutive columns
+    // j*32 + 8*(r/4) + 4*(l/32) of row i*32 + l%32 of the wave's 128-row slab.
     const int64_t rbase = dm0 + wm * 128, cbase = dn0 + wn * WTN;
-    const bool vec = (g.ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(g.Y) % 8 == 0) && cbase + WTN <= g.n;
     // Opaque copies of the lane's row and half: keeps the per-store address
     // arithmetic below inside the loop (folded into immediate offsets)
     // instead of 64 hoisted registers.
     int er = lrow, ek = lk;
     asm volatile("" : "+v"(er), "+v"(ek));
-    had_stores = false;
-    if (vec) {
+    nstores = 0;
+    // Staged path, for tiles whose 256 columns all lie inside Y (the same
+    // for every wave of the workgroup, which meets at the barriers below).
+    // Staging row s = 32 wm + l%32 holds row wm*128 + i*32 + l%32 of the
+    // tile; its 16-byte chunk c sits at slot c ^ (s % 32), so the 32 rows a
+    // write instruction touches and the 32 chunks of a row a read touches
+    // spread over the banks.  Rows past m fall outside the store resource
+    // and are dropped.
+    const bool staged = dn0 + BN <= g.n && g.ldy % 8 == 0 && reinterpret_cast<uintptr_t>(g.Y) % 16 == 0 &&
+                        (uint64_t)BM * g.ldy * 2 < mg::kMaxRecords;
+    // Register path (partial column tiles): 8-byte buffer stores, one lane
+    // offset, the column step in the immediate and the 32-row step in the
+    // scalar offset.
+    const bool vec = (g.ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(g.Y) % 8 == 0) && cbase + WTN <= g.n &&
+                     (uint64_t)128 * g.ldy * 2 < mg::kMaxRecords;
+    if (staged) {
+      typedef int v4i __attribute__((ext_vector_type(4)));
+      unsigned char *E = smem + 2 * NST * TILE;
+      const int64_t rows_valid = g.m - dm0 < BM ? g.m - dm0 : BM;
+      const rsrc_t ry = mg::make_rsrc(g.Y + dm0 * g.ldy + dn0, (uint64_t)((rows_valid - 1) * g.ldy + BN) * 2);
+      // LDS byte addresses of the staging area.  Its writes and reads are
+      // issued from assembly: the compiler cannot tell them apart from the
+      // next tile's direct loads into the operand stages (still in flight)
+      // and would otherwise wait for those loads first.  The writes are
+      // complete at the lgkmcnt(0) before the barrier; the reads wait for
+      // their data inside the same assembly block.
+      const uint32_t ebase = (uint32_t)(uintptr_t)(LDS_AS unsigned char *)E;
+      const uint32_t wrow = ebase + (uint32_t)((wm * 32 + er) * (BN * 2));
+      constexpr int RQ = 64 * BN / 8 / (64 * NWAVE);   // 16-byte chunks each thread copies out per row group
+      static_assert(RQ == 4, "the read-out below issues four reads");
+      uint32_t raddr[RQ];
+      int rtrow[RQ], rch[RQ];
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) {
+        const int c = tid + 64 * NWAVE * q;
+        const int sr = c / (BN / 8), ch = c % (BN / 8);
+        raddr[q] = ebase + (uint32_t)(sr * (BN * 2) + ((ch ^ (sr & 31)) << 4));
+        rtrow[q] = (sr >> 5) * 128 + (sr & 31);
+        rch[q] = ch;
+      }
+      typedef unsigned v2u __attribute__((ext_vector_type(2)));
+      typedef unsigned v4u __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const uint32_t lo = pack_bf16x2(acc[j][i][4 * gq + 0], acc[j][i][4 * gq + 1]);
+            const uint32_t hi = pack_bf16x2(acc[j][i][4 * gq + 2], acc[j][i][4 * gq + 3]);
+            const int c = wn * (WTN / 8) + j * 4 + gq;
+            const uint32_t a = wrow + (uint32_t)((c ^ er) << 4) + 8u * (uint32_t)ek;
+            asm volatile("ds_write_b64 %0, %1" : : "v"(a), "v"(v2u{lo, hi}) : "memory");
+          }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's part is in LDS
+        __builtin_amdgcn_s_barrier();
+        v4u v[RQ];
+        asm volatile(
+            "ds_read_b128 %0, %4\n\t"
+            "ds_read_b128 %1, %5\n\t"
+            "ds_read_b128 %2, %6\n\t"
+            "ds_read_b128 %3, %7\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+            : "v"(raddr[0]), "v"(raddr[1]), "v"(raddr[2]), "v"(raddr[3])
+            : "memory");
+#pragma unroll
+        for (int q = 0; q < RQ; ++q) {
+          const int trow = rtrow[q] + i * 32;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v[q]), ry,
+                                                 (int)(((int64_t)trow * g.ldy + rch[q] * 8) * 2), 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // this wave's reads of the area are done
+        __builtin_amdgcn_s_barrier();
+      }
+      nstores = kStLds;
+    } else if (vec) {
       const int64_t rows_left = g.m - rbase;
       if (rows_left > 0) {
         const rsrc_t ry = mg::make_rsrc(g.Y + rbase * g.ldy + cbase,
@@ -382,7 +467,7 @@ __global__ __launch_bounds__(128 * WGN) __attribute__((amdgpu_waves_per_eu(WGN /
             }
             __builtin_amdgcn_sched_barrier(0);
           }
-        had_stores = true;
+        nstores = kStReg;
       }
     } else {
 #pragma unroll
