@@ -293,6 +293,47 @@ __global__ __launch_bounds__(256) void mfma_gemm(Args g) {
   // D of a 32x32 tile: lane l holds column l%32; register r holds row
   // 8*(r/4) + 4*(l/32) + r%4.
   OUT *Y = static_cast<OUT *>(g.Y) + b * g.y_bs;
+  if constexpr (std::is_same<OUT, uint16_t>::value) {
+    // bf16 tiles whose columns all lie inside Y go out through LDS (free
+    // after the loop's last barrier) as 16-byte row segments, PR rows per
+    // pass; stored from the accumulators, every instruction would write 64
+    // bytes into each of two rows.  Chunk c of staged row r sits at slot
+    // c ^ (r % CPR): the two rows one write instruction touches differ in
+    // bit 2 of r and so land on different banks.
+    constexpr int CPR = BN / 8;                        // 16-byte chunks per row
+    constexpr int PR = STAGES * BM * kBK / BN;         // rows per pass
+    static_assert(PR == WTM || PR == BM, "a pass holds one or both wave rows of the tile");
+    if (n0 + BN <= g.n && g.ldy % 8 == 0 && reinterpret_cast<uintptr_t>(Y) % 16 == 0) {
+      uint16_t *E = &As[0][0];
+#pragma unroll
+      for (int p = 0; p < BM / PR; ++p) {
+        if (PR == BM || wm == p) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              const int col = wn * WTN + j * 32 + lrow;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int row = (PR == BM ? wm * WTM : 0) + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
+                E[row * BN + (((col >> 3) ^ (row % CPR)) << 3) + (col & 7)] = f32_to_bf16(acc[i][j][r]);
+              }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < PR * CPR / 256; ++q) {
+          const int c = tid + 256 * q;
+          const int row = c / CPR, ch = c % CPR;
+          const int64_t grow = m0 + p * PR + row;
+          const uint4 v = *reinterpret_cast<const uint4 *>(&E[row * BN + ((ch ^ (row % CPR)) << 3)]);
+          if (grow < g.m) *reinterpret_cast<uint4 *>(Y + grow * g.ldy + n0 + ch * 8) = v;
+        }
+        if (p + 1 < BM / PR) __syncthreads();
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
