@@ -145,6 +145,33 @@ def test_gemm_bf16_unsorted_and_invalid_indices_and_strides():
     assert torch.all(Yfull[:, n:] == 0)           # nothing written past n
 
 
+# Persistent 256 x 256 GEMM (m >= 1024, >= 192 tiles): ragged last row tile, a
+# last column tile narrower than 256 next to full ones, and Y a view into a
+# larger buffer.  Full column tiles leave through the LDS-staged epilogue (rows
+# past m dropped by the store resource), the partial one through the register
+# and per-element paths; nothing outside the view may change.
+@pytest.mark.parametrize("m,d,n,k,pad", [(3000, 1000, 4096, 500, 0), (2100, 800, 6152, 400, 8),
+                                         (1500, 640, 8192, 320, 24), (1030, 512, 49408, 256, 16)])
+def test_gemm_persistent_epilogue_paths(m, d, n, k, pad):
+    rng = np.random.default_rng(m + n + pad)
+    A = _acts(m, d, m + 3)
+    B = synth.weight(synth.stream(1, 91, n + d), d, n)
+    I = np.sort(rng.choice(d, size=k, replace=False)).astype(np.int32)
+    sentinel = 7.0
+    Ybig = torch.full((m + 3, n + pad), sentinel, dtype=BF, device=DEV)
+    R.rmm_gemm(dev_tensor(A, BF), dev_tensor(B, BF), dev_tensor(I, torch.int32), k, out=Ybig[:m, :n])
+    got = Ybig.float().cpu().numpy()
+    assert np.all(got[m:] == sentinel), "rows past m were written"
+    assert np.all(got[:, n:] == sentinel), "columns past n were written"
+    # every row of the ragged last row tile, plus rows spread over the others
+    rows = np.unique(np.concatenate([np.arange((m - 1) // 256 * 256, m), rng.choice(m, size=200, replace=False)]))
+    want = oracle.reduced_product(A[rows], B, I)
+    assert rel_fro(got[rows, :n], want) < TOL_BF16
+    # the last (narrow) column tile on its own, where the paths differ
+    c0 = (n - 1) // 256 * 256
+    assert rel_fro(got[rows, c0:n], want[:, c0:]) < TOL_BF16
+
+
 @pytest.mark.parametrize("m,d,n,k", [(64, 512, 512, 256), (1, 8, 3, 2), (65, 130, 70, 100), (200, 1024, 333, 1024)])
 def test_gemm_f32(m, d, n, k):
     rng = np.random.default_rng(m * n)
