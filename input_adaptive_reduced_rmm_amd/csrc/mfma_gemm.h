@@ -20,6 +20,8 @@
 // MFMA operand reads spread over the banks.
 #pragma once
 
+#include <type_traits>
+
 #include "rmm_internal.h"
 
 namespace rmm {
