@@ -19,10 +19,13 @@
 // thread converts int8 to bf16 (exact: |q| <= 128 needs 8 significant bits),
 // transposes its block in registers into K-runs and writes them to a
 // swizzled K-contiguous LDS tile.
-// Waves then multiply with v_mfma_f32_32x32x16_bf16: the packed A_I rows are
-// the first operand (read straight from global memory, rows >= m read zero),
-// the B^T fragments the second, so each lane ends with one output column and
-// 16 rows.  The int8 column scale multiplies the fp32 sum once, at the end.
+// The packed A_I rows of the K-tile (32 rows, rows >= m read zero) go into
+// the same LDS stage, one 16-byte chunk per thread: the register slots then
+// hold almost only weight bytes, which lets more K-tiles be in flight.
+// Waves multiply with v_mfma_f32_32x32x16_bf16: A_I fragments are the first
+// operand, the B^T fragments the second, so each lane ends with one output
+// column and 16 rows.  The int8 column scale multiplies the fp32 sum once, at
+// the end.
 #include <type_traits>
 
 #include "mfma_gemm.h"
@@ -75,7 +78,7 @@ __device__ __forceinline__ uint32_t i8_to_bf16_bits(uint32_t w, int byte) {
 }
 
 constexpr int kW8BN = 256;
-constexpr int kPdBf16 = 2, kPdW8 = 4;
+constexpr int kPdBf16 = 4, kPdW8 = 4;
 
 template <bool W8>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
@@ -86,6 +89,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
   constexpr int RPT = kBK * NBT / 256;     // rows per thread per K-tile
   static_assert(RPT == 4 || (W8 && RPT == 2), "loader assumes 4 rows per thread (2 for a narrow int8 panel)");
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][32 * kBK];
   __shared__ int32_t sidx[kMaxTilesPerSplit * kBK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -107,11 +111,12 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
 
   const int bnb = tid % NBT, bkb = tid / NBT;   // chunk column, row group (rows RPT*bkb..)
   const int lrow = lane & 31, lk = lane >> 5;
+  const int arow = tid >> 3, achk = tid & 7;    // this thread's A_I chunk of a K-tile
   // PD register slots: the loads of the next PD K-tiles are in flight while
   // the current one is multiplied from LDS (at this few rows the kernel is
   // bound by how many bytes each CU keeps in flight).
   constexpr int PD = W8 ? kPdW8 : kPdBf16;
-  uint4 rb[PD][RPT], ra[PD][4];
+  uint4 rb[PD][RPT], ra[PD];
 
   auto issue = [&](int slot, int q) {   // q: tile index within the split
 #pragma unroll
@@ -120,14 +125,12 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
       const uint32_t off = s >= 0 ? (uint32_t)(((int64_t)s * g.ldb) * E + bnb * 16) : mg::kOOB;
       rb[slot][r] = mg::bload16<mg::kNonTemporal>(rb_r, off);
     }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      ra[slot][ks] =
-          mg::bload16(ra_r, (uint32_t)(((int64_t)lrow * g.k_pad + (int64_t)(q0 + q) * kBK + ks * 16 + 8 * lk) * 2));
+    ra[slot] = mg::bload16(ra_r, (uint32_t)(((int64_t)arow * g.k_pad + (int64_t)(q0 + q) * kBK + achk * 8) * 2));
   };
 
   // Registers of one K-tile -> K-contiguous LDS stage `buf`.
   auto store = [&](int slot, int buf) {
+    *reinterpret_cast<uint4 *>(&As[buf][mg::swz(arow, achk)]) = ra[slot];
     // rows RPT*bkb .. RPT*bkb+RPT-1 -> K-chunk kc, elements half .. half+RPT-1
     const int kc = (RPT * bkb) >> 3, half = (RPT * bkb) & 7;
     if constexpr (!W8) {
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
 
-  constexpr int LOADS = RPT + 4;   // vector loads per issue
+  constexpr int LOADS = RPT + 1;   // vector loads per issue
   // Wait until at most n issues (n * LOADS loads) are outstanding.
   auto wait_issues = [&](int n) __attribute__((always_inline)) {
     switch (n) {
@@ -183,19 +186,18 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
     }
   };
   static_assert(PD >= 2 && PD <= 7 && 6 * LOADS <= 63, "prefetch depth");
-  // One K-tile q: LDS stage q&1 holds it, slot S = q % PD its A fragments;
-  // tiles q+1 .. q+PD-1 are in flight.  Refill slot S with tile q + PD,
-  // multiply, then convert tile q + 1 into the other stage.
+  // One K-tile q: LDS stage q&1 holds it (A_I and B), and slot S = q % PD,
+  // whose registers it came from, is free; tiles q+1 .. q+PD-1 are in flight.
+  // Refill slot S with tile q + PD, multiply, then convert tile q + 1 into
+  // the other stage.
   auto step = [&](auto s_c, int q) __attribute__((always_inline)) {
     constexpr int S = decltype(s_c)::value, SN = (S + 1) % PD;
     const int buf = q & 1;
-    uint4 af[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) af[ks] = ra[S][ks];
     if (q + PD < ntile) issue(S, q + PD);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8_t a8 = __builtin_bit_cast(bf16x8_t, af[ks]);
+      const bf16x8_t a8 = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4 *>(&As[buf][mg::swz(lrow, ks * 2 + lk)]));
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const bf16x8_t b8 = __builtin_bit_cast(
