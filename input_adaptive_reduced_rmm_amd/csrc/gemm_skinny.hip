@@ -5,8 +5,9 @@
 //
 // At m <= 32 the product is bound by reading the kept rows of B (k x n
 // elements) once; the flops are small.  The kernel therefore spreads those
-// rows over many workgroups: a workgroup owns a 128-column (bf16) or
-// 256-column (int8) panel and a contiguous range of K-tiles (split over K),
+// rows over many workgroups: a workgroup owns a 128-column panel (bf16 or
+// int8; a 256-column int8 panel ran 17-23 % slower on the largest 70B decode
+// product) and a contiguous range of K-tiles (split over K),
 // and writes fp32 partial sums that a second kernel adds in a fixed order
 // (deterministic).  With a single split the first kernel writes Y directly.
 //
@@ -77,7 +78,7 @@ __device__ __forceinline__ uint32_t i8_to_bf16_bits(uint32_t w, int byte) {
   return __float_as_uint((float)v) >> 16;
 }
 
-constexpr int kW8BN = 256;
+constexpr int kW8BN = 128;
 constexpr int kPdBf16 = 4, kPdW8 = 4;
 
 template <bool W8>
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
   constexpr int CPC = W8 ? 16 : 8;         // columns per 16-byte chunk
   constexpr int NBT = BN / CPC;            // threads across the panel
   constexpr int RPT = kBK * NBT / 256;     // rows per thread per K-tile
-  static_assert(RPT == 4 || (W8 && RPT == 2), "loader assumes 4 rows per thread (2 for a narrow int8 panel)");
+  static_assert(RPT == (W8 ? 2 : 4), "loader assumes 4 bf16 or 2 int8 rows per thread");
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t As[2][32 * kBK];
   __shared__ int32_t sidx[kMaxTilesPerSplit * kBK];
@@ -143,17 +144,6 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs g) {
         const int n_ev = bnb * CPC + 2 * q;
         *reinterpret_cast<uint2 *>(&Bs[buf][mg::swz(n_ev, kc) + half]) = ev;
         *reinterpret_cast<uint2 *>(&Bs[buf][mg::swz(n_ev + 1, kc) + half]) = od;
-      }
-    } else if constexpr (RPT == 4) {
-#pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const int q = c >> 2, byte = c & 3;
-        const uint32_t b0 = i8_to_bf16_bits(mg::u4get(rb[slot][0], q), byte);
-        const uint32_t b1 = i8_to_bf16_bits(mg::u4get(rb[slot][1], q), byte);
-        const uint32_t b2 = i8_to_bf16_bits(mg::u4get(rb[slot][2], q), byte);
-        const uint32_t b3 = i8_to_bf16_bits(mg::u4get(rb[slot][3], q), byte);
-        *reinterpret_cast<uint2 *>(&Bs[buf][mg::swz(bnb * CPC + c, kc) + half]) =
-            make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
       }
     } else {
 #pragma unroll
@@ -294,10 +284,10 @@ struct SkinnyPlan {
 
 // Workgroups per CU the grid aims at: about one resident round, so each
 // workgroup streams a long run of K-tiles instead of paying the pipeline fill
-// many times.  Registers hold the bf16 kernel to 3 resident workgroups per CU
-// and LDS the int8 kernel to 2; aiming at 3 or 4 bf16 workgroups per CU
-// measures the same.
-constexpr int kWgBf16 = 4, kWgW8 = 2;
+// many times.  LDS (two 16 KiB weight stages, two 4 KiB A_I stages and the
+// index list) holds both kernels to 3 resident workgroups per CU; aiming at 3
+// or 4 bf16 workgroups per CU measures the same.
+constexpr int kWgBf16 = 4, kWgW8 = 3;
 
 SkinnyPlan skinny_plan(bool w8, int64_t n, int64_t k_pad) {
   const int64_t bn = w8 ? kW8BN : 128;
