@@ -40,7 +40,7 @@ namespace {
 constexpr int kDB = 256;   // keys (or kept tokens) per workgroup pass, one per thread
 constexpr int kTokSub = 1;   // 256-token sub-tiles per output workgroup
 constexpr int kSelThreads = 1024;   // token selection workgroup
-constexpr int kSelKeys = 32768;     // token scores held in LDS by the selection (128 KiB)
+constexpr int kSelKeys = 32768;     // most token scores the selection holds in LDS (128 KiB)
 constexpr float kNegInfD = -__builtin_inff();
 
 __device__ __forceinline__ float dexp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -360,11 +360,13 @@ __global__ __launch_bounds__(kDB) void dec_tok_kernel(DecArgs g) {
 // scores), every score computed once, parked in LDS as an order-preserving
 // key and, when asked, written to tok; then sel::block_select keeps the row's
 // kt highest (ties to the lower index) into J.  Keys past the row's context
-// score -inf and are never kept (kt <= the row's context).
+// score -inf and are never kept (kt <= the row's context), so the select runs
+// over the row's own context only.  The keys take Lk x 4 bytes of dynamic
+// LDS: two workgroups share a CU while Lk <= 16384.
 template <int LQ>
 __global__ __launch_bounds__(kSelThreads) void dec_tok_select_kernel(DecArgs g) {
   constexpr int NW = kSelThreads / 64;
-  __shared__ __attribute__((aligned(16))) uint32_t keys[kSelKeys];
+  extern __shared__ __attribute__((aligned(16))) uint32_t keys[];
   __shared__ sel::BlockShared<kSelThreads> sh;
   __shared__ float red[NW * LQ];
   const int tid = threadIdx.x;
@@ -434,8 +436,13 @@ __global__ __launch_bounds__(kSelThreads) void dec_tok_select_kernel(DecArgs g) 
         const uint4 key = make_uint4(sel::score_key(sc[0]), sel::score_key(sc[1]), sel::score_key(sc[2]),
                                      sel::score_key(sc[3]));
         *reinterpret_cast<uint4 *>(&keys[4 * t]) = key;
-        kor |= key.x | key.y | key.z | key.w;
-        kand &= key.x & key.y & key.z & key.w;
+        const uint32_t kk[4] = {key.x, key.y, key.z, key.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * t + e < sr.Lk) {
+            kor |= kk[e];
+            kand &= kk[e];
+          }
       }
     }
   } else {
@@ -458,8 +465,10 @@ __global__ __launch_bounds__(kSelThreads) void dec_tok_select_kernel(DecArgs g) 
         if (g.tok) g.tok[h * g.Lk + j] = t;
         const uint32_t key = sel::score_key(t);
         keys[j] = key;
-        kor |= key;
-        kand &= key;
+        if (j < sr.Lk) {
+          kor |= key;
+          kand &= key;
+        }
       }
     }
   }
@@ -467,7 +476,7 @@ __global__ __launch_bounds__(kSelThreads) void dec_tok_select_kernel(DecArgs g) 
     for (int64_t t = tid; t < g.kt_pad; t += kSelThreads) g.Jw[h * g.kt_pad + t] = t < sr.kt ? (int32_t)t : -1;
     return;
   }
-  sel::block_select<kSelThreads>([&](int64_t j) -> uint32_t { return keys[j]; }, g.Lk, kor, kand, sr.kt,
+  sel::block_select<kSelThreads>([&](int64_t j) -> uint32_t { return keys[j]; }, sr.Lk, kor, kand, sr.kt,
                                  g.kt_pad, g.Jw + h * g.kt_pad, sh);
 }
 
@@ -699,12 +708,13 @@ hipError_t launch_attn_decode(int pass, const AttnDecodeDesc &d, hipStream_t st)
     // token scores and selection in one launch (attn_decode_select_fused)
     if (d.Lk > kSelKeys) return hipErrorInvalidValue;
     KernelTimer timer("dec_tok_select", st);
+    const unsigned kb = (unsigned)((d.Lk * 4 + 15) / 16 * 16);   // the row keys in LDS
     switch (lq) {
-      case 1: hipLaunchKernelGGL(dec_tok_select_kernel<1>, dim3((unsigned)g.nrows), dim3(kSelThreads), 0, st, g); break;
-      case 2: hipLaunchKernelGGL(dec_tok_select_kernel<2>, dim3((unsigned)g.nrows), dim3(kSelThreads), 0, st, g); break;
-      case 4: hipLaunchKernelGGL(dec_tok_select_kernel<4>, dim3((unsigned)g.nrows), dim3(kSelThreads), 0, st, g); break;
-      case 8: hipLaunchKernelGGL(dec_tok_select_kernel<8>, dim3((unsigned)g.nrows), dim3(kSelThreads), 0, st, g); break;
-      default: hipLaunchKernelGGL(dec_tok_select_kernel<16>, dim3((unsigned)g.nrows), dim3(kSelThreads), 0, st, g); break;
+      case 1: hipLaunchKernelGGL(dec_tok_select_kernel<1>, dim3((unsigned)g.nrows), dim3(kSelThreads), kb, st, g); break;
+      case 2: hipLaunchKernelGGL(dec_tok_select_kernel<2>, dim3((unsigned)g.nrows), dim3(kSelThreads), kb, st, g); break;
+      case 4: hipLaunchKernelGGL(dec_tok_select_kernel<4>, dim3((unsigned)g.nrows), dim3(kSelThreads), kb, st, g); break;
+      case 8: hipLaunchKernelGGL(dec_tok_select_kernel<8>, dim3((unsigned)g.nrows), dim3(kSelThreads), kb, st, g); break;
+      default: hipLaunchKernelGGL(dec_tok_select_kernel<16>, dim3((unsigned)g.nrows), dim3(kSelThreads), kb, st, g); break;
     }
   } else if (pass == 2) {
     KernelTimer timer("dec_out", st);
