@@ -196,78 +196,102 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------- f32 path
-constexpr int kFBM = 64, kFBN = 64, kFBK = 16;
+// TB x TB output tiles (64, or 32 when 64 x 64 tiles would leave most CUs
+// idle: fp32 MFMA runs at a sixteenth of the bf16 rate, so a small product
+// needs the whole chip), 64-deep K-steps: each step's A and B values are
+// loaded into registers while the previous step is multiplied from LDS, so
+// a product of a few K-steps pays about one memory latency instead of one
+// per step.  Four waves of (TB/2) x (TB/2), v_mfma_f32_16x16x4f32.
+constexpr int kFBK = 64;
 
+template <int TB>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
-  __shared__ float As[kFBM][kFBK + 1];
-  __shared__ float Bs[kFBK][kFBN];
+  constexpr int TW = TB / 32;            // 16 x 16 MFMA tiles per wave side
+  constexpr int TPA = 256 / TB;          // threads per A row
+  constexpr int FA = kFBK / TPA;         // A values per thread and step (multiple of 4)
+  constexpr int FB = TB / 4;             // B values per thread and step (4 threads per kept row)
+  static_assert(FA % 4 == 0 && (TB == 32 || TB == 64), "tile");
+  __shared__ float As[TB][kFBK + 1];     // row pitch 65: the 16 rows of a fragment read hit distinct banks
+  __shared__ float Bs[kFBK][TB + 4];     // row pitch TB + 4: the 4 rows of a fragment read hit distinct banks
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t tiles_n = (g.n + kFBN - 1) / kFBN;
-  const int64_t m0 = (blockIdx.x / tiles_n) * kFBM, n0 = (blockIdx.x % tiles_n) * kFBN;
+  const int64_t tiles_n = (g.n + TB - 1) / TB;
+  const int64_t m0 = (blockIdx.x / tiles_n) * TB, n0 = (blockIdx.x % tiles_n) * TB;
   const int64_t b = blockIdx.z;
   const float *A = static_cast<const float *>(g.A) + b * g.m * g.k_pad;
   const int32_t *idx = g.idx + b * g.idx_stride;
   const float *B = static_cast<const float *>(g.B) + ((b * g.hkv) / g.hq) * g.b_batch_stride;
   float *Y = static_cast<float *>(g.Y) + b * g.y_batch_stride;
 
-  f32x4_t acc[2][2];
+  f32x4_t acc[TW][TW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TW; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int ar = tid >> 2, akc = (tid & 3) * 4;   // A: 64 rows x 4 float4
-  const int br = tid >> 4, bc = (tid & 15) * 4;   // B: 16 rows x 16 float4
-  for (int64_t k0 = 0; k0 < g.k_pad; k0 += kFBK) {
-    {
-      const int64_t gr = m0 + ar;
-      float4 v = gr < g.m ? *reinterpret_cast<const float4 *>(A + gr * g.k_pad + k0 + akc)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-      As[ar][akc + 0] = v.x;
-      As[ar][akc + 1] = v.y;
-      As[ar][akc + 2] = v.z;
-      As[ar][akc + 3] = v.w;
-    }
-    {
-      const int64_t t = k0 + br;
-      int64_t src = -1;
-      if (t < g.k) {
-        const int32_t v = idx[t];
-        src = (v >= 0 && v < g.d) ? v : -1;
-      }
+  // Per thread and K-step: FA consecutive K values of A row ar, and FB
+  // consecutive columns of kept row br of B.
+  const int ar = tid / TPA, ac = (tid % TPA) * FA;
+  const int br = tid >> 2, bc = (tid & 3) * FB;
+  float4 ra[FA / 4];
+  float rb[FB];
+  auto load = [&](int64_t k0) {
+    const int64_t gr = m0 + ar;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t col = n0 + bc + q;
-        Bs[br][bc + q] = (src >= 0 && col < g.n) ? B[src * g.ldb + col] : 0.f;
-      }
+    for (int q = 0; q < FA / 4; ++q)
+      ra[q] = gr < g.m ? *reinterpret_cast<const float4 *>(A + gr * g.k_pad + k0 + ac + 4 * q)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int64_t t = k0 + br;
+    int64_t src = -1;
+    if (t < g.k) {
+      const int32_t v = idx[t];
+      src = (v >= 0 && v < g.d) ? v : -1;
     }
+#pragma unroll
+    for (int q = 0; q < FB; ++q) {
+      const int64_t col = n0 + bc + q;
+      rb[q] = (src >= 0 && col < g.n) ? B[src * g.ldb + col] : 0.f;
+    }
+  };
+
+  load(0);
+  for (int64_t k0 = 0; k0 < g.k_pad; k0 += kFBK) {
+#pragma unroll
+    for (int q = 0; q < FA / 4; ++q) {
+      As[ar][ac + 4 * q + 0] = ra[q].x;
+      As[ar][ac + 4 * q + 1] = ra[q].y;
+      As[ar][ac + 4 * q + 2] = ra[q].z;
+      As[ar][ac + 4 * q + 3] = ra[q].w;
+    }
+#pragma unroll
+    for (int q = 0; q < FB; ++q) Bs[br][bc + q] = rb[q];
     __syncthreads();
+    if (k0 + kFBK < g.k_pad) load(k0 + kFBK);   // next step's loads fly during this product
 #pragma unroll
     for (int kk = 0; kk < kFBK; kk += 4) {
-      float av[2], bv[2];
+      float av[TW], bv[TW];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) av[i] = As[wm * 32 + i * 16 + (lane & 15)][kk + (lane >> 4)];
+      for (int i = 0; i < TW; ++i) av[i] = As[wm * (TB / 2) + i * 16 + (lane & 15)][kk + (lane >> 4)];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bv[j] = Bs[kk + (lane >> 4)][wn * 32 + j * 16 + (lane & 15)];
+      for (int j = 0; j < TW; ++j) bv[j] = Bs[kk + (lane >> 4)][wn * (TB / 2) + j * 16 + (lane & 15)];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TW; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TW; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
   }
   // D of a 16x16 tile: lane l holds column l%16, register r holds row 4*(l/16) + r.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TW; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wn * 32 + j * 16 + (lane & 15);
+    for (int j = 0; j < TW; ++j) {
+      const int64_t col = n0 + wn * (TB / 2) + j * 16 + (lane & 15);
       if (col >= g.n) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t row = m0 + wm * 32 + i * 16 + 4 * (lane >> 4) + r;
+        const int64_t row = m0 + wm * (TB / 2) + i * 16 + 4 * (lane >> 4) + r;
         if (row < g.m) Y[row * g.ldy + col] = acc[i][j][r];
       }
     }
@@ -352,10 +376,15 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, OutType out, hipStream_t st) {
 }
 
 hipError_t launch_gemm_f32(const GemmArgs &g, hipStream_t st) {
-  const int64_t tiles = ((g.m + kFBM - 1) / kFBM) * ((g.n + kFBN - 1) / kFBN);
+  const int64_t tiles64 = ((g.m + 63) / 64) * ((g.n + 63) / 64) * g.batch;
   KernelTimer timer("gemm_f32", st);
-  hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)tiles, 1, (unsigned)g.batch), dim3(256), 0,
-                     st, g);
+  if (tiles64 >= 128) {
+    hipLaunchKernelGGL(gemm_f32_kernel<64>, dim3((unsigned)(tiles64 / g.batch), 1, (unsigned)g.batch), dim3(256), 0,
+                       st, g);
+  } else {
+    const int64_t tiles32 = ((g.m + 31) / 32) * ((g.n + 31) / 32);
+    hipLaunchKernelGGL(gemm_f32_kernel<32>, dim3((unsigned)tiles32, 1, (unsigned)g.batch), dim3(256), 0, st, g);
+  }
   return hipGetLastError();
 }
 
