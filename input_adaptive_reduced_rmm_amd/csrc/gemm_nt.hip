@@ -100,6 +100,7 @@ struct NtArgs {
   uint16_t *Y;
   int64_t ldy, m, n, k_pad, tiles_m, tiles_n;
   float *ypart;        // optional [2 tiles_m][n]: column sums of squares of the bf16 Y per 128-row slab
+  int y_stream;        // Y larger than the memory-side cache: non-temporal stores
 };
 
 // LDS operand tiles are [256 rows][64] bf16: 8 16-byte chunks per row, the
@@ -133,6 +134,8 @@ constexpr int vm_imm(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14);
 // 32 x 64 pieces (rows of both 128-row slabs) into a 64 x 256 staging area in
 // the LDS left over by the operand stages, and the workgroup writes the area
 // out as whole 512-byte rows: 16 stores per wave, each covering two rows.
+// A Y larger than the memory-side cache is stored non-temporally: the kernel
+// that reads it next could not find it there anyway.
 //
 // Register budget: the accumulators take half the register file, so the rest
 // must hold only fragments and a few addresses.  The LDS fragment addresses
@@ -439,8 +442,9 @@ __global__ __launch_bounds__(128 * WGN) __attribute__((amdgpu_waves_per_eu(WGN /
 #pragma unroll
         for (int q = 0; q < RQ; ++q) {
           const int trow = rtrow[q] + i * 32;
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v[q]), ry,
-                                                 (int)(((int64_t)trow * g.ldy + rch[q] * 8) * 2), 0, 0);
+          const int off = (int)(((int64_t)trow * g.ldy + rch[q] * 8) * 2);
+          if (g.y_stream) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v[q]), ry, off, 0, 2);
+          else __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v[q]), ry, off, 0, 0);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);   // this wave's reads of the area are done
         __builtin_amdgcn_s_barrier();
@@ -542,6 +546,7 @@ hipError_t launch_gemm_nt(const void *A_packed, const int32_t *idx_clean, const 
   g.tiles_m = ceil_div(m, 256);
   g.tiles_n = ceil_div(n, 256);
   g.ypart = y_scores ? ypart : nullptr;
+  g.y_stream = (double)m * (double)n * 2.0 > kStreamBytes;
   {
     KernelTimer timer("gemm_nt", st);
     const int64_t tiles = g.tiles_m * g.tiles_n;

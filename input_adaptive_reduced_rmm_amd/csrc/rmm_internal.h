@@ -37,6 +37,10 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int64_t kKTile = 64;  // K tile of the reduced GEMM; index rows are padded to it
+// Matrices above this size are streamed with non-temporal loads or stores
+// (read once, or written for a consumer that cannot find them in the
+// 256 MB memory-side cache anyway).
+constexpr double kStreamBytes = 192.0 * 1024 * 1024;
 
 // ------------------------------------------------------------------ colnorm
 struct ColnormPlan {
