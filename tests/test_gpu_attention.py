@@ -124,6 +124,9 @@ DECODE = [
     (16, 16, 2, 2, 128, 16, True),
     (7, 2000, 4, 4, 100, 1999, False),
     (2, 513, 2, 1, 1, 1, True),
+    # the longest context the one-workgroup token selection holds (32768 keys,
+    # 128 KiB of LDS)
+    (1, 32768, 2, 1, 64, 16384, True),
     # contexts longer than the one-workgroup token selection holds in LDS
     # (32768 scores): token scores and top-k as two launches
     (1, 40000, 2, 1, 64, 20000, True),
