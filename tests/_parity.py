@@ -22,6 +22,34 @@ def rel_fro(got, want) -> float:
     return float(np.linalg.norm(got - want) / (den if den > 0 else 1.0))
 
 
+# Column scores: every score within SCORE_RTOL of float64 (the worst case of a
+# blocked float32 sum of up to 16384 squares), and the root-mean-square
+# relative error within SCORE_RMS (the typical error of that sum, about
+# sqrt(terms per block) * 2^-24).
+SCORE_RTOL = 1e-5
+SCORE_RMS = 1e-6
+
+
+def score_rms(gpu_scores, oracle_scores) -> float:
+    """Root-mean-square relative error of the scores whose float64 value is
+    above 1e-30 (the per-score check covers the rest)."""
+    g = np.asarray(gpu_scores, dtype=np.float64)
+    o = np.asarray(oracle_scores, dtype=np.float64)
+    nz = o > 1e-30
+    if not np.any(nz):
+        return 0.0
+    rel = (g[nz] - o[nz]) / o[nz]
+    return float(np.sqrt(np.mean(rel * rel)))
+
+
+def check_scores(gpu_scores, oracle_scores, atol=0.0) -> float:
+    """Both score rules; returns the root-mean-square relative error."""
+    np.testing.assert_allclose(gpu_scores, oracle_scores, rtol=SCORE_RTOL, atol=atol)
+    rms = score_rms(gpu_scores, oracle_scores)
+    assert rms <= SCORE_RMS, rms
+    return rms
+
+
 def rank_gap(s: np.ndarray, k: int) -> float:
     """(s_(k) - s_(k+1)) / s_(k) for the k-th/(k+1)-th largest scores; inf when k == d."""
     d = s.shape[0]

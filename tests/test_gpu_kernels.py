@@ -11,7 +11,7 @@ import torch
 import oracle
 import synth
 from input_adaptive_reduced_rmm_amd import binding as R
-from _parity import TOL_BF16, TOL_F32, check_selection, dev_tensor, rel_fro
+from _parity import TOL_BF16, TOL_F32, check_scores, check_selection, dev_tensor, rel_fro
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -35,7 +35,7 @@ def test_colnorm(m, d, dtype):
     s = R.rmm_colnorm(dev_tensor(A, dtype)).cpu().numpy()
     want = oracle.column_scores(A)
     assert s.shape == (d,)
-    np.testing.assert_allclose(s, want, rtol=1e-5, atol=0)
+    print(f"  score rms rel err {check_scores(s, want):.2e}")
 
 
 def test_colnorm_batched_strided_and_scalar_path():
@@ -45,12 +45,12 @@ def test_colnorm_batched_strided_and_scalar_path():
     Qd = dev_tensor(Q, BF)
     s = R.rmm_colnorm(Qd.permute(1, 0, 2)).cpu().numpy()          # [H, L, dh] view
     for h in range(H):
-        np.testing.assert_allclose(s[h], oracle.column_scores(Q[:, h, :]), rtol=1e-5)
+        check_scores(s[h], oracle.column_scores(Q[:, h, :]))
     # misaligned base (scalar path): drop the first column of a wider matrix
     W = _acts(77, 301, 4)
     Wd = dev_tensor(W, BF)
     s2 = R.rmm_colnorm(Wd[:, 1:]).cpu().numpy()
-    np.testing.assert_allclose(s2, oracle.column_scores(W[:, 1:]), rtol=1e-5)
+    check_scores(s2, oracle.column_scores(W[:, 1:]))
 
 
 def test_colnorm_is_deterministic():
